@@ -1,0 +1,187 @@
+/*
+ * llsa.h -- C ABI of the MI355X (gfx950) Log-linear Sparse Attention library.
+ *
+ * The operator is the one described in "Trainable Log-linear Sparse Attention
+ * for Efficient Diffusion Transformers" (howistudyai.com explainer): input
+ * Q, K, V go through hierarchical compression, hierarchical Top-K selection
+ * and sparse attention with hierarchical KV enrichment and reweighting to the
+ * output O; a sparse index transpose drives the backward pass (explainer,
+ * paragraph "At a high level", and "Step 1" .. "Step 4").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor pointers are DEVICE pointers owned by the caller, contiguous and
+ *    row-major, at least 16-byte aligned.  The library never allocates or
+ *    frees device memory and never synchronises: each call enqueues its
+ *    kernels on `stream` (a hipStream_t passed as void*, NULL = default
+ *    stream) and returns.  It keeps no global state and is thread-safe.
+ *  - Q, K, V, O, dO are [batch, heads, seq_len, head_dim] in `dtype`.
+ *  - Level l = 1..L has n_l = seq_len / block^l tokens; level 0 is the input.
+ *    Pyramids are float32, levels stored one after the other:
+ *        level l at float offset sizes.pyramid_offset[l], shape [batch*heads, n_l, d].
+ *  - Index lists are int32, levels stored one after the other:
+ *        level l at offset sizes.index_offset[l], shape [batch*heads, n_l, K_l],
+ *    with K_L = min(K, n_L) and K_l = min(K, B*K_{l+1}) for l < L; every row
+ *    holds distinct indices in ascending order.
+ *  - All shape, pointer and alignment checks run on the host before any HIP
+ *    call; on an error status nothing is launched and no output is touched.
+ *    Launch failures are reported as LLSA_ERR_HIP.
+ *  - Supported set: head_dim = 64, block = 16, 1 <= levels <= 6,
+ *    1 <= topk <= 16, dtype LLSA_F32 or LLSA_BF16, non-causal.  Other values
+ *    give LLSA_ERR_UNSUPPORTED.
+ */
+#ifndef LLSA_H
+#define LLSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LLSA_MAX_LEVELS 6
+
+enum llsa_status {
+    LLSA_OK = 0,
+    LLSA_ERR_INVALID = 1,      /* bad shape, null or misaligned pointer, inconsistent sizes */
+    LLSA_ERR_UNSUPPORTED = 2,  /* valid but outside the supported set above               */
+    LLSA_ERR_WORKSPACE = 3,    /* workspace pointer null or smaller than required          */
+    LLSA_ERR_HIP = 4           /* a kernel launch failed                                   */
+};
+
+enum llsa_dtype { LLSA_F32 = 0, LLSA_BF16 = 1 };
+
+typedef struct llsa_problem {
+    int32_t batch, heads, seq_len, head_dim;
+    int32_t block;        /* B: tokens pooled into one token of the next level            */
+    int32_t levels;       /* L: pooling steps; seq_len % block^levels == 0                */
+    int32_t topk;         /* K: picks per query and level                                  */
+    int32_t enrich;       /* Le: coarse levels 2..Le+1 enrich attention; -1 means L-1      */
+    int32_t dtype;        /* llsa_dtype of Q, K, V, O, dO                                  */
+    int32_t grad_dtype;   /* llsa_dtype of dQ, dK, dV                                      */
+    float scale;          /* softmax scale; 0 means 1/sqrt(head_dim)                       */
+    int32_t drop_covered; /* 1: leave out a coarse pick whose level-1 children are all
+                             fine picks of the query block (then K = all blocks is exactly
+                             dense attention); 0: keep every coarse pick                  */
+} llsa_problem;
+
+typedef struct llsa_sizes {
+    int32_t levels;                              /* L                                   */
+    int32_t enrich;                              /* resolved Le                         */
+    int32_t level_tokens[LLSA_MAX_LEVELS + 1];   /* [0] = seq_len, [l] = n_l            */
+    int32_t level_k[LLSA_MAX_LEVELS + 1];        /* [l] = K_l, [0] unused               */
+    int64_t pyramid_elems;                       /* floats in ONE pyramid (q, k or v)   */
+    int64_t pyramid_offset[LLSA_MAX_LEVELS + 2]; /* float offset of level l             */
+    int64_t index_elems;                         /* int32s in the index buffer          */
+    int64_t index_offset[LLSA_MAX_LEVELS + 2];   /* int32 offset of level l             */
+    int64_t csr_ptr_elems;                       /* int32s of all CSR ptr arrays        */
+    int64_t csr_ptr_offset[LLSA_MAX_LEVELS + 2]; /* level l: [batch*heads, n_l + 1]     */
+    int64_t csr_col_elems;                       /* int32s of all CSR col arrays        */
+    int64_t csr_col_offset[LLSA_MAX_LEVELS + 2]; /* level l: [batch*heads, n_l * K_l]   */
+    int64_t lse_elems;                           /* floats of lse: batch*heads*seq_len  */
+    size_t transpose_workspace_bytes;            /* per llsa_index_transpose call, max  */
+    size_t bwd_workspace_bytes;                  /* llsa_attn_bwd                       */
+} llsa_sizes;
+
+/* Host only: derived sizes and layout offsets for problem `p`.  The CSR
+ * arrays cover levels 1..Le+1 (the levels the backward pass reads). */
+int llsa_sizes_query(const llsa_problem *p, llsa_sizes *out);
+
+/*
+ * Hierarchical compression (explainer "Step 1: Hierarchical Compression"):
+ * level l token j is the mean of level l-1 tokens jB .. jB+B-1, for
+ * l = 1..L, computed for Q, K and V in float32.
+ * In : q, k, v [batch, heads, seq_len, head_dim] (dtype).
+ * Out: pyr_q, pyr_k, pyr_v, each sizes.pyramid_elems floats (layout above).
+ */
+int llsa_pool(const llsa_problem *p, const void *q, const void *k, const void *v,
+              float *pyr_q, float *pyr_k, float *pyr_v, void *stream);
+
+/*
+ * Hierarchical Top-K selection (explainer "Step 2: Hierarchical Top-K
+ * Selection"): at level L every query scores all n_L keys; at level l < L
+ * query i scores only the B children of each pick of its parent i/B at level
+ * l+1.  A score is the float32 dot product of pooled query and pooled key;
+ * the K_l highest scores are kept, ties going to the lower index; each row is
+ * stored in ascending index order.
+ * In : pyr_q, pyr_k from llsa_pool.
+ * Out: idx, sizes.index_elems int32 (layout above).
+ */
+int llsa_select(const llsa_problem *p, const float *pyr_q, const float *pyr_k,
+                int32_t *idx, void *stream);
+
+/*
+ * Sparse attention with hierarchical KV enrichment and reweighting (explainer
+ * "Step 3: Hierarchical KV Enrichment + KV Reweighting"): query block i
+ * (tokens iB .. iB+B-1) attends to every token of its K_1 fine picks
+ * I^(1)[i] (weight 1) and, for l = 2..Le+1, to the pooled tokens K^(l)[c],
+ * V^(l)[c] of the picks c of its level-l ancestor i / B^(l-1) (weight B^l,
+ * i.e. logit + ln B^l; see drop_covered).  Logits are scale * q.k.  The
+ * kernels read only the index lists, never a dense mask.
+ * In : q, k, v (dtype), pyr_k, pyr_v (float32), idx.
+ * Out: o [batch, heads, seq_len, head_dim] (dtype), lse [batch*heads*seq_len]
+ *      float32 natural-log normaliser of every query row.
+ */
+int llsa_attn_fwd(const llsa_problem *p, const void *q, const void *k, const void *v,
+                  const float *pyr_k, const float *pyr_v, const int32_t *idx,
+                  void *o, float *lse, void *stream);
+
+/*
+ * Sparse index transpose (explainer "Step 4: Efficient Sparse Index
+ * Transpose"): query-major picks become key-major lists by counting the picks
+ * of every key, an exclusive prefix sum of the counts, and a fill.
+ * In : idx [n_batch, n_rows, k] int32, every value in [0, n_cols), rows of
+ *      distinct values.
+ * Out: csr_ptr [n_batch, n_cols + 1]: ptr[c] = number of picks of keys < c,
+ *      so ptr[n_cols] = n_rows * k; csr_col [n_batch, n_rows * k]: the rows
+ *      that picked key c, ascending, at csr_col[ptr[c] .. ptr[c+1]).
+ * workspace: at least llsa_index_transpose_workspace(...) bytes of device
+ *      memory (may be NULL when that is 0).
+ * An index outside [0, n_cols) is not detected; its row is then undefined.
+ */
+size_t llsa_index_transpose_workspace(int32_t n_batch, int32_t n_rows, int32_t k,
+                                      int32_t n_cols);
+int llsa_index_transpose(int32_t n_batch, int32_t n_rows, int32_t k, int32_t n_cols,
+                         const int32_t *idx, int32_t *csr_ptr, int32_t *csr_col,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward pass of llsa_attn_fwd for the loss <O, dO> with the picks held
+ * fixed (Top-K has no gradient; pooled Q only feeds the picks), driven by the
+ * key-major lists (explainer "Step 4"; "Sparse Index Transpose" building
+ * block): dQ is computed query-major, dK and dV key-major from the CSR of
+ * I^(1), pooled-token gradients of levels 2..Le+1 from the CSR of I^(l) and
+ * then spread back to the B^l tokens under each pooled token (mean adjoint).
+ * In : everything llsa_attn_fwd read, its outputs o and lse, dout (dtype),
+ *      csr_ptr / csr_col for levels 1..Le+1 at sizes.csr_*_offset[l], each
+ *      produced by llsa_index_transpose(batch*heads, n_l, K_l, n_l, ...).
+ * Out: dq, dk, dv [batch, heads, seq_len, head_dim] in grad_dtype.
+ * workspace: at least sizes.bwd_workspace_bytes of device memory.
+ */
+int llsa_attn_bwd(const llsa_problem *p, const void *q, const void *k, const void *v,
+                  const float *pyr_k, const float *pyr_v, const int32_t *idx,
+                  const int32_t *csr_ptr, const int32_t *csr_col,
+                  const void *o, const float *lse, const void *dout,
+                  void *dq, void *dk, void *dv,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Dense (full, non-causal) softmax attention in the same kernel style, the
+ * comparator of the explainer's "Scoreboard" speed-up (full attention).
+ * In : q, k, v [batch, heads, seq_len, head_dim] (dtype; only LLSA_BF16),
+ *      scale as in llsa_problem (other fields ignored except batch, heads,
+ *      seq_len, head_dim, dtype).
+ * Out: o (dtype), lse float32 [batch*heads*seq_len].
+ */
+int llsa_dense_attn_fwd(const llsa_problem *p, const void *q, const void *k, const void *v,
+                        void *o, float *lse, void *stream);
+
+/* Human-readable name of a status code (static string). */
+const char *llsa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLSA_H */

@@ -1,0 +1,216 @@
+// C ABI of the LLSA library: host-side validation, derived sizes and kernel
+// launches.  Every check runs before any HIP call; nothing allocates device
+// memory or synchronises.
+#include <math.h>
+#include <string.h>
+
+#include "llsa.h"
+#include "internal.hpp"
+
+using llsa::Geometry;
+
+namespace {
+
+bool aligned16(const void *p) { return p != nullptr && (((uintptr_t)p) & 15u) == 0; }
+
+int64_t ipow16(int e) {
+    int64_t r = 1;
+    while (e-- > 0) r *= 16;
+    return r;
+}
+
+// Fills g from p; returns an llsa_status.
+int make_geometry(const llsa_problem *p, Geometry *g, llsa_sizes *sz) {
+    if (p == nullptr) return LLSA_ERR_INVALID;
+    if (p->batch <= 0 || p->heads <= 0 || p->seq_len <= 0 || p->head_dim <= 0 || p->block <= 1 ||
+        p->levels < 1 || p->topk < 1)
+        return LLSA_ERR_INVALID;
+    if (p->dtype != LLSA_F32 && p->dtype != LLSA_BF16) return LLSA_ERR_INVALID;
+    if (p->grad_dtype != LLSA_F32 && p->grad_dtype != LLSA_BF16) return LLSA_ERR_INVALID;
+    if (p->drop_covered != 0 && p->drop_covered != 1) return LLSA_ERR_INVALID;
+    if (!(p->scale >= 0.0f) || isinf(p->scale)) return LLSA_ERR_INVALID;
+    if (p->levels > LLSA_MAX_LEVELS) return LLSA_ERR_UNSUPPORTED;
+    // divisibility by block^levels (checked in 64 bits before anything else)
+    int64_t span = 1;
+    for (int l = 0; l < p->levels; ++l) {
+        span *= p->block;
+        if (span > p->seq_len) return LLSA_ERR_INVALID;
+    }
+    if (p->seq_len % span != 0) return LLSA_ERR_INVALID;
+    const int L = p->levels;
+    const int Le = p->enrich < 0 ? L - 1 : p->enrich;
+    if (p->enrich < -1 || Le > L - 1) return LLSA_ERR_INVALID;
+    if (p->head_dim != 64 || p->block != 16) return LLSA_ERR_UNSUPPORTED;
+    if (p->topk > 16) return LLSA_ERR_UNSUPPORTED;
+    const int64_t bh = (int64_t)p->batch * p->heads;
+    if (bh * p->seq_len * p->head_dim >= ((int64_t)1 << 40) || bh * p->seq_len >= ((int64_t)1 << 31) ||
+        bh > (1 << 30))
+        return LLSA_ERR_UNSUPPORTED;
+
+    memset(g, 0, sizeof(*g));
+    g->bh = (int)bh;
+    g->N = p->seq_len;
+    g->L = L;
+    g->K = p->topk;
+    g->Le = Le;
+    g->n[0] = p->seq_len;
+    for (int l = 1; l <= L; ++l) g->n[l] = (int)(p->seq_len / ipow16(l));
+    g->kl[L] = p->topk < g->n[L] ? p->topk : g->n[L];
+    for (int l = L - 1; l >= 1; --l) {
+        const int cand = g->kl[l + 1] * 16;
+        g->kl[l] = p->topk < cand ? p->topk : cand;
+    }
+    // every level's segment starts on a 64-byte boundary (16 floats / int32s)
+    auto pad = [](int64_t x) { return (x + 15) / 16 * 16; };
+    int64_t off = 0, ioff = 0, poff = 0, coff = 0;
+    for (int l = 1; l <= L + 1; ++l) {
+        g->pyr_off[l] = off;
+        g->idx_off[l] = ioff;
+        g->ptr_off[l] = poff;
+        g->col_off[l] = coff;
+        if (l <= L) {
+            off += pad(bh * g->n[l] * 64);
+            ioff += pad(bh * g->n[l] * g->kl[l]);
+            if (l <= Le + 1) {
+                poff += pad(bh * (g->n[l] + 1));
+                coff += pad(bh * g->n[l] * g->kl[l]);
+            }
+        }
+    }
+    g->scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
+    g->drop_covered = p->drop_covered;
+    g->bf16 = p->dtype == LLSA_BF16;
+    g->grad_bf16 = p->grad_dtype == LLSA_BF16;
+    if (sz) {
+        memset(sz, 0, sizeof(*sz));
+        sz->levels = L;
+        sz->enrich = Le;
+        for (int l = 0; l <= L; ++l) {
+            sz->level_tokens[l] = g->n[l];
+            sz->level_k[l] = l == 0 ? 0 : g->kl[l];
+        }
+        for (int l = 1; l <= L + 1; ++l) {
+            sz->pyramid_offset[l] = g->pyr_off[l];
+            sz->index_offset[l] = g->idx_off[l];
+            sz->csr_ptr_offset[l] = g->ptr_off[l];
+            sz->csr_col_offset[l] = g->col_off[l];
+        }
+        sz->pyramid_elems = g->pyr_off[L + 1];
+        sz->index_elems = g->idx_off[L + 1];
+        sz->csr_ptr_elems = g->ptr_off[L + 1];
+        sz->csr_col_elems = g->col_off[L + 1];
+        sz->lse_elems = bh * p->seq_len;
+        sz->transpose_workspace_bytes = llsa::transpose_workspace_bytes((int)bh, g->n[1], g->kl[1], g->n[1]);
+        sz->bwd_workspace_bytes = llsa::bwd_workspace_bytes(*g);
+    }
+    return LLSA_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? LLSA_OK : LLSA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int llsa_sizes_query(const llsa_problem *p, llsa_sizes *out) {
+    if (out == nullptr) return LLSA_ERR_INVALID;
+    Geometry g;
+    return make_geometry(p, &g, out);
+}
+
+int llsa_pool(const llsa_problem *p, const void *q, const void *k, const void *v, float *pyr_q,
+              float *pyr_k, float *pyr_v, void *stream) {
+    Geometry g;
+    const int st = make_geometry(p, &g, nullptr);
+    if (st != LLSA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(pyr_q) || !aligned16(pyr_k) ||
+        !aligned16(pyr_v))
+        return LLSA_ERR_INVALID;
+    return status_of(llsa::launch_pool(g, q, k, v, pyr_q, pyr_k, pyr_v, (hipStream_t)stream));
+}
+
+int llsa_select(const llsa_problem *p, const float *pyr_q, const float *pyr_k, int32_t *idx,
+                void *stream) {
+    Geometry g;
+    const int st = make_geometry(p, &g, nullptr);
+    if (st != LLSA_OK) return st;
+    if (!aligned16(pyr_q) || !aligned16(pyr_k) || !aligned16(idx)) return LLSA_ERR_INVALID;
+    return status_of(llsa::launch_select(g, pyr_q, pyr_k, idx, (hipStream_t)stream));
+}
+
+int llsa_attn_fwd(const llsa_problem *p, const void *q, const void *k, const void *v,
+                  const float *pyr_k, const float *pyr_v, const int32_t *idx, void *o, float *lse,
+                  void *stream) {
+    Geometry g;
+    const int st = make_geometry(p, &g, nullptr);
+    if (st != LLSA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(pyr_k) || !aligned16(pyr_v) ||
+        !aligned16(idx) || !aligned16(o) || !aligned16(lse))
+        return LLSA_ERR_INVALID;
+    return status_of(llsa::launch_attn_fwd(g, q, k, v, pyr_k, pyr_v, idx, o, lse, (hipStream_t)stream));
+}
+
+size_t llsa_index_transpose_workspace(int32_t n_batch, int32_t n_rows, int32_t k, int32_t n_cols) {
+    return llsa::transpose_workspace_bytes(n_batch, n_rows, k, n_cols);
+}
+
+int llsa_index_transpose(int32_t n_batch, int32_t n_rows, int32_t k, int32_t n_cols,
+                         const int32_t *idx, int32_t *csr_ptr, int32_t *csr_col, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    if (n_batch <= 0 || n_rows <= 0 || k <= 0 || n_cols <= 0) return LLSA_ERR_INVALID;
+    if ((int64_t)n_rows * k >= ((int64_t)1 << 31) / n_batch) return LLSA_ERR_UNSUPPORTED;
+    if (n_cols > 32768) return LLSA_ERR_UNSUPPORTED;
+    if (!aligned16(idx) || !aligned16(csr_ptr) || !aligned16(csr_col)) return LLSA_ERR_INVALID;
+    const size_t need = llsa::transpose_workspace_bytes(n_batch, n_rows, k, n_cols);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LLSA_ERR_WORKSPACE;
+    return status_of(llsa::launch_transpose(n_batch, n_rows, k, n_cols, idx, csr_ptr, csr_col,
+                                            workspace, (hipStream_t)stream));
+}
+
+int llsa_attn_bwd(const llsa_problem *p, const void *q, const void *k, const void *v,
+                  const float *pyr_k, const float *pyr_v, const int32_t *idx,
+                  const int32_t *csr_ptr, const int32_t *csr_col, const void *o, const float *lse,
+                  const void *dout, void *dq, void *dk, void *dv, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    Geometry g;
+    const int st = make_geometry(p, &g, nullptr);
+    if (st != LLSA_OK) return st;
+    int ncoarse = 0;
+    for (int l = 2; l <= g.Le + 1; ++l) ncoarse += g.kl[l];
+    if (ncoarse > 32) return LLSA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(pyr_k) || !aligned16(pyr_v) ||
+        !aligned16(idx) || !aligned16(csr_ptr) || !aligned16(csr_col) || !aligned16(o) ||
+        !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return LLSA_ERR_INVALID;
+    const size_t need = llsa::bwd_workspace_bytes(g);
+    if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return LLSA_ERR_WORKSPACE;
+    return status_of(llsa::launch_attn_bwd(g, q, k, v, pyr_k, pyr_v, idx, csr_ptr, csr_col, o, lse,
+                                           dout, dq, dk, dv, workspace, (hipStream_t)stream));
+}
+
+int llsa_dense_attn_fwd(const llsa_problem *p, const void *q, const void *k, const void *v,
+                        void *o, float *lse, void *stream) {
+    if (p == nullptr) return LLSA_ERR_INVALID;
+    if (p->batch <= 0 || p->heads <= 0 || p->seq_len <= 0 || p->head_dim <= 0) return LLSA_ERR_INVALID;
+    if (!(p->scale >= 0.0f) || isinf(p->scale)) return LLSA_ERR_INVALID;
+    if (p->head_dim != 64 || p->dtype != LLSA_BF16 || p->seq_len % 16 != 0) return LLSA_ERR_UNSUPPORTED;
+    const int64_t bh = (int64_t)p->batch * p->heads;
+    if (bh * p->seq_len >= ((int64_t)1 << 31)) return LLSA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return LLSA_ERR_INVALID;
+    const float scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
+    return status_of(llsa::launch_dense_fwd((int)bh, p->seq_len, scale, q, k, v, o, lse, (hipStream_t)stream));
+}
+
+const char *llsa_strerror(int status) {
+    switch (status) {
+    case LLSA_OK: return "ok";
+    case LLSA_ERR_INVALID: return "invalid argument";
+    case LLSA_ERR_UNSUPPORTED: return "unsupported problem";
+    case LLSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LLSA_ERR_HIP: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

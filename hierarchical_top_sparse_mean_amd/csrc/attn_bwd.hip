@@ -1,0 +1,725 @@
+// Backward pass of the enriched sparse attention for the loss <O, dO> with
+// the picks held fixed ("Trainable Log-linear Sparse Attention for Efficient
+// Diffusion Transformers", explainer "Step 4: Efficient Sparse Index
+// Transpose": the key-major index lists drive the key-side gradients, no
+// dense mask is ever formed).
+//
+// Three passes:
+//  A  query-major (one wave per query block, a workgroup per level-2 node):
+//     D = rowsum(dO * O), formed in float32 as sum_j P_j dP_j (the same value
+//     without the rounding of the stored bf16 O; float32 inputs use O
+//     directly), dQ over fine and coarse keys, and the coarse-token
+//     gradient partials summed over the workgroup's query blocks (every block
+//     under one level-2 node shares its coarse picks).
+//  B  coarse reduce: for every pooled token c of level l, sum the partials of
+//     the level-l rows that picked c, read from the CSR of I^(l).
+//  C  key-major (one wave per key block): dK, dV of the block's 16 tokens
+//     from the query blocks in its CSR(I^(1)) segment, plus the pooled-token
+//     gradients of every coarse level spread back through the mean (each of
+//     the B^l tokens under a pooled token receives 1/B^l of its gradient).
+// Accumulation order is fixed everywhere (no float atomics), so results are
+// bitwise reproducible.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace llsa {
+
+constexpr int kMaxCoarseLv = kMaxLevels - 1;
+constexpr int kBwdCoarseTiles = 2;   // coarse entries per query block <= 32
+constexpr int kTS = 72;              // bf16 LDS row stride (144 B)
+constexpr int kTE = kBlock * kTS;    // elements of one staged 16 x 64 tile
+
+struct BwdArgs {
+    int bh, N, n1, n2, K1;
+    int ncl, ncoarse;
+    int cl_n[kMaxCoarseLv], cl_k[kMaxCoarseLv], cl_span[kMaxCoarseLv], cl_entry0[kMaxCoarseLv];
+    int64_t cl_idx_off[kMaxCoarseLv], cl_pyr_off[kMaxCoarseLv];
+    int64_t cl_ptr_off[kMaxCoarseLv], cl_col_off[kMaxCoarseLv];
+    int64_t cl_grad_off[kMaxCoarseLv];   // float offset of level in dpk / dpv
+    float scale, sl2;
+    int drop;
+    int grad_bf16;
+};
+
+struct BwdWs {
+    float *D;        // [bh, N]
+    float *partial;  // [bh * n2, ncoarse, 2, 64]
+    float *dpk;      // coarse-level gradients, per level [bh, n_l, 64]
+    float *dpv;
+};
+
+static BwdArgs make_bwd_args(const Geometry &g) {
+    BwdArgs a{};
+    a.bh = g.bh;
+    a.N = g.N;
+    a.n1 = g.n[1];
+    a.n2 = g.L >= 2 ? g.n[2] : 0;
+    a.K1 = g.kl[1];
+    a.ncl = g.Le < g.L - 1 ? g.Le : g.L - 1;
+    a.ncoarse = 0;
+    int64_t span = 1, goff = 0;
+    for (int j = 0; j < a.ncl; ++j) {
+        const int l = j + 2;
+        span *= kBlock;
+        a.cl_n[j] = g.n[l];
+        a.cl_k[j] = g.kl[l];
+        a.cl_span[j] = (int)span;
+        a.cl_entry0[j] = a.ncoarse;
+        a.cl_idx_off[j] = g.idx_off[l];
+        a.cl_pyr_off[j] = g.pyr_off[l];
+        a.cl_ptr_off[j] = g.ptr_off[l];
+        a.cl_col_off[j] = g.col_off[l];
+        a.cl_grad_off[j] = goff;
+        goff += (int64_t)g.bh * g.n[l] * kHeadDim;
+        a.ncoarse += g.kl[l];
+    }
+    a.scale = g.scale;
+    a.sl2 = g.scale * kLog2e;
+    a.drop = g.drop_covered;
+    a.grad_bf16 = g.grad_bf16 ? 1 : 0;
+    return a;
+}
+
+static BwdWs carve_ws(const Geometry &g, const BwdArgs &a, void *ws) {
+    BwdWs w{};
+    char *p = (char *)ws;
+    auto take = [&](size_t bytes) {
+        char *r = p;
+        p += (bytes + 255) / 256 * 256;
+        return (float *)r;
+    };
+    w.D = take(sizeof(float) * (size_t)g.bh * g.N);
+    w.partial = take(sizeof(float) * (size_t)g.bh * (size_t)a.n2 * a.ncoarse * 2 * kHeadDim);
+    size_t coarse = 0;
+    for (int j = 0; j < a.ncl; ++j) coarse += (size_t)g.bh * a.cl_n[j] * kHeadDim;
+    w.dpk = take(sizeof(float) * coarse);
+    w.dpv = take(sizeof(float) * coarse);
+    return w;
+}
+
+size_t bwd_workspace_bytes(const Geometry &g) {
+    const BwdArgs a = make_bwd_args(g);
+    size_t total = 0;
+    auto add = [&](size_t bytes) { total += (bytes + 255) / 256 * 256; };
+    add(sizeof(float) * (size_t)g.bh * g.N);
+    add(sizeof(float) * (size_t)g.bh * (size_t)a.n2 * a.ncoarse * 2 * kHeadDim);
+    size_t coarse = 0;
+    for (int j = 0; j < a.ncl; ++j) coarse += (size_t)g.bh * a.cl_n[j] * kHeadDim;
+    add(sizeof(float) * coarse);
+    add(sizeof(float) * coarse);
+    return total;
+}
+
+// Coarse entry e of query block ib: level slot j, pooled token c, log2 weight;
+// false when the entry does not exist or is dropped for this block.
+__device__ __forceinline__ bool bwd_coarse_entry(const BwdArgs &a, const int32_t *__restrict__ idx,
+                                                 const int32_t *__restrict__ fine, int h, int ib,
+                                                 int e, int &j, int &c, float &bias) {
+    if (e >= a.ncoarse) return false;
+    j = 0;
+    int pick = e;
+    while (j < a.ncl - 1 && pick >= a.cl_k[j]) {
+        pick -= a.cl_k[j];
+        ++j;
+    }
+    const int span = a.cl_span[j];
+    c = idx[a.cl_idx_off[j] + ((int64_t)h * a.cl_n[j] + ib / span) * a.cl_k[j] + pick];
+    bias = 4.0f * (float)(j + 2);
+    if (a.drop && a.K1 >= span) {
+        int cov = 0;
+        for (int f = 0; f < a.K1; ++f) cov += (fine[f] / span == c) ? 1 : 0;
+        if (cov == span) return false;
+    }
+    return true;
+}
+
+__device__ __forceinline__ void store_grad4(void *base, int64_t off, f32x4 v, int bf) {
+    if (bf) {
+        const bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        *reinterpret_cast<u32x2 *>((__bf16 *)base + off) = __builtin_bit_cast(u32x2, b);
+    } else {
+        *reinterpret_cast<f32x4 *>((float *)base + off) = v;
+    }
+}
+__device__ __forceinline__ void store_grad1(void *base, int64_t off, float v, int bf) {
+    if (bf)
+        ((__bf16 *)base)[off] = (__bf16)v;
+    else
+        ((float *)base)[off] = v;
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t x) { return __builtin_bit_cast(float, x << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t x) { return __builtin_bit_cast(float, x & 0xffff0000u); }
+
+__device__ __forceinline__ float dot8(bf16x8 a, bf16x8 b) {
+    const u32x4 x = __builtin_bit_cast(u32x4, a), y = __builtin_bit_cast(u32x4, b);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += bf_lo(x[j]) * bf_lo(y[j]) + bf_hi(x[j]) * bf_hi(y[j]);
+    return s;
+}
+
+// ================================================================ pass A
+// x ~= hi + lo with both parts in bf16 (relative error about 2^-17): the
+// gradient contractions run as two bf16 MFMAs so that rounding dS or P to
+// bf16 does not limit the accuracy of sums over hundreds of queries.
+__device__ __forceinline__ void split4(const float (&x)[4], bf16x4 &hi, bf16x4 &lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = (__bf16)x[i];
+        lo[i] = (__bf16)(x[i] - (float)hi[i]);
+    }
+}
+
+// Operand rows of coarse tile ct for query block ib: lane row = entry ct*16+c16.
+struct CoarseTile {
+    bf16x8 ka0, ka1, va0, va1;  // pooled K / V rows (bf16) as MFMA operands
+    float bias_row;             // log2 weight of entry c16, -inf if absent / dropped
+    float bias4[4];             // same for entries 4g+i
+};
+
+__device__ __forceinline__ void load_coarse_tile(const BwdArgs &a, const float *__restrict__ pk,
+                                                 const float *__restrict__ pv,
+                                                 const int32_t *__restrict__ idx,
+                                                 const int32_t *__restrict__ fine, int h, int ib,
+                                                 int ct, int g, int c16, CoarseTile &T) {
+    int jl, cc;
+    float bias;
+    const bool ok = bwd_coarse_entry(a, idx, fine, h, ib, ct * kBlock + c16, jl, cc, bias);
+    f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, k2 = k0, k3 = k0, v0 = k0, v1 = k0, v2 = k0, v3 = k0;
+    if (ok) {
+        const int64_t roff = a.cl_pyr_off[jl] + ((int64_t)h * a.cl_n[jl] + cc) * kHeadDim;
+        const f32x4 *ks = reinterpret_cast<const f32x4 *>(pk + roff);
+        const f32x4 *vsrc = reinterpret_cast<const f32x4 *>(pv + roff);
+        k0 = ks[2 * g];
+        k1 = ks[2 * g + 1];
+        k2 = ks[8 + 2 * g];
+        k3 = ks[8 + 2 * g + 1];
+        v0 = vsrc[2 * g];
+        v1 = vsrc[2 * g + 1];
+        v2 = vsrc[8 + 2 * g];
+        v3 = vsrc[8 + 2 * g + 1];
+    }
+    T.bias_row = ok ? bias : -INFINITY;
+    T.ka0 = f32_to_bf16x8(k0, k1);
+    T.ka1 = f32_to_bf16x8(k2, k3);
+    T.va0 = f32_to_bf16x8(v0, v1);
+    T.va1 = f32_to_bf16x8(v2, v3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int j2, c2;
+        float b2;
+        T.bias4[i] = bwd_coarse_entry(a, idx, fine, h, ib, ct * kBlock + 4 * g + i, j2, c2, b2) ? b2 : -INFINITY;
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
+    const float *__restrict__ pk, const float *__restrict__ pv, const int32_t *__restrict__ idx,
+    const float *__restrict__ lse, const __bf16 *__restrict__ dout, void *__restrict__ dq,
+    BwdWs ws, BwdArgs a) {
+    // per wave: K tile (for K^T reads), Q tile, dO tile, coarse K tiles; the
+    // cross-wave reduction buffer reuses the same LDS after the main loop
+    constexpr int kTileBytes = 4 * (3 + kBwdCoarseTiles) * kTE * 2;
+    constexpr int kRedBytes = 4 * kBwdCoarseTiles * 2 * kBlock * kHeadDim * 4;
+    __shared__ __attribute__((aligned(16))) char smem[kTileBytes > kRedBytes ? kTileBytes : kRedBytes];
+    __shared__ float lds_row[4][2][kBlock];  // per query: lse2, D
+    typedef __bf16 Tile[kTE];
+    Tile *lds_k = reinterpret_cast<Tile *>(smem);
+    Tile *lds_q = lds_k + 4;
+    Tile *lds_do = lds_q + 4;
+    Tile(*lds_ck)[kBwdCoarseTiles] = reinterpret_cast<Tile(*)[kBwdCoarseTiles]>(lds_do + 4);
+    typedef float RedTile[2][kBlock * kHeadDim];
+    RedTile(*lds_red)[kBwdCoarseTiles] = reinterpret_cast<RedTile(*)[kBwdCoarseTiles]>(smem);
+
+    const int w = wave_id();
+    const int lane = lane_id();
+    const int g = lane >> 4, c16 = lane & 15;
+    const int groups_per_head = (a.n1 + kBlock - 1) / kBlock;
+    const int h = blockIdx.x / groups_per_head;
+    const int G = blockIdx.x % groups_per_head;
+    const int64_t head_off = (int64_t)h * a.N * kHeadDim;
+    const int nct = (a.ncoarse + kBlock - 1) / kBlock;
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+    f32x4 dkc[kBwdCoarseTiles][4], dvc[kBwdCoarseTiles][4];
+#pragma unroll
+    for (int ct = 0; ct < kBwdCoarseTiles; ++ct)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            dkc[ct][dt] = zero4;
+            dvc[ct][dt] = zero4;
+        }
+
+    const int rofs = (4 * g + (c16 >> 2)) * kTS + 4 * (c16 & 3);  // transposed-read address
+    for (int jb = 0; jb < 4; ++jb) {
+        const int ib = G * kBlock + w * 4 + jb;
+        if (ib >= a.n1) break;
+        const int64_t row = (int64_t)ib * kBlock + c16;
+        const __bf16 *qrow = q + head_off + row * kHeadDim;
+        const __bf16 *drow = dout + head_off + row * kHeadDim;
+        const bf16x8 qa0 = load_bf16x8(qrow + 8 * g), qa1 = load_bf16x8(qrow + 32 + 8 * g);
+        const bf16x8 da0 = load_bf16x8(drow + 8 * g), da1 = load_bf16x8(drow + 32 + 8 * g);
+        const float lse2 = lse[(int64_t)h * a.N + row] * kLog2e;
+        const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
+
+        // ---- phase 1: D = dO . O = sum_j P_j dP_j over the attended set (float32)
+        float dsum = 0.f;
+        for (int t = 0; t < a.K1; ++t) {
+            const int f = __builtin_amdgcn_readfirstlane(fine[t]);
+            const __bf16 *kt = k + head_off + (int64_t)f * kBlock * kHeadDim + c16 * kHeadDim;
+            const __bf16 *vt = v + head_off + (int64_t)f * kBlock * kHeadDim + c16 * kHeadDim;
+            const bf16x8 ka0 = load_bf16x8(kt + 8 * g), ka1 = load_bf16x8(kt + 32 + 8 * g);
+            const bf16x8 va0 = load_bf16x8(vt + 8 * g), va1 = load_bf16x8(vt + 32 + 8 * g);
+            const f32x4 s = mfma_bf16_32(ka1, qa1, mfma_bf16_32(ka0, qa0, zero4));
+            const f32x4 dp = mfma_bf16_32(va1, da1, mfma_bf16_32(va0, da0, zero4));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dsum += exp2f(s[i] * a.sl2 - lse2) * dp[i];
+        }
+        for (int ct = 0; ct < nct; ++ct) {
+            CoarseTile T;
+            load_coarse_tile(a, pk, pv, idx, fine, h, ib, ct, g, c16, T);
+            const f32x4 s = mfma_bf16_32(T.ka1, qa1, mfma_bf16_32(T.ka0, qa0, zero4));
+            const f32x4 dp = mfma_bf16_32(T.va1, da1, mfma_bf16_32(T.va0, da0, zero4));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dsum += exp2f(s[i] * a.sl2 + T.bias4[i] - lse2) * dp[i];
+        }
+        const float Dq = sum4_groups(dsum);
+        if (g == 0) {
+            ws.D[(int64_t)h * a.N + row] = Dq;
+            lds_row[w][0][c16] = lse2;
+            lds_row[w][1][c16] = Dq;
+        }
+        store_bf16x8(&lds_q[w][c16 * kTS + 8 * g], qa0);
+        store_bf16x8(&lds_q[w][c16 * kTS + 32 + 8 * g], qa1);
+        store_bf16x8(&lds_do[w][c16 * kTS + 8 * g], da0);
+        store_bf16x8(&lds_do[w][c16 * kTS + 32 + 8 * g], da1);
+
+        // ---- phase 2: dS and dQ; coarse partials
+        f32x4 dqacc[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) dqacc[dt] = zero4;
+        for (int t = 0; t < a.K1; ++t) {
+            const int f = __builtin_amdgcn_readfirstlane(fine[t]);
+            const __bf16 *kt = k + head_off + (int64_t)f * kBlock * kHeadDim + c16 * kHeadDim;
+            const __bf16 *vt = v + head_off + (int64_t)f * kBlock * kHeadDim + c16 * kHeadDim;
+            const bf16x8 ka0 = load_bf16x8(kt + 8 * g), ka1 = load_bf16x8(kt + 32 + 8 * g);
+            const bf16x8 va0 = load_bf16x8(vt + 8 * g), va1 = load_bf16x8(vt + 32 + 8 * g);
+            wave_lds_sync();
+            store_bf16x8(&lds_k[w][c16 * kTS + 8 * g], ka0);
+            store_bf16x8(&lds_k[w][c16 * kTS + 32 + 8 * g], ka1);
+            const f32x4 s = mfma_bf16_32(ka1, qa1, mfma_bf16_32(ka0, qa0, zero4));
+            const f32x4 dp = mfma_bf16_32(va1, da1, mfma_bf16_32(va0, da0, zero4));
+            float ds[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ds[i] = exp2f(s[i] * a.sl2 - lse2) * (dp[i] - Dq);
+            bf16x4 dhi, dlo;
+            split4(ds, dhi, dlo);
+            wave_lds_sync();
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const bf16x4 kT = lds_read_tr4(&lds_k[w][rofs + 16 * dt]);
+                dqacc[dt] = mfma_bf16_16(kT, dlo, mfma_bf16_16(kT, dhi, dqacc[dt]));
+            }
+        }
+        for (int ct = 0; ct < nct; ++ct) {
+            CoarseTile T;
+            load_coarse_tile(a, pk, pv, idx, fine, h, ib, ct, g, c16, T);
+            wave_lds_sync();
+            store_bf16x8(&lds_ck[w][ct][c16 * kTS + 8 * g], T.ka0);
+            store_bf16x8(&lds_ck[w][ct][c16 * kTS + 32 + 8 * g], T.ka1);
+            // transposed orientation: lane (query c16, entries 4g+i) -> dQ
+            const f32x4 s = mfma_bf16_32(T.ka1, qa1, mfma_bf16_32(T.ka0, qa0, zero4));
+            const f32x4 dp = mfma_bf16_32(T.va1, da1, mfma_bf16_32(T.va0, da0, zero4));
+            // plain orientation: lane (entry c16, queries 4g+i) -> coarse partials
+            const f32x4 s2 = mfma_bf16_32(qa1, T.ka1, mfma_bf16_32(qa0, T.ka0, zero4));
+            const f32x4 dp2 = mfma_bf16_32(da1, T.va1, mfma_bf16_32(da0, T.va0, zero4));
+            float ds[4], ds2[4], p2[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ds[i] = exp2f(s[i] * a.sl2 + T.bias4[i] - lse2) * (dp[i] - Dq);
+                const float l2q = lds_row[w][0][4 * g + i];
+                const float Dqi = lds_row[w][1][4 * g + i];
+                p2[i] = exp2f(s2[i] * a.sl2 + T.bias_row - l2q);
+                ds2[i] = p2[i] * (dp2[i] - Dqi);
+            }
+            bf16x4 dhi, dlo, d2hi, d2lo, p2hi, p2lo;
+            split4(ds, dhi, dlo);
+            split4(ds2, d2hi, d2lo);
+            split4(p2, p2hi, p2lo);
+            wave_lds_sync();
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const bf16x4 kT = lds_read_tr4(&lds_ck[w][ct][rofs + 16 * dt]);
+                dqacc[dt] = mfma_bf16_16(kT, dlo, mfma_bf16_16(kT, dhi, dqacc[dt]));
+                const bf16x4 qT = lds_read_tr4(&lds_q[w][rofs + 16 * dt]);
+                const bf16x4 dT = lds_read_tr4(&lds_do[w][rofs + 16 * dt]);
+                if (ct == 0) {
+                    dkc[0][dt] = mfma_bf16_16(d2lo, qT, mfma_bf16_16(d2hi, qT, dkc[0][dt]));
+                    dvc[0][dt] = mfma_bf16_16(p2lo, dT, mfma_bf16_16(p2hi, dT, dvc[0][dt]));
+                } else {
+                    dkc[1][dt] = mfma_bf16_16(d2lo, qT, mfma_bf16_16(d2hi, qT, dkc[1][dt]));
+                    dvc[1][dt] = mfma_bf16_16(p2lo, dT, mfma_bf16_16(p2hi, dT, dvc[1][dt]));
+                }
+            }
+        }
+        // ---- dQ store: lane (query c16, dims 16dt + 4g + i)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            store_grad4(dq, head_off + row * kHeadDim + 16 * dt + 4 * g, dqacc[dt] * a.scale, a.grad_bf16);
+        wave_lds_sync();
+    }
+    if (nct == 0) return;
+    __syncthreads();   // every wave is done with the tiles that share this LDS
+    // ---- reduce coarse partials over the 4 waves; layout C: lane (dim 16dt + c16, entries 4g+i)
+    for (int ct = 0; ct < nct; ++ct)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ent = 4 * g + i, dim = 16 * dt + c16;
+                lds_red[w][ct][0][ent * kHeadDim + dim] = (ct == 0 ? dkc[0][dt][i] : dkc[1][dt][i]) * a.scale;
+                lds_red[w][ct][1][ent * kHeadDim + dim] = ct == 0 ? dvc[0][dt][i] : dvc[1][dt][i];
+            }
+    __syncthreads();
+    float *part = ws.partial + ((int64_t)h * a.n2 + G) * a.ncoarse * 2 * kHeadDim;
+    for (int x = threadIdx.x; x < a.ncoarse * 2 * kHeadDim; x += 256) {
+        const int ent = x / (2 * kHeadDim), kv = (x / kHeadDim) & 1, dim = x % kHeadDim;
+        const int ct = ent / kBlock, er = ent % kBlock;
+        const float s = lds_red[0][ct][kv][er * kHeadDim + dim] + lds_red[1][ct][kv][er * kHeadDim + dim] +
+                        lds_red[2][ct][kv][er * kHeadDim + dim] + lds_red[3][ct][kv][er * kHeadDim + dim];
+        part[x] = s;
+    }
+}
+
+// ================================================================ pass B
+// One thread per (level, pooled token, column): sum over the level-l rows
+// that picked the token (CSR of I^(l)) and over the level-2 nodes under each
+// such row.
+__global__ __launch_bounds__(256) void bwd_coarse_reduce_kernel(const int32_t *__restrict__ idx,
+                                                                const int32_t *__restrict__ csr_ptr,
+                                                                const int32_t *__restrict__ csr_col,
+                                                                BwdWs ws, BwdArgs a, int j) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int nl = a.cl_n[j], kl = a.cl_k[j];
+    if (t >= (int64_t)a.bh * nl * kHeadDim) return;
+    const int h = (int)(t / ((int64_t)nl * kHeadDim));
+    const int c = (int)((t / kHeadDim) % nl);
+    const int dim = (int)(t % kHeadDim);
+    const int32_t *P = csr_ptr + a.cl_ptr_off[j] + (int64_t)h * (nl + 1);
+    const int32_t *C = csr_col + a.cl_col_off[j] + (int64_t)h * nl * kl;
+    const int32_t *I = idx + a.cl_idx_off[j] + (int64_t)h * nl * kl;
+    const int nodes = a.cl_span[j] / kBlock;   // level-2 nodes under one level-l token
+    float sk = 0.f, sv = 0.f;
+    for (int e = P[c]; e < P[c + 1]; ++e) {
+        const int r = C[e];
+        int slot = 0;
+        while (slot < kl && I[(int64_t)r * kl + slot] != c) ++slot;
+        if (slot == kl) continue;   // not a pick of row r: inconsistent lists, skip
+        const int ent = a.cl_entry0[j] + slot;
+        for (int s = 0; s < nodes; ++s) {
+            const int64_t G = (int64_t)h * a.n2 + (int64_t)r * nodes + s;
+            const float *pp = ws.partial + (G * a.ncoarse + ent) * 2 * kHeadDim;
+            sk += pp[dim];
+            sv += pp[kHeadDim + dim];
+        }
+    }
+    ws.dpk[a.cl_grad_off[j] + ((int64_t)h * nl + c) * kHeadDim + dim] = sk;
+    ws.dpv[a.cl_grad_off[j] + ((int64_t)h * nl + c) * kHeadDim + dim] = sv;
+}
+
+// ================================================================ pass C
+__global__ __launch_bounds__(256, 2) void bwd_dkv_bf16_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
+    const float *__restrict__ lse, const __bf16 *__restrict__ dout, const int32_t *__restrict__ csr_ptr,
+    const int32_t *__restrict__ csr_col, void *__restrict__ dk, void *__restrict__ dv, BwdWs ws,
+    BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) __bf16 lds_q[4][kTE];
+    __shared__ __attribute__((aligned(16))) __bf16 lds_do[4][kTE];
+    const int w = wave_id();
+    const int lane = lane_id();
+    const int g = lane >> 4, c16 = lane & 15;
+    const int64_t kb = (int64_t)blockIdx.x * 4 + w;
+    if (kb >= (int64_t)a.bh * a.n1) return;
+    const int h = (int)(kb / a.n1);
+    const int f = (int)(kb % a.n1);
+    const int64_t head_off = (int64_t)h * a.N * kHeadDim;
+    const __bf16 *krow = k + head_off + ((int64_t)f * kBlock + c16) * kHeadDim;
+    const __bf16 *vrow = v + head_off + ((int64_t)f * kBlock + c16) * kHeadDim;
+    const bf16x8 kb0 = load_bf16x8(krow + 8 * g), kb1 = load_bf16x8(krow + 32 + 8 * g);
+    const bf16x8 vb0 = load_bf16x8(vrow + 8 * g), vb1 = load_bf16x8(vrow + 32 + 8 * g);
+    f32x4 dka[4], dva[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        dka[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dva[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int rofs = (4 * g + (c16 >> 2)) * kTS + 4 * (c16 & 3);
+    const int32_t *P = csr_ptr + (int64_t)h * (a.n1 + 1);
+    const int32_t *C = csr_col + (int64_t)h * a.n1 * a.K1;
+    const int e0 = __builtin_amdgcn_readfirstlane(P[f]), e1 = __builtin_amdgcn_readfirstlane(P[f + 1]);
+    for (int e = e0; e < e1; ++e) {
+        const int ib = __builtin_amdgcn_readfirstlane(C[e]);
+        const int64_t row = (int64_t)ib * kBlock + c16;
+        const __bf16 *qr = q + head_off + row * kHeadDim;
+        const __bf16 *dr = dout + head_off + row * kHeadDim;
+        const bf16x8 qa0 = load_bf16x8(qr + 8 * g), qa1 = load_bf16x8(qr + 32 + 8 * g);
+        const bf16x8 da0 = load_bf16x8(dr + 8 * g), da1 = load_bf16x8(dr + 32 + 8 * g);
+        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(lse + (int64_t)h * a.N + (int64_t)ib * kBlock + 4 * g);
+        const f32x4 D4 = *reinterpret_cast<const f32x4 *>(ws.D + (int64_t)h * a.N + (int64_t)ib * kBlock + 4 * g);
+        wave_lds_sync();
+        store_bf16x8(&lds_q[w][c16 * kTS + 8 * g], qa0);
+        store_bf16x8(&lds_q[w][c16 * kTS + 32 + 8 * g], qa1);
+        store_bf16x8(&lds_do[w][c16 * kTS + 8 * g], da0);
+        store_bf16x8(&lds_do[w][c16 * kTS + 32 + 8 * g], da1);
+        // S = Q K^T: lane (key c16, queries 4g+i)
+        f32x4 s = mfma_bf16_32(qa0, kb0, f32x4{0.f, 0.f, 0.f, 0.f});
+        s = mfma_bf16_32(qa1, kb1, s);
+        f32x4 dp = mfma_bf16_32(da0, vb0, f32x4{0.f, 0.f, 0.f, 0.f});
+        dp = mfma_bf16_32(da1, vb1, dp);
+        float pp[4], ds[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pp[i] = exp2f(s[i] * a.sl2 - l4[i] * kLog2e);
+            ds[i] = pp[i] * (dp[i] - D4[i]);
+        }
+        bf16x4 phi, plo, dhi, dlo;
+        split4(pp, phi, plo);
+        split4(ds, dhi, dlo);
+        wave_lds_sync();
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const bf16x4 dT = lds_read_tr4(&lds_do[w][rofs + 16 * dt]);
+            const bf16x4 qT = lds_read_tr4(&lds_q[w][rofs + 16 * dt]);
+            dva[dt] = mfma_bf16_16(plo, dT, mfma_bf16_16(phi, dT, dva[dt]));
+            dka[dt] = mfma_bf16_16(dlo, qT, mfma_bf16_16(dhi, qT, dka[dt]));
+        }
+    }
+    // C layout: lane (dim 16dt + c16, keys 4g+i); add pooled-level gradients / B^l
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        const int dim = 16 * dt + c16;
+        float ck = 0.f, cv = 0.f;
+        float inv = 1.f;
+        for (int j = 0; j < a.ncl; ++j) {
+            inv *= (1.0f / kBlock);
+            const int c = f / a.cl_span[j];
+            const int64_t off = a.cl_grad_off[j] + ((int64_t)h * a.cl_n[j] + c) * kHeadDim + dim;
+            ck += ws.dpk[off] * (inv * (1.0f / kBlock));
+            cv += ws.dpv[off] * (inv * (1.0f / kBlock));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t off = head_off + ((int64_t)f * kBlock + 4 * g + i) * kHeadDim + dim;
+            store_grad1(dk, off, dka[dt][i] * a.scale + ck, a.grad_bf16);
+            store_grad1(dv, off, dva[dt][i] + cv, a.grad_bf16);
+        }
+    }
+}
+
+// ================================================================ f32 path
+// Pass A (f32): one thread per query.
+__global__ __launch_bounds__(256) void bwd_dq_f32_kernel(
+    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
+    const float *__restrict__ pk, const float *__restrict__ pv, const int32_t *__restrict__ idx,
+    const float *__restrict__ o, const float *__restrict__ lse, const float *__restrict__ dout,
+    void *__restrict__ dq, BwdWs ws, BwdArgs a) {
+    const int64_t tq = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (tq >= (int64_t)a.bh * a.N) return;
+    const int h = (int)(tq / a.N);
+    const int tok = (int)(tq % a.N);
+    const int ib = tok / kBlock;
+    const int64_t head_off = (int64_t)h * a.N * kHeadDim;
+    const float *qv = q + head_off + (int64_t)tok * kHeadDim;
+    const float *gv = dout + head_off + (int64_t)tok * kHeadDim;
+    const float *ov = o + head_off + (int64_t)tok * kHeadDim;
+    float D = 0.f;
+    for (int e = 0; e < kHeadDim; ++e) D = fmaf(gv[e], ov[e], D);
+    ws.D[tq] = D;
+    const float lse2 = lse[tq] * kLog2e;
+    float acc[kHeadDim];
+#pragma unroll
+    for (int e = 0; e < kHeadDim; ++e) acc[e] = 0.f;
+    auto visit = [&](const float *kr, const float *vr, float bias) {
+        float s = 0.f, dp = 0.f;
+        for (int e = 0; e < kHeadDim; ++e) {
+            s = fmaf(qv[e], kr[e], s);
+            dp = fmaf(gv[e], vr[e], dp);
+        }
+        const float p = exp2f(s * a.sl2 + bias - lse2);
+        const float ds = p * (dp - D);
+#pragma unroll
+        for (int e = 0; e < kHeadDim; ++e) acc[e] = fmaf(ds, kr[e], acc[e]);
+    };
+    const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
+    for (int j = 0; j < a.K1; ++j)
+        for (int t = 0; t < kBlock; ++t) {
+            const int64_t u = (int64_t)fine[j] * kBlock + t;
+            visit(k + head_off + u * kHeadDim, v + head_off + u * kHeadDim, 0.f);
+        }
+    for (int e = 0; e < a.ncoarse; ++e) {
+        int jl, c;
+        float b;
+        if (bwd_coarse_entry(a, idx, fine, h, ib, e, jl, c, b)) {
+            const int64_t roff = a.cl_pyr_off[jl] + ((int64_t)h * a.cl_n[jl] + c) * kHeadDim;
+            visit(pk + roff, pv + roff, b);
+        }
+    }
+    for (int e = 0; e < kHeadDim; ++e) store_grad1(dq, head_off + (int64_t)tok * kHeadDim + e, acc[e] * a.scale, a.grad_bf16);
+}
+
+// Pooled-token gradients (f32): one thread per (level, pooled token); walks
+// the CSR of I^(l) and every query block under each row that picked it.
+__global__ __launch_bounds__(64) void bwd_coarse_f32_kernel(
+    const float *__restrict__ q, const float *__restrict__ pk, const float *__restrict__ pv,
+    const int32_t *__restrict__ idx, const float *__restrict__ lse, const float *__restrict__ dout,
+    const int32_t *__restrict__ csr_ptr, const int32_t *__restrict__ csr_col, BwdWs ws, BwdArgs a,
+    int j) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int nl = a.cl_n[j], kl = a.cl_k[j], span = a.cl_span[j];
+    if (t >= (int64_t)a.bh * nl) return;
+    const int h = (int)(t / nl);
+    const int c = (int)(t % nl);
+    const int64_t head_off = (int64_t)h * a.N * kHeadDim;
+    const int64_t roff = a.cl_pyr_off[j] + ((int64_t)h * nl + c) * kHeadDim;
+    const float *kr = pk + roff, *vr = pv + roff;
+    const float bias = 4.0f * (float)(j + 2);
+    float gk[kHeadDim], gvv[kHeadDim];
+    for (int e = 0; e < kHeadDim; ++e) {
+        gk[e] = 0.f;
+        gvv[e] = 0.f;
+    }
+    const int32_t *P = csr_ptr + a.cl_ptr_off[j] + (int64_t)h * (nl + 1);
+    const int32_t *C = csr_col + a.cl_col_off[j] + (int64_t)h * nl * kl;
+    for (int e = P[c]; e < P[c + 1]; ++e) {
+        const int r = C[e];
+        for (int ib = r * span; ib < (r + 1) * span; ++ib) {
+            const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
+            if (a.drop && a.K1 >= span) {
+                int cov = 0;
+                for (int ff = 0; ff < a.K1; ++ff) cov += (fine[ff] / span == c) ? 1 : 0;
+                if (cov == span) continue;
+            }
+            for (int tt = 0; tt < kBlock; ++tt) {
+                const int64_t tok = (int64_t)ib * kBlock + tt;
+                const float *qv = q + head_off + tok * kHeadDim;
+                const float *gv = dout + head_off + tok * kHeadDim;
+                float s = 0.f, dp = 0.f;
+                for (int x = 0; x < kHeadDim; ++x) {
+                    s = fmaf(qv[x], kr[x], s);
+                    dp = fmaf(gv[x], vr[x], dp);
+                }
+                const float p = exp2f(s * a.sl2 + bias - lse[(int64_t)h * a.N + tok] * kLog2e);
+                const float ds = p * (dp - ws.D[(int64_t)h * a.N + tok]);
+                for (int x = 0; x < kHeadDim; ++x) {
+                    gk[x] = fmaf(ds, qv[x], gk[x]);
+                    gvv[x] = fmaf(p, gv[x], gvv[x]);
+                }
+            }
+        }
+    }
+    for (int x = 0; x < kHeadDim; ++x) {
+        ws.dpk[a.cl_grad_off[j] + ((int64_t)h * nl + c) * kHeadDim + x] = gk[x] * a.scale;
+        ws.dpv[a.cl_grad_off[j] + ((int64_t)h * nl + c) * kHeadDim + x] = gvv[x];
+    }
+}
+
+// Pass C (f32): one thread per key token.
+__global__ __launch_bounds__(256) void bwd_dkv_f32_kernel(
+    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
+    const float *__restrict__ lse, const float *__restrict__ dout, const int32_t *__restrict__ csr_ptr,
+    const int32_t *__restrict__ csr_col, void *__restrict__ dk, void *__restrict__ dv, BwdWs ws,
+    BwdArgs a) {
+    const int64_t tu = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (tu >= (int64_t)a.bh * a.N) return;
+    const int h = (int)(tu / a.N);
+    const int u = (int)(tu % a.N);
+    const int f = u / kBlock;
+    const int64_t head_off = (int64_t)h * a.N * kHeadDim;
+    const float *kr = k + head_off + (int64_t)u * kHeadDim;
+    const float *vr = v + head_off + (int64_t)u * kHeadDim;
+    float gk[kHeadDim], gvv[kHeadDim];
+    for (int e = 0; e < kHeadDim; ++e) {
+        gk[e] = 0.f;
+        gvv[e] = 0.f;
+    }
+    const int32_t *P = csr_ptr + (int64_t)h * (a.n1 + 1);
+    const int32_t *C = csr_col + (int64_t)h * a.n1 * a.K1;
+    for (int e = P[f]; e < P[f + 1]; ++e) {
+        const int ib = C[e];
+        for (int tt = 0; tt < kBlock; ++tt) {
+            const int64_t tok = (int64_t)ib * kBlock + tt;
+            const float *qv = q + head_off + tok * kHeadDim;
+            const float *gv = dout + head_off + tok * kHeadDim;
+            float s = 0.f, dp = 0.f;
+            for (int x = 0; x < kHeadDim; ++x) {
+                s = fmaf(qv[x], kr[x], s);
+                dp = fmaf(gv[x], vr[x], dp);
+            }
+            const float p = exp2f(s * a.sl2 - lse[(int64_t)h * a.N + tok] * kLog2e);
+            const float ds = p * (dp - ws.D[(int64_t)h * a.N + tok]);
+            for (int x = 0; x < kHeadDim; ++x) {
+                gk[x] = fmaf(ds, qv[x], gk[x]);
+                gvv[x] = fmaf(p, gv[x], gvv[x]);
+            }
+        }
+    }
+    for (int x = 0; x < kHeadDim; ++x) gk[x] *= a.scale;
+    float inv = 1.f;
+    for (int j = 0; j < a.ncl; ++j) {
+        inv *= (1.0f / kBlock);
+        const int c = f / a.cl_span[j];
+        const int64_t off = a.cl_grad_off[j] + ((int64_t)h * a.cl_n[j] + c) * kHeadDim;
+        for (int x = 0; x < kHeadDim; ++x) {
+            gk[x] += ws.dpk[off + x] * (inv * (1.0f / kBlock));
+            gvv[x] += ws.dpv[off + x] * (inv * (1.0f / kBlock));
+        }
+    }
+    for (int x = 0; x < kHeadDim; ++x) {
+        store_grad1(dk, head_off + (int64_t)u * kHeadDim + x, gk[x], a.grad_bf16);
+        store_grad1(dv, head_off + (int64_t)u * kHeadDim + x, gvv[x], a.grad_bf16);
+    }
+}
+
+hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, const void *v,
+                           const float *pk, const float *pv, const int32_t *idx,
+                           const int32_t *csr_ptr, const int32_t *csr_col, const void *o,
+                           const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                           void *wsp, hipStream_t s) {
+    const BwdArgs a = make_bwd_args(g);
+    const BwdWs ws = carve_ws(g, a, wsp);
+    if (g.bf16) {
+        const int gph = (a.n1 + kBlock - 1) / kBlock;
+        hipLaunchKernelGGL(bwd_dq_bf16_kernel, dim3((unsigned)(g.bh * gph)), dim3(256), 0, s,
+                           (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx,
+                           lse, (const __bf16 *)dout, dq, ws, a);
+        for (int j = 0; j < a.ncl; ++j) {
+            const int64_t total = (int64_t)g.bh * a.cl_n[j] * kHeadDim;
+            hipLaunchKernelGGL(bwd_coarse_reduce_kernel, dim3((unsigned)((total + 255) / 256)),
+                               dim3(256), 0, s, idx, csr_ptr, csr_col, ws, a, j);
+        }
+        const int64_t kbs = (int64_t)g.bh * a.n1;
+        hipLaunchKernelGGL(bwd_dkv_bf16_kernel, dim3((unsigned)((kbs + 3) / 4)), dim3(256), 0, s,
+                           (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, lse,
+                           (const __bf16 *)dout, csr_ptr + g.ptr_off[1], csr_col + g.col_off[1], dk,
+                           dv, ws, a);
+    } else {
+        const int64_t total = (int64_t)g.bh * g.N;
+        hipLaunchKernelGGL(bwd_dq_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                           (const float *)q, (const float *)k, (const float *)v, pk, pv, idx,
+                           (const float *)o, lse, (const float *)dout, dq, ws, a);
+        for (int j = 0; j < a.ncl; ++j) {
+            const int64_t nt = (int64_t)g.bh * a.cl_n[j];
+            hipLaunchKernelGGL(bwd_coarse_f32_kernel, dim3((unsigned)((nt + 63) / 64)), dim3(64), 0,
+                               s, (const float *)q, pk, pv, idx, lse, (const float *)dout, csr_ptr,
+                               csr_col, ws, a, j);
+        }
+        hipLaunchKernelGGL(bwd_dkv_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                           s, (const float *)q, (const float *)k, (const float *)v, lse,
+                           (const float *)dout, csr_ptr + g.ptr_off[1], csr_col + g.col_off[1], dk,
+                           dv, ws, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace llsa

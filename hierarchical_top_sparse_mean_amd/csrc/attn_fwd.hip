@@ -1,0 +1,270 @@
+// Sparse attention with hierarchical KV enrichment and reweighting
+// ("Trainable Log-linear Sparse Attention for Efficient Diffusion
+// Transformers", explainer "Step 3: Hierarchical KV Enrichment + KV
+// Reweighting"), driven only by the index lists.
+//
+// bf16 path: one wave per query block of 16 queries.  Scores are computed
+// transposed, S^T = K Q^T, on v_mfma_f32_16x16x32_bf16 so that lane l owns
+// query l%16 and keys 4(l/16)..+3 of every 16-key tile; that register layout
+// is exactly the B operand of O^T += V^T P^T, so probabilities never leave
+// registers.  K and Q tiles are loaded straight from HBM into MFMA operand
+// registers; a gathered V tile goes through LDS once and is read back with
+// the gfx950 transposing LDS load.  Coarse tokens (float32 pyramid) are
+// converted to bf16 on the fly and carry the logit bias log2(B^l).  Softmax
+// runs in the exp2 domain over chunks of up to 8 tiles with one cross-lane
+// max per chunk.
+//
+// f32 path: one thread per query, all arithmetic in float32 (used for f32
+// inputs, where the output tolerance is tighter than bf16 products allow).
+#include "common.hpp"
+#include "internal.hpp"
+#include "attn_tile.hpp"
+
+namespace llsa {
+
+constexpr int kMaxCoarseLevels = kMaxLevels - 1;
+
+struct FwdArgs {
+    int bh, N, n1, K1;
+    int ncl;                                   // coarse levels used (2..ncl+1)
+    int ncoarse;                               // coarse entries per query block
+    int cl_n[kMaxCoarseLevels];                // tokens at that level
+    int cl_k[kMaxCoarseLevels];                // picks at that level
+    int cl_span[kMaxCoarseLevels];             // level-1 blocks under one token
+    int64_t cl_idx_off[kMaxCoarseLevels];      // index offset of the level
+    int64_t cl_pyr_off[kMaxCoarseLevels];      // pyramid offset of the level
+    float sl2;                                 // scale * log2(e)
+    int drop;                                  // drop fully covered coarse picks
+};
+
+static FwdArgs make_fwd_args(const Geometry &g) {
+    FwdArgs a{};
+    a.bh = g.bh;
+    a.N = g.N;
+    a.n1 = g.n[1];
+    a.K1 = g.kl[1];
+    a.ncl = g.Le < g.L - 1 ? g.Le : g.L - 1;
+    a.ncoarse = 0;
+    int64_t span = 1;
+    for (int j = 0; j < a.ncl; ++j) {
+        const int l = j + 2;
+        span *= kBlock;
+        a.cl_n[j] = g.n[l];
+        a.cl_k[j] = g.kl[l];
+        a.cl_span[j] = (int)span;
+        a.cl_idx_off[j] = g.idx_off[l];
+        a.cl_pyr_off[j] = g.pyr_off[l];
+        a.ncoarse += g.kl[l];
+    }
+    a.sl2 = g.scale * kLog2e;
+    a.drop = g.drop_covered;
+    return a;
+}
+
+// Coarse entry e of query block ib (levels in order, picks in order): returns
+// the pooled-token row offset (floats) and the log2 weight, or false if the
+// entry does not exist or is dropped.
+__device__ __forceinline__ bool coarse_entry(const FwdArgs &a, const int32_t *__restrict__ idx,
+                                             const int32_t *__restrict__ fine, int h, int ib,
+                                             int e, int64_t &row_off, float &bias) {
+    if (e >= a.ncoarse) return false;
+    int j = 0;
+    int pick = e;
+    while (j < a.ncl - 1 && pick >= a.cl_k[j]) {
+        pick -= a.cl_k[j];
+        ++j;
+    }
+    const int span = a.cl_span[j];
+    const int anc = ib / span;
+    const int c = idx[a.cl_idx_off[j] + ((int64_t)h * a.cl_n[j] + anc) * a.cl_k[j] + pick];
+    if (a.drop && a.K1 >= span) {
+        int cov = 0;
+        for (int f = 0; f < a.K1; ++f) cov += (fine[f] / span == c) ? 1 : 0;
+        if (cov == span) return false;
+    }
+    row_off = a.cl_pyr_off[j] + ((int64_t)h * a.cl_n[j] + c) * kHeadDim;
+    bias = 4.0f * (float)(j + 2);  // log2(16^l)
+    return true;
+}
+
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
+    const float *__restrict__ pk, const float *__restrict__ pv, const int32_t *__restrict__ idx,
+    __bf16 *__restrict__ o, float *__restrict__ lse, FwdArgs a) {
+    __shared__ __attribute__((aligned(16))) __bf16 vs_all[4][kFwdTiles * kTileElems];
+    const int w = wave_id();
+    const int lane = lane_id();
+    const int g = lane >> 4, c16 = lane & 15;
+    const int64_t blk = (int64_t)blockIdx.x * 4 + w;
+    if (blk >= (int64_t)a.bh * a.n1) return;
+    const int h = (int)(blk / a.n1);
+    const int ib = (int)(blk % a.n1);
+    const int64_t head_off = (int64_t)h * a.N * kHeadDim;
+    const __bf16 *kh = k + head_off;
+    const __bf16 *vh = v + head_off;
+    __bf16 *vw = vs_all[w];
+
+    const __bf16 *qrow = q + head_off + (int64_t)(ib * kBlock + c16) * kHeadDim;
+    const bf16x8 qa0 = load_bf16x8(qrow + 8 * g);
+    const bf16x8 qa1 = load_bf16x8(qrow + 32 + 8 * g);
+    const int32_t *fine = idx + blk * a.K1;
+
+    float m = -INFINITY, lsum = 0.f;
+    f32x4 oacc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    float bias[kFwdTiles][4];
+    f32x4 st[kFwdTiles];
+    // ---- fine key blocks, weight 1
+    for (int t0 = 0; t0 < a.K1; t0 += kFwdTiles) {
+        const int nt = min(kFwdTiles, a.K1 - t0);
+#pragma unroll
+        for (int t = 0; t < kFwdTiles; ++t) {
+            if (t < nt) {
+                const int f = __builtin_amdgcn_readfirstlane(fine[t0 + t]);
+                const __bf16 *kt = kh + (int64_t)f * kBlock * kHeadDim;
+                const __bf16 *vt = vh + (int64_t)f * kBlock * kHeadDim;
+                const bf16x8 ka0 = load_bf16x8(kt + c16 * kHeadDim + 8 * g);
+                const bf16x8 ka1 = load_bf16x8(kt + c16 * kHeadDim + 32 + 8 * g);
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const int ci = lane + kWave * r;  // 16-byte chunk of the 2 KB tile
+                    store_bf16x8(vw + t * kTileElems + (ci >> 3) * kVStride + (ci & 7) * 8,
+                                 load_bf16x8(vt + ci * 8));
+                }
+                f32x4 s = mfma_bf16_32(ka0, qa0, f32x4{0.f, 0.f, 0.f, 0.f});
+                s = mfma_bf16_32(ka1, qa1, s);
+                st[t] = s * a.sl2;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) bias[t][i] = 0.f;
+            }
+        }
+        softmax_pv_chunk(st, bias, nt, vw, m, lsum, oacc, g, c16);
+    }
+    // ---- coarse tokens of levels 2..ncl+1, weight B^l
+    const int nct = (a.ncoarse + kBlock - 1) / kBlock;
+    for (int t0 = 0; t0 < nct; t0 += kFwdTiles) {
+        const int nt = min(kFwdTiles, nct - t0);
+#pragma unroll
+        for (int t = 0; t < kFwdTiles; ++t) {
+            if (t < nt) {
+                // operand row: entry (t0+t)*16 + c16
+                int64_t roff = 0;
+                float b = 0.f;
+                const bool ok = coarse_entry(a, idx, fine, h, ib, (t0 + t) * kBlock + c16, roff, b);
+                f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, k2 = k0, k3 = k0;
+                f32x4 v0 = k0, v1 = k0, v2 = k0, v3 = k0;
+                if (ok) {
+                    const f32x4 *ks = reinterpret_cast<const f32x4 *>(pk + roff);
+                    const f32x4 *vsrc = reinterpret_cast<const f32x4 *>(pv + roff + 16 * g);
+                    k0 = ks[2 * g];
+                    k1 = ks[2 * g + 1];
+                    k2 = ks[8 + 2 * g];
+                    k3 = ks[8 + 2 * g + 1];
+                    v0 = vsrc[0];
+                    v1 = vsrc[1];
+                    v2 = vsrc[2];
+                    v3 = vsrc[3];
+                }
+                __bf16 *vrow = vw + t * kTileElems + c16 * kVStride + 16 * g;
+                store_bf16x8(vrow, f32_to_bf16x8(v0, v1));
+                store_bf16x8(vrow + 8, f32_to_bf16x8(v2, v3));
+                const bf16x8 ka0 = f32_to_bf16x8(k0, k1);
+                const bf16x8 ka1 = f32_to_bf16x8(k2, k3);
+                f32x4 s = mfma_bf16_32(ka0, qa0, f32x4{0.f, 0.f, 0.f, 0.f});
+                s = mfma_bf16_32(ka1, qa1, s);
+                st[t] = s * a.sl2;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    int64_t r2;
+                    float b2;
+                    const bool ok2 = coarse_entry(a, idx, fine, h, ib, (t0 + t) * kBlock + 4 * g + i, r2, b2);
+                    bias[t][i] = ok2 ? b2 : -INFINITY;
+                }
+            }
+        }
+        softmax_pv_chunk(st, bias, nt, vw, m, lsum, oacc, g, c16);
+    }
+    // ---- normalise and store
+    lsum = sum4_groups(lsum);
+    const float inv = 1.0f / lsum;
+    __bf16 *orow = o + head_off + (int64_t)(ib * kBlock + c16) * kHeadDim + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        const f32x4 r = oacc[dt] * inv;
+        const bf16x4 rb = {(__bf16)r[0], (__bf16)r[1], (__bf16)r[2], (__bf16)r[3]};
+        *reinterpret_cast<u32x2 *>(orow + 16 * dt) = __builtin_bit_cast(u32x2, rb);
+    }
+    if (g == 0) lse[(int64_t)h * a.N + ib * kBlock + c16] = (m + log2f(lsum)) * kLn2;
+}
+
+// ---------------------------------------------------------------- f32 path
+__global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
+    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
+    const float *__restrict__ pk, const float *__restrict__ pv, const int32_t *__restrict__ idx,
+    float *__restrict__ o, float *__restrict__ lse, FwdArgs a) {
+    const int64_t tq = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (tq >= (int64_t)a.bh * a.N) return;
+    const int h = (int)(tq / a.N);
+    const int tok = (int)(tq % a.N);
+    const int ib = tok / kBlock;
+    const int64_t head_off = (int64_t)h * a.N * kHeadDim;
+    float qv[kHeadDim], acc[kHeadDim];
+#pragma unroll
+    for (int e = 0; e < kHeadDim; ++e) {
+        qv[e] = q[head_off + (int64_t)tok * kHeadDim + e];
+        acc[e] = 0.f;
+    }
+    float m = -INFINITY, l = 0.f;
+    auto attend = [&](const float *kr, const float *vr, float bias) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < kHeadDim; ++e) s = fmaf(qv[e], kr[e], s);
+        const float z = s * a.sl2 + bias;
+        const float mn = fmaxf(m, z);
+        const float alpha = exp2f(m - mn);
+        const float p = exp2f(z - mn);
+        l = l * alpha + p;
+#pragma unroll
+        for (int e = 0; e < kHeadDim; ++e) acc[e] = acc[e] * alpha + p * vr[e];
+        m = mn;
+    };
+    const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
+    for (int j = 0; j < a.K1; ++j) {
+        const int f = fine[j];
+        for (int t = 0; t < kBlock; ++t) {
+            const int64_t u = (int64_t)f * kBlock + t;
+            attend(k + head_off + u * kHeadDim, v + head_off + u * kHeadDim, 0.f);
+        }
+    }
+    for (int e = 0; e < a.ncoarse; ++e) {
+        int64_t roff;
+        float b;
+        if (coarse_entry(a, idx, fine, h, ib, e, roff, b)) attend(pk + roff, pv + roff, b);
+    }
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int e = 0; e < kHeadDim; ++e) o[head_off + (int64_t)tok * kHeadDim + e] = acc[e] * inv;
+    lse[tq] = (m + log2f(l)) * kLn2;
+}
+
+hipError_t launch_attn_fwd(const Geometry &g, const void *q, const void *k, const void *v,
+                           const float *pk, const float *pv, const int32_t *idx, void *o,
+                           float *lse, hipStream_t s) {
+    const FwdArgs a = make_fwd_args(g);
+    if (g.bf16) {
+        const int64_t blocks = (int64_t)g.bh * g.n[1];
+        hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3((unsigned)((blocks + 3) / 4)), dim3(256), 0,
+                           s, (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx,
+                           (__bf16 *)o, lse, a);
+    } else {
+        const int64_t total = (int64_t)g.bh * g.N;
+        hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                           s, (const float *)q, (const float *)k, (const float *)v, pk, pv, idx,
+                           (float *)o, lse, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace llsa

@@ -1,0 +1,96 @@
+// Device-side helpers shared by the gfx950 kernels of the LLSA library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace llsa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 lds_bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+
+constexpr int kHeadDim = 64;   // supported head dimension
+constexpr int kBlock = 16;     // supported block size B (= one MFMA tile edge)
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+#define LLSA_LDS __attribute__((address_space(3)))
+
+// 16x16 output += A(16 x 32) * B(32 x 16), bf16 in, f32 accumulate.
+// Lane l holds A[l%16][k-slots of group l/16] and B[k-slots][l%16];
+// result C[m][n] sits in lane n + 16*(m/4), register m%4.
+__device__ __forceinline__ f32x4 mfma_bf16_32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// Same with 4 k-slots per lane (16 x 16 x 16).
+__device__ __forceinline__ f32x4 mfma_bf16_16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                      __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+// f32: one k-slot per lane (16 x 16 x 4).
+__device__ __forceinline__ f32x4 mfma_f32_4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read of 4 bf16: within each 16-lane group, lane i receives
+// element i%4 of the 8-byte chunks addressed by lanes i/4, i/4+4, i/4+8, i/4+12.
+// Pointing lane s of group g at M[r0 + s/4][c0 + 4*(s%4)] of a row-major bf16
+// matrix M therefore hands lane i the column M[r0 .. r0+3][c0 + i].
+__device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16 *p) {
+    lds_bf16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LLSA_LDS lds_bf16x4 *)(p));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const __bf16 *p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ void store_bf16x8(__bf16 *p, bf16x8 v) {
+    *reinterpret_cast<u32x4 *>(p) = __builtin_bit_cast(u32x4, v);
+}
+
+__device__ __forceinline__ bf16x8 f32_to_bf16x8(f32x4 a, f32x4 b) {
+    return bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
+                  (__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]};
+}
+
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+}
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+__device__ __forceinline__ uint32_t shfl_xor_u(uint32_t v, int m) {
+    return (uint32_t)__shfl_xor((int)v, m, kWave);
+}
+
+// Orders the 4 lanes {l, l^16, l^32, l^48} that share one query in the
+// transposed score layout.
+__device__ __forceinline__ float max4_groups(float v) {
+    v = fmaxf(v, shfl_xor_f(v, 16));
+    v = fmaxf(v, shfl_xor_f(v, 32));
+    return v;
+}
+__device__ __forceinline__ float sum4_groups(float v) {
+    v += shfl_xor_f(v, 16);
+    v += shfl_xor_f(v, 32);
+    return v;
+}
+
+// Wave-scope ordering for data exchanged through LDS by lanes of one wave.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace llsa

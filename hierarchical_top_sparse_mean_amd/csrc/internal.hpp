@@ -1,0 +1,48 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace llsa {
+
+constexpr int kMaxLevels = 6;
+
+// Resolved problem geometry, computed once on the host by the C ABI layer.
+struct Geometry {
+    int bh;                          // batch * heads
+    int N;                           // tokens
+    int L;                           // pooling steps
+    int K;                           // requested picks
+    int Le;                          // enrichment depth (coarse levels 2..Le+1)
+    int n[kMaxLevels + 1];           // tokens per level, n[0] = N
+    int kl[kMaxLevels + 1];          // picks per level
+    int64_t pyr_off[kMaxLevels + 2]; // float offset of level l in a pyramid
+    int64_t idx_off[kMaxLevels + 2]; // int32 offset of level l in the index buffer
+    int64_t ptr_off[kMaxLevels + 2]; // int32 offset of level l CSR ptr
+    int64_t col_off[kMaxLevels + 2]; // int32 offset of level l CSR col
+    float scale;
+    int drop_covered;
+    bool bf16;                       // input dtype
+    bool grad_bf16;                  // gradient dtype
+};
+
+hipError_t launch_pool(const Geometry &g, const void *q, const void *k, const void *v,
+                       float *pq, float *pk, float *pv, hipStream_t s);
+hipError_t launch_select(const Geometry &g, const float *pq, const float *pk, int32_t *idx,
+                         hipStream_t s);
+hipError_t launch_attn_fwd(const Geometry &g, const void *q, const void *k, const void *v,
+                           const float *pk, const float *pv, const int32_t *idx, void *o,
+                           float *lse, hipStream_t s);
+size_t transpose_workspace_bytes(int nb, int rows, int k, int cols);
+hipError_t launch_transpose(int nb, int rows, int k, int cols, const int32_t *idx,
+                            int32_t *ptr, int32_t *col, void *ws, hipStream_t s);
+size_t bwd_workspace_bytes(const Geometry &g);
+hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, const void *v,
+                           const float *pk, const float *pv, const int32_t *idx,
+                           const int32_t *csr_ptr, const int32_t *csr_col, const void *o,
+                           const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                           void *ws, hipStream_t s);
+hipError_t launch_dense_fwd(int bh, int N, float scale, const void *q, const void *k,
+                            const void *v, void *o, float *lse, hipStream_t s);
+
+}  // namespace llsa

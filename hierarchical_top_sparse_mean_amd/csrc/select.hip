@@ -1,0 +1,220 @@
+// Hierarchical Top-K selection ("Trainable Log-linear Sparse Attention for
+// Efficient Diffusion Transformers", explainer "Step 2: Hierarchical Top-K
+// Selection"): dense scores at the coarsest level, then at every finer level
+// only the B children of the parent's picks are scored.
+//
+// One wave serves 16 query rows that share their candidates: at a finer level
+// these are the 16 children of one parent, whose candidate list is the
+// children of the parent's K picks (K tiles of 16 contiguous pooled keys); at
+// the coarsest level a 16-row slice against all keys.  Scores are float32 on
+// the matrix cores (v_mfma_f32_16x16x4_f32), computed transposed so that lane
+// l owns query l%16 and 4 candidates of each 16-candidate tile.  Top-K runs in
+// registers on 64-bit keys (order-preserving score bits, inverted index), so
+// one unsigned compare orders by score and breaks ties toward the lower index:
+// every lane sorts its candidates in groups of KM with bitonic networks and
+// merges them into a running top-KM list, then the 4 lanes of a query merge
+// their lists through two butterfly exchanges.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace llsa {
+
+__device__ __forceinline__ uint64_t score_key(float s, uint32_t idx) {
+    uint32_t u = __builtin_bit_cast(uint32_t, s);
+    if (s == 0.0f) u = 0u;  // -0 and +0 compare equal
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint64_t)(~idx);
+}
+
+template <int N>
+__device__ __forceinline__ void sort_desc(uint64_t (&a)[N]) {
+#pragma unroll
+    for (int k = 2; k <= N; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int p = i ^ j;
+                if (p > i) {
+                    const bool desc = (i & k) == 0;
+                    const uint64_t x = a[i], y = a[p];
+                    const bool sw = desc ? (x < y) : (x > y);
+                    a[i] = sw ? y : x;
+                    a[p] = sw ? x : y;
+                }
+            }
+}
+
+// r, g sorted descending; r becomes the N largest of both, descending.
+template <int N>
+__device__ __forceinline__ void merge_top(uint64_t (&r)[N], const uint64_t (&g)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const uint64_t y = g[N - 1 - i];
+        r[i] = r[i] > y ? r[i] : y;
+    }
+#pragma unroll
+    for (int j = N >> 1; j > 0; j >>= 1)
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int p = i ^ j;
+            if (p > i) {
+                const uint64_t x = r[i], y = r[p];
+                r[i] = x < y ? y : x;
+                r[p] = x < y ? x : y;
+            }
+        }
+}
+
+template <int N>
+__device__ __forceinline__ void sort_asc_u32(uint32_t (&a)[N]) {
+#pragma unroll
+    for (int k = 2; k <= N; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int p = i ^ j;
+                if (p > i) {
+                    const bool asc = (i & k) == 0;
+                    const uint32_t x = a[i], y = a[p];
+                    const bool sw = asc ? (x > y) : (x < y);
+                    a[i] = sw ? y : x;
+                    a[p] = sw ? x : y;
+                }
+            }
+}
+
+constexpr int kSelTilesPerChunk = 8;
+
+// parent == nullptr: coarsest level, candidates 0..n-1, row groups are
+// 16-row slices.  Otherwise: row group p = the 16 children of parent p,
+// candidates = children of parent[p][0..kp).
+template <int KM>
+__global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ ql,
+                                                     const float *__restrict__ kl,
+                                                     const int32_t *__restrict__ parent,
+                                                     int32_t *__restrict__ out, int n, int kout,
+                                                     int kp, int groups_per_head,
+                                                     int64_t groups_total) {
+    const int64_t gid = (int64_t)blockIdx.x * 4 + wave_id();
+    if (gid >= groups_total) return;
+    const int h = (int)(gid / groups_per_head);
+    const int gi = (int)(gid % groups_per_head);
+    const int lane = lane_id();
+    const int g = lane >> 4, col = lane & 15;
+
+    const float *qh = ql + (int64_t)h * n * kHeadDim;
+    const float *kh = kl + (int64_t)h * n * kHeadDim;
+    const int row = gi * kBlock + col;
+    const bool row_ok = row < n;
+
+    float qf[16];
+    {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(qh + (int64_t)(row_ok ? row : 0) * kHeadDim + 16 * g);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f32x4 t = row_ok ? src[j] : f32x4{0.f, 0.f, 0.f, 0.f};
+            qf[4 * j] = t[0];
+            qf[4 * j + 1] = t[1];
+            qf[4 * j + 2] = t[2];
+            qf[4 * j + 3] = t[3];
+        }
+    }
+
+    const bool dense = parent == nullptr;
+    const int ntiles = dense ? (n + kBlock - 1) / kBlock : kp;
+    const int32_t *prow = dense ? nullptr : parent + ((int64_t)h * groups_per_head + gi) * kp;
+
+    uint64_t best[KM];
+#pragma unroll
+    for (int i = 0; i < KM; ++i) best[i] = 0;
+
+    for (int t0 = 0; t0 < ntiles; t0 += kSelTilesPerChunk) {
+        uint64_t keys[4 * kSelTilesPerChunk];
+#pragma unroll
+        for (int t = 0; t < kSelTilesPerChunk; ++t) {
+            const int tile = t0 + t;
+            if (tile < ntiles) {
+                const int base = dense ? tile * kBlock : __builtin_amdgcn_readfirstlane(prow[tile]) * kBlock;
+                const int cand = base + col;
+                const bool cok = cand < n;
+                const f32x4 *src = reinterpret_cast<const f32x4 *>(kh + (int64_t)(cok ? cand : 0) * kHeadDim + 16 * g);
+                float kf[16];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    f32x4 tt = cok ? src[j] : f32x4{0.f, 0.f, 0.f, 0.f};
+                    kf[4 * j] = tt[0];
+                    kf[4 * j + 1] = tt[1];
+                    kf[4 * j + 2] = tt[2];
+                    kf[4 * j + 3] = tt[3];
+                }
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 16; ++s) acc = mfma_f32_4(kf[s], qf[s], acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = base + 4 * g + i;
+                    keys[4 * t + i] = (c < n) ? score_key(acc[i], (uint32_t)c) : 0ull;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) keys[4 * t + i] = 0ull;
+            }
+        }
+#pragma unroll
+        for (int grp = 0; grp < 4 * kSelTilesPerChunk / KM; ++grp) {
+            uint64_t part[KM];
+#pragma unroll
+            for (int i = 0; i < KM; ++i) part[i] = keys[grp * KM + i];
+            sort_desc<KM>(part);
+            merge_top<KM>(best, part);
+        }
+    }
+    // the 4 lanes holding one query merge their lists
+#pragma unroll
+    for (int m = 16; m <= 32; m <<= 1) {
+        uint64_t other[KM];
+#pragma unroll
+        for (int i = 0; i < KM; ++i) {
+            const uint32_t lo = shfl_xor_u((uint32_t)best[i], m);
+            const uint32_t hi = shfl_xor_u((uint32_t)(best[i] >> 32), m);
+            other[i] = ((uint64_t)hi << 32) | lo;
+        }
+        merge_top<KM>(best, other);
+    }
+    uint32_t sel[KM];
+#pragma unroll
+    for (int i = 0; i < KM; ++i) sel[i] = (i < kout) ? ~(uint32_t)best[i] : 0xffffffffu;
+    sort_asc_u32<KM>(sel);
+    if (g == 0 && row_ok) {
+        int32_t *dst = out + ((int64_t)h * n + row) * kout;
+#pragma unroll
+        for (int i = 0; i < KM; ++i)
+            if (i < kout) dst[i] = (int32_t)sel[i];
+    }
+}
+
+hipError_t launch_select(const Geometry &g, const float *pq, const float *pk, int32_t *idx,
+                         hipStream_t s) {
+    for (int l = g.L; l >= 1; --l) {
+        const bool dense = (l == g.L);
+        const int n = g.n[l];
+        const int gph = dense ? (n + kBlock - 1) / kBlock : n / kBlock;
+        const int64_t total = (int64_t)g.bh * gph;
+        const int32_t *parent = dense ? nullptr : idx + g.idx_off[l + 1];
+        const int kp = dense ? 0 : g.kl[l + 1];
+        const dim3 grid((unsigned)((total + 3) / 4));
+        if (g.K <= 8)
+            hipLaunchKernelGGL(select_kernel<8>, grid, dim3(256), 0, s, pq + g.pyr_off[l],
+                               pk + g.pyr_off[l], parent, idx + g.idx_off[l], n, g.kl[l], kp, gph,
+                               total);
+        else
+            hipLaunchKernelGGL(select_kernel<16>, grid, dim3(256), 0, s, pq + g.pyr_off[l],
+                               pk + g.pyr_off[l], parent, idx + g.idx_off[l], n, g.kl[l], kp, gph,
+                               total);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace llsa

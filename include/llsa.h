@@ -17,9 +17,11 @@
  *    stream) and returns.  It keeps no global state and is thread-safe.
  *  - Q, K, V, O, dO are [batch, heads, seq_len, head_dim] in `dtype`.
  *  - Level l = 1..L has n_l = seq_len / block^l tokens; level 0 is the input.
- *    Pyramids are float32, levels stored one after the other:
+ *    Pyramids are float32, levels stored in order, each starting on a
+ *    64-byte boundary:
  *        level l at float offset sizes.pyramid_offset[l], shape [batch*heads, n_l, d].
- *  - Index lists are int32, levels stored one after the other:
+ *  - Index lists are int32, levels stored in order, each starting on a
+ *    64-byte boundary:
  *        level l at offset sizes.index_offset[l], shape [batch*heads, n_l, K_l],
  *    with K_L = min(K, n_L) and K_l = min(K, B*K_{l+1}) for l < L; every row
  *    holds distinct indices in ascending order.
@@ -77,6 +79,7 @@ typedef struct llsa_sizes {
     int64_t index_offset[LLSA_MAX_LEVELS + 2];   /* int32 offset of level l             */
     int64_t csr_ptr_elems;                       /* int32s of all CSR ptr arrays        */
     int64_t csr_ptr_offset[LLSA_MAX_LEVELS + 2]; /* level l: [batch*heads, n_l + 1]     */
+                                                 /* (CSR levels also 64-byte aligned)   */
     int64_t csr_col_elems;                       /* int32s of all CSR col arrays        */
     int64_t csr_col_offset[LLSA_MAX_LEVELS + 2]; /* level l: [batch*heads, n_l * K_l]   */
     int64_t lse_elems;                           /* floats of lse: batch*heads*seq_len  */

@@ -264,12 +264,13 @@ static int kv_capacity(int B, int L, const int *kl, int Le)
     return cap;
 }
 
-/* o[bh][N][d], lse[bh][N] (natural log). */
+/* o[bh][N][d], lse[bh][N] (natural log).  blockmask (NULL = all) selects the
+ * query blocks [bh][N/B] to compute; rows of other blocks are left untouched. */
 void oracle_attn_fwd(int bh, int N, int d, int B, int L, int K, int Le, double scale,
                      int drop_covered,
                      const double *q, const double *k, const double *v,
                      const double *pyr_k, const double *pyr_v, const int32_t *idx,
-                     double *o, double *lse)
+                     const uint8_t *blockmask, double *o, double *lse)
 {
     int kl[64];
     level_k(N, B, L, K, kl);
@@ -277,6 +278,7 @@ void oracle_attn_fwd(int bh, int N, int d, int B, int L, int K, int Le, double s
     int cap = kv_capacity(B, L, kl, Le);
 #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t blk = 0; blk < (int64_t)bh * n1; ++blk) {
+        if (blockmask && !blockmask[blk]) continue;
         int h = (int)(blk / n1);
         int64_t i = blk % n1;
         kv_t *kv = (kv_t *)malloc(sizeof(kv_t) * cap);
@@ -314,11 +316,15 @@ void oracle_attn_fwd(int bh, int N, int d, int B, int L, int K, int Le, double s
  * query with plain accumulation; pooled-token gradients are gathered per
  * level and pushed back through the mean: each of the B^l tokens under a
  * level-l token receives 1/B^l of its gradient.
+ * blockmask (NULL = all) restricts the loss to the rows of the selected query
+ * blocks [bh][N/B]: dK, dV are then exact for every key whose attending
+ * query blocks are all selected.
  */
 void oracle_attn_bwd(int bh, int N, int d, int B, int L, int K, int Le, double scale,
                      int drop_covered,
                      const double *q, const double *k, const double *v,
                      const double *pyr_k, const double *pyr_v, const int32_t *idx,
+                     const uint8_t *blockmask,
                      const double *dout, double *dq, double *dk, double *dv)
 {
     int kl[64];
@@ -338,6 +344,7 @@ void oracle_attn_bwd(int bh, int N, int d, int B, int L, int K, int Le, double s
         double *p = (double *)malloc(sizeof(double) * cap);
         double *ot = (double *)malloc(sizeof(double) * d);
         for (int64_t i = 0; i < n1; ++i) {
+            if (blockmask && !blockmask[(int64_t)h * n1 + i]) continue;
             int cnt = build_kv(h, i, N, d, B, L, kl, Le, drop_covered, k, v, pyr_k, pyr_v, idx, bh, kv);
             for (int t = 0; t < B; ++t) {
                 int64_t tok = i * B + t;

@@ -49,10 +49,11 @@ def _load():
         lib.oracle_select_level.argtypes = [i, i, i, i, i, _dp, _dp, _ip, i, _ip, _dp]
         lib.oracle_select_level.restype = i
         lib.oracle_select.argtypes = [i, i, i, i, i, i, _dp, _dp, _ip, _dp]
+        u8 = ctypes.POINTER(ctypes.c_uint8)
         lib.oracle_attn_fwd.argtypes = [i, i, i, i, i, i, i, d, i, _dp, _dp, _dp, _dp, _dp,
-                                        _ip, _dp, _dp]
+                                        _ip, u8, _dp, _dp]
         lib.oracle_attn_bwd.argtypes = [i, i, i, i, i, i, i, d, i, _dp, _dp, _dp, _dp, _dp,
-                                        _ip, _dp, _dp, _dp, _dp]
+                                        _ip, u8, _dp, _dp, _dp, _dp]
         lib.oracle_transpose.argtypes = [i, i, i, i, _ip, _ip, _ip]
         lib.oracle_transpose.restype = i
         _lib = lib
@@ -141,9 +142,17 @@ def _flat_idx(levels):
     return np.ascontiguousarray(np.concatenate([_i32(a).ravel() for a in levels]))
 
 
+def _mask(blockmask):
+    if blockmask is None:
+        return None, None
+    m = np.ascontiguousarray(np.asarray(blockmask, dtype=np.uint8))
+    return m, m.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+
+
 def attn_fwd(q, k, v, pyr_k, pyr_v, idx, B: int, K: int, Le: int, scale: float,
-             drop_covered: bool = True):
+             drop_covered: bool = True, blockmask=None):
     """Step 3.  q,k,v: [bh, N, d]; pyramids / idx: lists level 1..L.
+    blockmask [bh, N/B] (optional) selects the query blocks to compute (others are 0).
 
     Returns (o [bh, N, d], lse [bh, N])."""
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -152,15 +161,17 @@ def attn_fwd(q, k, v, pyr_k, pyr_v, idx, B: int, K: int, Le: int, scale: float,
     pk, pv, ii = _flat_pyr(pyr_k), _flat_pyr(pyr_v), _flat_idx(idx)
     o = np.zeros((bh, N, d))
     lse = np.zeros((bh, N))
+    m, mp = _mask(blockmask)
     _load().oracle_attn_fwd(bh, N, d, B, L, K, Le, float(scale), int(drop_covered),
                             _p(q, _dp), _p(k, _dp), _p(v, _dp), _p(pk, _dp), _p(pv, _dp),
-                            _p(ii, _ip), _p(o, _dp), _p(lse, _dp))
+                            _p(ii, _ip), mp, _p(o, _dp), _p(lse, _dp))
     return o, lse
 
 
 def attn_bwd(q, k, v, pyr_k, pyr_v, idx, dout, B: int, K: int, Le: int, scale: float,
-             drop_covered: bool = True):
-    """Gradients of <O, dO> for fixed picks.  Returns (dq, dk, dv), each [bh, N, d]."""
+             drop_covered: bool = True, blockmask=None):
+    """Gradients of <O, dO> for fixed picks.  Returns (dq, dk, dv), each [bh, N, d].
+    blockmask [bh, N/B] (optional) keeps only those query blocks' rows in the loss."""
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     bh, N, d = q.shape
     L = len(pyr_k)
@@ -168,9 +179,10 @@ def attn_bwd(q, k, v, pyr_k, pyr_v, idx, dout, B: int, K: int, Le: int, scale: f
     dq = np.zeros((bh, N, d))
     dk = np.zeros((bh, N, d))
     dv = np.zeros((bh, N, d))
+    m, mp = _mask(blockmask)
     _load().oracle_attn_bwd(bh, N, d, B, L, K, Le, float(scale), int(drop_covered),
                             _p(q, _dp), _p(k, _dp), _p(v, _dp), _p(pk, _dp), _p(pv, _dp),
-                            _p(ii, _ip), _p(dout, _dp), _p(dq, _dp), _p(dk, _dp), _p(dv, _dp))
+                            _p(ii, _ip), mp, _p(dout, _dp), _p(dq, _dp), _p(dk, _dp), _p(dv, _dp))
     return dq, dk, dv
 
 

@@ -1,0 +1,173 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Bar: pyramids within 1e-5; indices bit-exact except near-ties of the
+oracle (gap below 1e-5 relative, counted) and rows under a differing parent;
+outputs and gradients within 1e-4 (float32 inputs) / 2e-2 (bfloat16 inputs)
+max-abs; the CSR transpose exact.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU-only hosts, never run there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from hierarchical_top_sparse_mean_amd import llsa as L  # noqa: E402
+from hierarchical_top_sparse_mean_amd.inputs import WORKLOADS  # noqa: E402
+from oracle import oracle as O  # noqa: E402
+
+from parity_util import Case, check_case, check_csr_valid, run_gpu  # noqa: E402
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _workload_case(name):
+    w = WORKLOADS[name]
+    return Case(w.batch, w.heads, w.seq_len, w.dtype, w.levels, w.topk, w.enrich,
+                backward=w.backward, sinus=w.sinusoid)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_parity(name):
+    _log(f"[parity] workload {name}")
+    summ = check_case(_workload_case(name))
+    _log(f"[parity] {name}: {summ}")
+
+
+# ------------------------------------------------------------- edge cases --
+EDGE = [
+    # (batch, heads, N, dtype, L, K, Le, backward, extra)
+    (1, 2, 768, torch.bfloat16, 2, 2, 1, True, {}),        # 3 coarsest tokens: ragged dense tile
+    (1, 3, 16 * 21, torch.bfloat16, 1, 5, 0, True, {}),    # single level, 21 blocks, odd K
+    (2, 1, 16 * 21, torch.float32, 1, 3, 0, True, {}),     # single level, f32
+    (1, 2, 8192, torch.bfloat16, 3, 2, 2, True, {}),       # three pooling steps, two coarse levels
+    (1, 2, 8192, torch.float32, 3, 2, 2, True, {}),
+    (1, 2, 4096, torch.bfloat16, 2, 8, 0, True, {}),       # no enrichment
+    (1, 2, 4096, torch.bfloat16, 2, 1, 1, True, {}),       # K = 1
+    (1, 2, 4096, torch.bfloat16, 2, 16, 1, True, {}),      # K = 16 (largest supported)
+    (1, 2, 4096, torch.bfloat16, 2, 3, 1, True, {"drop_covered": False}),
+    (2, 2, 2048, torch.bfloat16, 2, 4, 1, True, {"grad_dtype": torch.bfloat16}),
+    (1, 1, 256, torch.bfloat16, 2, 16, 1, True, {}),       # K = all blocks (dense reduction)
+    (1, 1, 256, torch.float32, 2, 16, 1, True, {}),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"b{e[0]}h{e[1]}N{e[2]}{str(e[3])[6:]}L{e[4]}K{e[5]}Le{e[6]}{'-'.join(e[8])}" for e in EDGE])
+def test_edge_parity(case):
+    b, h, N, dt, L_, K, Le, bwd, extra = case
+    _log(f"[parity] edge {case}")
+    c = Case(b, h, N, dt, L_, K, Le, backward=bwd, **extra)
+    summ = check_case(c)
+    _log(f"[parity] edge done {summ}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_all_blocks_is_dense_attention(dtype):
+    # K = every level-1 block: covered coarse picks are dropped and the result
+    # is plain softmax attention (checked against a float64 textbook formula)
+    _log(f"[parity] dense reduction {dtype}")
+    c = Case(1, 2, 256, dtype, 2, 16, 1, backward=False)
+    g = run_gpu(c)
+    q = c.q.double().numpy().reshape(2, 256, 64)
+    k = c.k.double().numpy().reshape(2, 256, 64)
+    v = c.v.double().numpy().reshape(2, 256, 64)
+    s = np.einsum("hqd,hkd->hqk", q, k) / 8.0
+    p = np.exp(s - s.max(-1, keepdims=True))
+    want = np.einsum("hqk,hkd->hqd", p / p.sum(-1, keepdims=True), v)
+    assert np.abs(g["o"] - want).max() <= (1e-4 if dtype == torch.float32 else 2e-2)
+
+
+def test_q_zero_closed_form_bitexact_picks():
+    # Q = 0: every score is 0 in any precision, ties go to the lowest index at
+    # every level, O is the mean of V over the attended multiset of tokens
+    _log("[parity] q=0 closed form")
+    N, K = 4096, 8
+    base = Case(1, 2, N, torch.bfloat16, 2, K, 1, backward=False)
+    c = Case(1, 2, N, torch.bfloat16, 2, K, 1, q=torch.zeros(1, 2, N, 64), k=base.k, v=base.v,
+             backward=False)
+    g = run_gpu(c)
+    for lv in g["idx"]:
+        assert (lv == np.arange(K)).all()
+    v = c.v.double().numpy().reshape(2, N, 64)
+    toks = list(range(K * 16)) + list(range(K * 256))
+    want = v[:, toks].mean(axis=1)
+    assert np.abs(g["o"] - want[:, None, :]).max() <= 2e-2
+    assert np.abs(g["lse"] - np.log(len(toks))).max() <= 1e-5
+
+
+def test_constant_values_give_that_value():
+    _log("[parity] constant V")
+    N = 4096
+    base = Case(1, 2, N, torch.bfloat16, 2, 8, 1, backward=False)
+    vals = torch.randn(64, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    c = Case(1, 2, N, torch.bfloat16, 2, 8, 1, q=base.q, k=base.k,
+             v=vals.float().expand(1, 2, N, 64).contiguous(), backward=False)
+    g = run_gpu(c)
+    assert np.abs(g["o"] - vals.double().numpy()).max() <= 2e-2
+
+
+def test_deterministic_bitwise():
+    # two runs of the whole path give identical bytes (no float atomics)
+    _log("[parity] determinism")
+    c = Case(1, 4, 4096, torch.bfloat16, 2, 8, 1, backward=True, sinus=True)
+    a = run_gpu(c)
+    b = run_gpu(c)
+    for key in ("o", "lse", "dq", "dk", "dv"):
+        assert np.array_equal(a[key], b[key]), key
+    for x, y in zip(a["idx"], b["idx"]):
+        assert np.array_equal(x, y)
+
+
+# ------------------------------------------------------------- transpose --
+@pytest.mark.parametrize("nb,rows,k,cols", [(3, 100, 8, 100), (2, 4096, 8, 4096), (1, 37, 5, 23),
+                                            (4, 64, 1, 64), (1, 16384, 8, 32768), (2, 50, 16, 1000)])
+def test_transpose_parity(nb, rows, k, cols):
+    _log(f"[parity] transpose {nb} {rows} {k} {cols}")
+    rng = np.random.default_rng(rows * 31 + k)
+    # skewed picks: half of the rows favour a few hot keys -> long and empty segments
+    idx = np.empty((nb, rows, k), dtype=np.int32)
+    hot = rng.choice(cols, size=min(cols, 2 * k), replace=False)
+    for b in range(nb):
+        for r in range(rows):
+            pool = hot if (r % 2 == 0 and len(hot) >= k) else np.arange(cols)
+            idx[b, r] = np.sort(rng.choice(pool, size=k, replace=False))
+    ptr_o, col_o = O.transpose(idx, cols)
+    d_idx = torch.from_numpy(idx).cuda()
+    ptr = torch.empty((nb, cols + 1), dtype=torch.int32, device="cuda")
+    col = torch.empty((nb, rows * k), dtype=torch.int32, device="cuda")
+    ws_bytes = L.llsa_index_transpose_workspace(nb, rows, k, cols)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    L.llsa_index_transpose(nb, rows, k, cols, d_idx, ptr, col, ws, ws_bytes)
+    torch.cuda.synchronize()
+    assert np.array_equal(ptr.cpu().numpy(), ptr_o)
+    assert np.array_equal(col.cpu().numpy(), col_o)
+    check_csr_valid(idx, ptr.cpu().numpy(), col.cpu().numpy())
+
+
+def test_dense_comparator_matches_oracle_dense():
+    # the full-attention comparator against K = all blocks in the oracle
+    _log("[parity] dense comparator")
+    N = 1024
+    c = Case(1, 2, N, torch.bfloat16, 2, N // 16, 1, backward=False, sinus=True)
+    p = L.problem(1, 2, N, dtype=torch.bfloat16)
+    o = torch.empty(1, 2, N, 64, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(2 * N, dtype=torch.float32, device="cuda")
+    L.llsa_dense_attn_fwd(p, c.q.cuda(), c.k.cuda(), c.v.cuda(), o, lse)
+    torch.cuda.synchronize()
+    q = c.q.double().numpy().reshape(2, N, 64)
+    k = c.k.double().numpy().reshape(2, N, 64)
+    v = c.v.double().numpy().reshape(2, N, 64)
+    s = np.einsum("hqd,hkd->hqk", q, k) / 8.0
+    m = s.max(-1, keepdims=True)
+    pr = np.exp(s - m)
+    want = np.einsum("hqk,hkd->hqd", pr / pr.sum(-1, keepdims=True), v)
+    want_lse = (m[..., 0] + np.log(pr.sum(-1)))
+    assert np.abs(o.float().cpu().numpy().reshape(2, N, 64) - want).max() <= 2e-2
+    assert np.abs(lse.cpu().numpy().reshape(2, N) - want_lse).max() <= 2e-2

@@ -1,0 +1,266 @@
+"""Benchmark of the log-linear sparse attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+pool -> select -> sparse attention forward -> index transpose (levels 1..Le+1)
+-> backward, each through the C ABI on the current stream.  Inputs are
+resident in HBM before the timed region.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload n65536_bf16]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3
+METRIC = "LLSA fwd+bwd tokens/sec at N=65536, K=8; % bf16 MFMA peak; sel GB/s"
+
+
+def algorithmic(w, s):
+    """Compulsory HBM bytes and useful FLOPs per call (see the derivation in the
+    design notes): every tensor the call must read or write, once."""
+    bh, N, d = w.bh, w.seq_len, w.head_dim
+    e = 2 if str(w.dtype) == "torch.bfloat16" else 4
+    L = w.levels
+    n = [s.level_tokens[l] for l in range(L + 1)]
+    kl = [0] + [s.level_k[l] for l in range(1, L + 1)]
+    Le = s.enrich
+    pyr = sum(bh * n[l] * d * 4 for l in range(1, L + 1))
+    idx = sum(bh * n[l] * kl[l] * 4 for l in range(1, L + 1))
+    tok = bh * N * d * e
+    coarse_pyr = sum(bh * n[l] * d * 4 for l in range(2, Le + 2))
+    nkv = kl[1] * 16 + sum(kl[l] for l in range(2, Le + 2))
+    out = {}
+    out["pool"] = dict(bytes=3 * tok + 3 * pyr, flops=0)
+    sel_bytes = 2 * bh * n[L] * d * 4 + bh * n[L] * kl[L] * 4
+    sel_flops = 2 * d * bh * n[L] * n[L]
+    for l in range(L - 1, 0, -1):
+        sel_bytes += 2 * bh * n[l] * d * 4 + bh * n[l + 1] * kl[l + 1] * 4 + bh * n[l] * kl[l] * 4
+        sel_flops += 2 * d * bh * n[l] * kl[l + 1] * 16
+    out["select"] = dict(bytes=sel_bytes, flops=sel_flops)
+    out["attn_fwd"] = dict(bytes=4 * tok + bh * N * 4 + 2 * coarse_pyr + idx,
+                           flops=4 * bh * N * d * nkv)
+    tr = 0
+    for l in range(1, Le + 2):
+        tr += bh * n[l] * kl[l] * 4 + bh * (n[l] + 1) * 4 + bh * n[l] * kl[l] * 4
+    out["transpose"] = dict(bytes=tr, flops=0)
+    g = 4  # float32 gradients
+    out["attn_bwd"] = dict(bytes=4 * tok + 3 * bh * N * d * g + 3 * bh * N * 4 + 2 * coarse_pyr + idx + tr,
+                           flops=int(2.5 * 4 * bh * N * d * nkv))
+    return out, nkv
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(w, max_heads):
+    """The fp64 CPU oracle, untouched, on the first heads of the same workload."""
+    import numpy as np
+    import torch
+    from hierarchical_top_sparse_mean_amd.inputs import make_inputs
+    from oracle import oracle as O
+    cores = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    threads = min(cores, int(omp)) if omp else cores
+    heads = max(1, min(w.heads, max_heads, threads))
+    q, k, v, do = make_inputs(1, heads, w.seq_len, w.head_dim, w.dtype, w.sinusoid, True, 0)
+    q, k, v, do = (x.double().numpy().reshape(heads, w.seq_len, w.head_dim) for x in (q, k, v, do))
+    B, L, K = w.block, w.levels, w.topk
+    t0 = time.perf_counter()
+    pq, pk, pv = O.pool(q, B, L), O.pool(k, B, L), O.pool(v, B, L)
+    idx, _ = O.select(pq, pk, B, K)
+    O.attn_fwd(q, k, v, pk, pv, idx, B, K, w.enrich, w.scale)
+    for l in range(1, w.enrich + 2):
+        O.transpose(idx[l - 1], w.seq_len // B ** l)
+    O.attn_bwd(q, k, v, pk, pv, idx, do, B, K, w.enrich, w.scale)
+    dt = time.perf_counter() - t0
+    tokens = heads * w.seq_len          # batch 1
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} of {w.heads} heads x {w.seq_len} tokens, pool+select+fwd+transpose+bwd "
+                      f"in fp64 ({dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="n65536_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the operator shards by (batch, head) with no "
+              "communication, and this build runs on a single MI355X; use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from hierarchical_top_sparse_mean_amd import llsa as L
+    from hierarchical_top_sparse_mean_amd.inputs import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                          "launches": 3}))
+        return
+    q, k, v, dout = workload_inputs(w)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    dout = dout.to(dev) if dout is not None else None
+    p = L.problem(w.batch, w.heads, w.seq_len, w.head_dim, w.block, w.levels, w.topk, w.enrich,
+                  w.dtype, torch.float32)
+    B = L.Buffers(p, backward=w.backward)
+    s = B.s
+    bh = w.bh
+    calls = ["pool", "select", "attn_fwd"] + (["transpose", "attn_bwd"] if w.backward else [])
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        L.llsa_pool(p, q, k, v, B.pyr_q, B.pyr_k, B.pyr_v)
+        mark(1)
+        L.llsa_select(p, B.pyr_q, B.pyr_k, B.idx)
+        mark(2)
+        L.llsa_attn_fwd(p, q, k, v, B.pyr_k, B.pyr_v, B.idx, B.o, B.lse)
+        mark(3)
+        if w.backward:
+            for l in range(1, s.enrich + 2):
+                ptr, col = B.csr_level(l)
+                L.llsa_index_transpose(bh, s.level_tokens[l], s.level_k[l], s.level_tokens[l],
+                                       B.index_level(l), ptr, col, B.tws, B.tws_bytes)
+            mark(4)
+            L.llsa_attn_bwd(p, q, k, v, B.pyr_k, B.pyr_v, B.idx, B.csr_ptr, B.csr_col, B.o, B.lse,
+                            dout, B.dq, B.dk, B.dv, B.ws, B.ws.numel())
+            mark(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    nev = len(calls) + 1
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    per_call = {c: sum(events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)) / args.steps
+                for j, c in enumerate(calls)}
+    tokens = w.batch * w.seq_len
+    value = tokens / (ms_per_step / 1e3)
+
+    alg, nkv = algorithmic(w, s)
+    detail = {}
+    for c in calls:
+        ms = per_call[c]
+        a = alg[c]
+        detail[c] = {"ms": round(ms, 4), "GB/s": round(a["bytes"] / ms / 1e6, 1),
+                     "hbm_frac": round(a["bytes"] / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        if a["flops"]:
+            detail[c]["TFLOP/s"] = round(a["flops"] / ms / 1e9, 2)
+    for c in ("attn_fwd", "attn_bwd"):
+        if c in detail:
+            detail[c]["bf16_mfma_frac"] = round(detail[c]["TFLOP/s"] / BF16_PEAK_TFLOPS, 4)
+            # MFMA fraction this kernel could reach if it ran at the HBM peak
+            detail[c]["bf16_mfma_frac_cap_at_hbm_peak"] = round(
+                alg[c]["flops"] / (alg[c]["bytes"] / (HBM_PEAK_GBS * 1e9)) / 1e12 / BF16_PEAK_TFLOPS, 4)
+
+    # dominant call -> roofline (HBM-bound; algorithmic bytes / measured time)
+    dom = max(calls, key=lambda c: per_call[c])
+    ach = alg[dom]["bytes"] / per_call[dom] / 1e6
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tr = json.load(f)
+        ent = tr.get(dom)
+        if ent and ent.get("workload") == w.name and ent.get("source_hash") == source_hash(ent["sources"]):
+            traffic = ent["bytes_per_call"]
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes": alg[dom]["bytes"]}
+
+    dense = None
+    if not args.no_dense and w.dtype == torch.bfloat16:
+        o_d = torch.empty_like(q)
+        lse_d = torch.empty(bh * w.seq_len, dtype=torch.float32, device=dev)
+        L.llsa_dense_attn_fwd(p, q, k, v, o_d, lse_d)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        e0.record()
+        for _ in range(reps):
+            L.llsa_dense_attn_fwd(p, q, k, v, o_d, lse_d)
+        e1.record()
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / reps
+        dflops = 4.0 * bh * w.seq_len * w.seq_len * w.head_dim
+        llsa_fwd = per_call["pool"] + per_call["select"] + per_call["attn_fwd"]
+        dense = {"fwd_ms": round(dms, 3), "TFLOP/s": round(dflops / dms / 1e9, 1),
+                 "bf16_mfma_frac": round(dflops / dms / 1e9 / BF16_PEAK_TFLOPS, 4),
+                 "llsa_fwd_ms": round(llsa_fwd, 4),
+                 "speedup_fwd": round(dms / llsa_fwd, 2)}
+        del o_d, lse_d
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_heads)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
+                   "head_dim": w.head_dim, "block": w.block, "levels": w.levels, "topk": w.topk,
+                   "enrich": w.enrich, "keys_per_query_block": nkv,
+                   "grad_dtype": "f32", "pass": "fwd+bwd" if w.backward else "fwd"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "calls": detail,
+        "select_GB/s": detail["select"]["GB/s"],
+        "attn_fwd_bf16_mfma_frac": detail["attn_fwd"].get("bf16_mfma_frac"),
+        "dense_comparator": dense,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

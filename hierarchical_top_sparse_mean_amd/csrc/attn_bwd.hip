@@ -6,9 +6,10 @@
 //
 // Three passes:
 //  A  query-major (one wave per query block, a workgroup per level-2 node):
-//     D = rowsum(dO * O), formed in float32 as sum_j P_j dP_j (the same value
-//     without the rounding of the stored bf16 O; float32 inputs use O
-//     directly), dQ over fine and coarse keys, and the coarse-token
+//     D = rowsum(dO * O) -- formed in float32 as sum_j P_j dP_j over the
+//     attended set, which is the same value without the rounding of the
+//     stored bf16 O (float32 inputs read O) --, dQ over fine and coarse keys,
+//     and the coarse-token
 //     gradient partials summed over the workgroup's query blocks (every block
 //     under one level-2 node shares its coarse picks).
 //  B  coarse reduce: for every pooled token c of level l, sum the partials of
@@ -25,7 +26,6 @@
 namespace llsa {
 
 constexpr int kMaxCoarseLv = kMaxLevels - 1;
-constexpr int kBwdCoarseTiles = 2;   // coarse entries per query block <= 32
 constexpr int kTS = 72;              // bf16 LDS row stride (144 B)
 constexpr int kTE = kBlock * kTS;    // elements of one staged 16 x 64 tile
 
@@ -213,38 +213,41 @@ __device__ __forceinline__ void load_coarse_tile(const BwdArgs &a, const float *
     }
 }
 
+// One workgroup (4 waves) per level-2 node, every wave 4 of its 16 query
+// blocks in turn; the fine tiles of a block stream through two register sets
+// (the next tile's K / V are in flight while the current one is computed).
+template <int NCT>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ pk, const float *__restrict__ pv, const int32_t *__restrict__ idx,
-    const float *__restrict__ lse, const __bf16 *__restrict__ dout, void *__restrict__ dq,
-    BwdWs ws, BwdArgs a) {
-    // per wave: K tile (for K^T reads), Q tile, dO tile, coarse K tiles; the
-    // cross-wave reduction buffer reuses the same LDS after the main loop
-    constexpr int kTileBytes = 4 * (3 + kBwdCoarseTiles) * kTE * 2;
-    constexpr int kRedBytes = 4 * kBwdCoarseTiles * 2 * kBlock * kHeadDim * 4;
+    const float *__restrict__ lse, const __bf16 *__restrict__ dout, void *__restrict__ dq, BwdWs ws,
+    BwdArgs a) {
+    constexpr int NT = NCT > 0 ? NCT : 1;
+    constexpr int kTileBytes = 4 * (3 + NT) * kTE * 2;
+    constexpr int kRedBytes = 4 * 2 * kBlock * kHeadDim * 4;   // one coarse tile at a time
     __shared__ __attribute__((aligned(16))) char smem[kTileBytes > kRedBytes ? kTileBytes : kRedBytes];
     __shared__ float lds_row[4][2][kBlock];  // per query: lse2, D
     typedef __bf16 Tile[kTE];
     Tile *lds_k = reinterpret_cast<Tile *>(smem);
     Tile *lds_q = lds_k + 4;
     Tile *lds_do = lds_q + 4;
-    Tile(*lds_ck)[kBwdCoarseTiles] = reinterpret_cast<Tile(*)[kBwdCoarseTiles]>(lds_do + 4);
+    Tile(*lds_ck)[NT] = reinterpret_cast<Tile(*)[NT]>(lds_do + 4);
     typedef float RedTile[2][kBlock * kHeadDim];
-    RedTile(*lds_red)[kBwdCoarseTiles] = reinterpret_cast<RedTile(*)[kBwdCoarseTiles]>(smem);
+    RedTile *lds_red = reinterpret_cast<RedTile *>(smem);
 
     const int w = wave_id();
     const int lane = lane_id();
     const int g = lane >> 4, c16 = lane & 15;
     const int groups_per_head = (a.n1 + kBlock - 1) / kBlock;
-    const int h = blockIdx.x / groups_per_head;
-    const int G = blockIdx.x % groups_per_head;
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = bid / groups_per_head;
+    const int G = bid % groups_per_head;
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
-    const int nct = (a.ncoarse + kBlock - 1) / kBlock;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    f32x4 dkc[kBwdCoarseTiles][4], dvc[kBwdCoarseTiles][4];
+    f32x4 dkc[NT][4], dvc[NT][4];
 #pragma unroll
-    for (int ct = 0; ct < kBwdCoarseTiles; ++ct)
+    for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
             dkc[ct][dt] = zero4;
@@ -252,37 +255,96 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
         }
 
     const int rofs = (4 * g + (c16 >> 2)) * kTS + 4 * (c16 & 3);  // transposed-read address
+    struct TileRegs {
+        bf16x8 ka0, ka1, va0, va1;
+    };
     for (int jb = 0; jb < 4; ++jb) {
         const int ib = G * kBlock + w * 4 + jb;
         if (ib >= a.n1) break;
         const int64_t row = (int64_t)ib * kBlock + c16;
         const __bf16 *qrow = q + head_off + row * kHeadDim;
         const __bf16 *drow = dout + head_off + row * kHeadDim;
+        const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
+        auto load_tile = [&](int t, TileRegs &R) {
+            const int f = __builtin_amdgcn_readfirstlane(fine[min(t, a.K1 - 1)]);
+            const __bf16 *kt = k + head_off + (int64_t)f * kBlock * kHeadDim + c16 * kHeadDim;
+            const __bf16 *vt = v + head_off + (int64_t)f * kBlock * kHeadDim + c16 * kHeadDim;
+            R.ka0 = load_bf16x8(kt + 8 * g);
+            R.ka1 = load_bf16x8(kt + 32 + 8 * g);
+            R.va0 = load_bf16x8(vt + 8 * g);
+            R.va1 = load_bf16x8(vt + 32 + 8 * g);
+        };
         const bf16x8 qa0 = load_bf16x8(qrow + 8 * g), qa1 = load_bf16x8(qrow + 32 + 8 * g);
         const bf16x8 da0 = load_bf16x8(drow + 8 * g), da1 = load_bf16x8(drow + 32 + 8 * g);
         const float lse2 = lse[(int64_t)h * a.N + row] * kLog2e;
-        const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
+        TileRegs RA, RB;
+        load_tile(0, RA);
+        load_tile(1, RB);
+        CoarseTile T[NT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) load_coarse_tile(a, pk, pv, idx, fine, h, ib, ct, g, c16, T[ct]);
+        store_bf16x8(&lds_q[w][c16 * kTS + 8 * g], qa0);
+        store_bf16x8(&lds_q[w][c16 * kTS + 32 + 8 * g], qa1);
+        store_bf16x8(&lds_do[w][c16 * kTS + 8 * g], da0);
+        store_bf16x8(&lds_do[w][c16 * kTS + 32 + 8 * g], da1);
 
-        // ---- phase 1: D = dO . O = sum_j P_j dP_j over the attended set (float32)
-        float dsum = 0.f;
-        for (int t = 0; t < a.K1; ++t) {
-            const int f = __builtin_amdgcn_readfirstlane(fine[t]);
-            const __bf16 *kt = k + head_off + (int64_t)f * kBlock * kHeadDim + c16 * kHeadDim;
-            const __bf16 *vt = v + head_off + (int64_t)f * kBlock * kHeadDim + c16 * kHeadDim;
-            const bf16x8 ka0 = load_bf16x8(kt + 8 * g), ka1 = load_bf16x8(kt + 32 + 8 * g);
-            const bf16x8 va0 = load_bf16x8(vt + 8 * g), va1 = load_bf16x8(vt + 32 + 8 * g);
-            const f32x4 s = mfma_bf16_32(ka1, qa1, mfma_bf16_32(ka0, qa0, zero4));
-            const f32x4 dp = mfma_bf16_32(va1, da1, mfma_bf16_32(va0, da0, zero4));
+        // dQ = scale * (A - D B) with A = sum_j P_j dP_j k_j, B = sum_j P_j k_j and
+        // D = sum_j P_j dP_j (= dO . O): one streaming pass over the fine tiles,
+        // no D needed up front.  Coarse tiles come last, when D is complete.
+        f32x4 accA[4], accB[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dsum += exp2f(s[i] * a.sl2 - lse2) * dp[i];
+        for (int dt = 0; dt < 4; ++dt) {
+            accA[dt] = zero4;
+            accB[dt] = zero4;
         }
-        for (int ct = 0; ct < nct; ++ct) {
-            CoarseTile T;
-            load_coarse_tile(a, pk, pv, idx, fine, h, ib, ct, g, c16, T);
-            const f32x4 s = mfma_bf16_32(T.ka1, qa1, mfma_bf16_32(T.ka0, qa0, zero4));
-            const f32x4 dp = mfma_bf16_32(T.va1, da1, mfma_bf16_32(T.va0, da0, zero4));
+        float dsum = 0.f;
+        auto fine_tile = [&](const TileRegs &R) {
+            wave_lds_sync();
+            store_bf16x8(&lds_k[w][c16 * kTS + 8 * g], R.ka0);
+            store_bf16x8(&lds_k[w][c16 * kTS + 32 + 8 * g], R.ka1);
+            const f32x4 s = mfma_bf16_32(R.ka1, qa1, mfma_bf16_32(R.ka0, qa0, zero4));
+            const f32x4 dp = mfma_bf16_32(R.va1, da1, mfma_bf16_32(R.va0, da0, zero4));
+            float p[4], x[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dsum += exp2f(s[i] * a.sl2 + T.bias4[i] - lse2) * dp[i];
+            for (int i = 0; i < 4; ++i) {
+                p[i] = exp2f(s[i] * a.sl2 - lse2);
+                x[i] = p[i] * dp[i];
+                dsum += x[i];
+            }
+            bf16x4 phi, plo, xhi, xlo;
+            split4(p, phi, plo);
+            split4(x, xhi, xlo);
+            const bf16x8 pcat = cat8(phi, plo), xcat = cat8(xhi, xlo);
+            wave_lds_sync();
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const bf16x4 kT = lds_read_tr4(&lds_k[w][rofs + 16 * dt]);
+                const bf16x8 kk = cat8(kT, kT);
+                accA[dt] = mfma_bf16_32(kk, xcat, accA[dt]);
+                accB[dt] = mfma_bf16_32(kk, pcat, accB[dt]);
+            }
+        };
+        for (int t = 0; t < a.K1; t += 2) {
+            fine_tile(RA);
+            load_tile(t + 2, RA);
+            if (t + 1 < a.K1) fine_tile(RB);
+            load_tile(t + 3, RB);
+        }
+        // ---- coarse tiles: scores in both orientations, then D is complete
+        f32x4 cs[NT], cdp[NT], cs2[NT], cdp2[NT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            // transposed orientation: lane (query c16, entries 4g+i) -> dQ
+            cs[ct] = mfma_bf16_32(T[ct].ka1, qa1, mfma_bf16_32(T[ct].ka0, qa0, zero4));
+            cdp[ct] = mfma_bf16_32(T[ct].va1, da1, mfma_bf16_32(T[ct].va0, da0, zero4));
+            // plain orientation: lane (entry c16, queries 4g+i) -> coarse partials
+            cs2[ct] = mfma_bf16_32(qa1, T[ct].ka1, mfma_bf16_32(qa0, T[ct].ka0, zero4));
+            cdp2[ct] = mfma_bf16_32(da1, T[ct].va1, mfma_bf16_32(da0, T[ct].va0, zero4));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                cs[ct][i] = exp2f(cs[ct][i] * a.sl2 + T[ct].bias4[i] - lse2);
+                dsum += cs[ct][i] * cdp[ct][i];
+            }
         }
         const float Dq = sum4_groups(dsum);
         if (g == 0) {
@@ -290,142 +352,113 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
             lds_row[w][0][c16] = lse2;
             lds_row[w][1][c16] = Dq;
         }
-        store_bf16x8(&lds_q[w][c16 * kTS + 8 * g], qa0);
-        store_bf16x8(&lds_q[w][c16 * kTS + 32 + 8 * g], qa1);
-        store_bf16x8(&lds_do[w][c16 * kTS + 8 * g], da0);
-        store_bf16x8(&lds_do[w][c16 * kTS + 32 + 8 * g], da1);
-
-        // ---- phase 2: dS and dQ; coarse partials
-        f32x4 dqacc[4];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) dqacc[dt] = zero4;
-        for (int t = 0; t < a.K1; ++t) {
-            const int f = __builtin_amdgcn_readfirstlane(fine[t]);
-            const __bf16 *kt = k + head_off + (int64_t)f * kBlock * kHeadDim + c16 * kHeadDim;
-            const __bf16 *vt = v + head_off + (int64_t)f * kBlock * kHeadDim + c16 * kHeadDim;
-            const bf16x8 ka0 = load_bf16x8(kt + 8 * g), ka1 = load_bf16x8(kt + 32 + 8 * g);
-            const bf16x8 va0 = load_bf16x8(vt + 8 * g), va1 = load_bf16x8(vt + 32 + 8 * g);
+        for (int ct = 0; ct < NCT; ++ct) {
             wave_lds_sync();
-            store_bf16x8(&lds_k[w][c16 * kTS + 8 * g], ka0);
-            store_bf16x8(&lds_k[w][c16 * kTS + 32 + 8 * g], ka1);
-            const f32x4 s = mfma_bf16_32(ka1, qa1, mfma_bf16_32(ka0, qa0, zero4));
-            const f32x4 dp = mfma_bf16_32(va1, da1, mfma_bf16_32(va0, da0, zero4));
-            float ds[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ds[i] = exp2f(s[i] * a.sl2 - lse2) * (dp[i] - Dq);
-            bf16x4 dhi, dlo;
-            split4(ds, dhi, dlo);
+            store_bf16x8(&lds_ck[w][ct][c16 * kTS + 8 * g], T[ct].ka0);
+            store_bf16x8(&lds_ck[w][ct][c16 * kTS + 32 + 8 * g], T[ct].ka1);
             wave_lds_sync();
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                const bf16x4 kT = lds_read_tr4(&lds_k[w][rofs + 16 * dt]);
-                dqacc[dt] = mfma_bf16_16(kT, dlo, mfma_bf16_16(kT, dhi, dqacc[dt]));
-            }
-        }
-        for (int ct = 0; ct < nct; ++ct) {
-            CoarseTile T;
-            load_coarse_tile(a, pk, pv, idx, fine, h, ib, ct, g, c16, T);
-            wave_lds_sync();
-            store_bf16x8(&lds_ck[w][ct][c16 * kTS + 8 * g], T.ka0);
-            store_bf16x8(&lds_ck[w][ct][c16 * kTS + 32 + 8 * g], T.ka1);
-            // transposed orientation: lane (query c16, entries 4g+i) -> dQ
-            const f32x4 s = mfma_bf16_32(T.ka1, qa1, mfma_bf16_32(T.ka0, qa0, zero4));
-            const f32x4 dp = mfma_bf16_32(T.va1, da1, mfma_bf16_32(T.va0, da0, zero4));
-            // plain orientation: lane (entry c16, queries 4g+i) -> coarse partials
-            const f32x4 s2 = mfma_bf16_32(qa1, T.ka1, mfma_bf16_32(qa0, T.ka0, zero4));
-            const f32x4 dp2 = mfma_bf16_32(da1, T.va1, mfma_bf16_32(da0, T.va0, zero4));
             float ds[4], ds2[4], p2[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                ds[i] = exp2f(s[i] * a.sl2 + T.bias4[i] - lse2) * (dp[i] - Dq);
+                ds[i] = cs[ct][i] * (cdp[ct][i] - Dq);
                 const float l2q = lds_row[w][0][4 * g + i];
                 const float Dqi = lds_row[w][1][4 * g + i];
-                p2[i] = exp2f(s2[i] * a.sl2 + T.bias_row - l2q);
-                ds2[i] = p2[i] * (dp2[i] - Dqi);
+                p2[i] = exp2f(cs2[ct][i] * a.sl2 + T[ct].bias_row - l2q);
+                ds2[i] = p2[i] * (cdp2[ct][i] - Dqi);
             }
             bf16x4 dhi, dlo, d2hi, d2lo, p2hi, p2lo;
             split4(ds, dhi, dlo);
             split4(ds2, d2hi, d2lo);
             split4(p2, p2hi, p2lo);
-            wave_lds_sync();
+            const bf16x8 dcat = cat8(dhi, dlo), d2cat = cat8(d2hi, d2lo), p2cat = cat8(p2hi, p2lo);
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
                 const bf16x4 kT = lds_read_tr4(&lds_ck[w][ct][rofs + 16 * dt]);
-                dqacc[dt] = mfma_bf16_16(kT, dlo, mfma_bf16_16(kT, dhi, dqacc[dt]));
+                accA[dt] = mfma_bf16_32(cat8(kT, kT), dcat, accA[dt]);   // + Kc^T dS_c
                 const bf16x4 qT = lds_read_tr4(&lds_q[w][rofs + 16 * dt]);
                 const bf16x4 dT = lds_read_tr4(&lds_do[w][rofs + 16 * dt]);
-                if (ct == 0) {
-                    dkc[0][dt] = mfma_bf16_16(d2lo, qT, mfma_bf16_16(d2hi, qT, dkc[0][dt]));
-                    dvc[0][dt] = mfma_bf16_16(p2lo, dT, mfma_bf16_16(p2hi, dT, dvc[0][dt]));
-                } else {
-                    dkc[1][dt] = mfma_bf16_16(d2lo, qT, mfma_bf16_16(d2hi, qT, dkc[1][dt]));
-                    dvc[1][dt] = mfma_bf16_16(p2lo, dT, mfma_bf16_16(p2hi, dT, dvc[1][dt]));
-                }
+                dkc[ct][dt] = mfma_bf16_32(d2cat, cat8(qT, qT), dkc[ct][dt]);
+                dvc[ct][dt] = mfma_bf16_32(p2cat, cat8(dT, dT), dvc[ct][dt]);
             }
         }
-        // ---- dQ store: lane (query c16, dims 16dt + 4g + i)
+        f32x4 dqacc[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) dqacc[dt] = accA[dt] - Dq * accB[dt];
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
             store_grad4(dq, head_off + row * kHeadDim + 16 * dt + 4 * g, dqacc[dt] * a.scale, a.grad_bf16);
         wave_lds_sync();
     }
-    if (nct == 0) return;
-    __syncthreads();   // every wave is done with the tiles that share this LDS
-    // ---- reduce coarse partials over the 4 waves; layout C: lane (dim 16dt + c16, entries 4g+i)
-    for (int ct = 0; ct < nct; ++ct)
+    // ---- reduce the coarse partials over the 4 waves, one coarse tile at a time
+    float *part = ws.partial + ((int64_t)h * a.n2 + G) * a.ncoarse * 2 * kHeadDim;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        __syncthreads();
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int ent = 4 * g + i, dim = 16 * dt + c16;
-                lds_red[w][ct][0][ent * kHeadDim + dim] = (ct == 0 ? dkc[0][dt][i] : dkc[1][dt][i]) * a.scale;
-                lds_red[w][ct][1][ent * kHeadDim + dim] = ct == 0 ? dvc[0][dt][i] : dvc[1][dt][i];
+                lds_red[w][0][ent * kHeadDim + dim] = dkc[ct][dt][i] * a.scale;
+                lds_red[w][1][ent * kHeadDim + dim] = dvc[ct][dt][i];
             }
-    __syncthreads();
-    float *part = ws.partial + ((int64_t)h * a.n2 + G) * a.ncoarse * 2 * kHeadDim;
-    for (int x = threadIdx.x; x < a.ncoarse * 2 * kHeadDim; x += 256) {
-        const int ent = x / (2 * kHeadDim), kv = (x / kHeadDim) & 1, dim = x % kHeadDim;
-        const int ct = ent / kBlock, er = ent % kBlock;
-        const float s = lds_red[0][ct][kv][er * kHeadDim + dim] + lds_red[1][ct][kv][er * kHeadDim + dim] +
-                        lds_red[2][ct][kv][er * kHeadDim + dim] + lds_red[3][ct][kv][er * kHeadDim + dim];
-        part[x] = s;
+        __syncthreads();
+        const int n_ent = min(kBlock, a.ncoarse - ct * kBlock);
+        for (int x = threadIdx.x; x < n_ent * 2 * kHeadDim; x += 256) {
+            const int er = x / (2 * kHeadDim), kv = (x / kHeadDim) & 1, dim = x % kHeadDim;
+            const int oo = er * kHeadDim + dim;
+            part[(ct * kBlock) * 2 * kHeadDim + x] =
+                lds_red[0][kv][oo] + lds_red[1][kv][oo] + lds_red[2][kv][oo] + lds_red[3][kv][oo];
+        }
     }
 }
 
 // ================================================================ pass B
-// One thread per (level, pooled token, column): sum over the level-l rows
-// that picked the token (CSR of I^(l)) and over the level-2 nodes under each
-// such row.
+// One wave per pooled token c of level l (lanes = columns): the level-l rows
+// that picked c come from the CSR of I^(l); each lane looks up one row's slot
+// of c, then the wave sums the partials of every level-2 node under each row.
 __global__ __launch_bounds__(256) void bwd_coarse_reduce_kernel(const int32_t *__restrict__ idx,
                                                                 const int32_t *__restrict__ csr_ptr,
                                                                 const int32_t *__restrict__ csr_col,
                                                                 BwdWs ws, BwdArgs a, int j) {
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int nl = a.cl_n[j], kl = a.cl_k[j];
-    if (t >= (int64_t)a.bh * nl * kHeadDim) return;
-    const int h = (int)(t / ((int64_t)nl * kHeadDim));
-    const int c = (int)((t / kHeadDim) % nl);
-    const int dim = (int)(t % kHeadDim);
+    const int64_t tok = (int64_t)blockIdx.x * 4 + wave_id();
+    if (tok >= (int64_t)a.bh * nl) return;
+    const int lane = lane_id();
+    const int h = (int)(tok / nl);
+    const int c = (int)(tok % nl);
     const int32_t *P = csr_ptr + a.cl_ptr_off[j] + (int64_t)h * (nl + 1);
     const int32_t *C = csr_col + a.cl_col_off[j] + (int64_t)h * nl * kl;
     const int32_t *I = idx + a.cl_idx_off[j] + (int64_t)h * nl * kl;
     const int nodes = a.cl_span[j] / kBlock;   // level-2 nodes under one level-l token
+    const int e0 = P[c], e1 = P[c + 1];
     float sk = 0.f, sv = 0.f;
-    for (int e = P[c]; e < P[c + 1]; ++e) {
-        const int r = C[e];
-        int slot = 0;
-        while (slot < kl && I[(int64_t)r * kl + slot] != c) ++slot;
-        if (slot == kl) continue;   // not a pick of row r: inconsistent lists, skip
-        const int ent = a.cl_entry0[j] + slot;
-        for (int s = 0; s < nodes; ++s) {
-            const int64_t G = (int64_t)h * a.n2 + (int64_t)r * nodes + s;
-            const float *pp = ws.partial + (G * a.ncoarse + ent) * 2 * kHeadDim;
-            sk += pp[dim];
-            sv += pp[kHeadDim + dim];
+    for (int base = e0; base < e1; base += kWave) {
+        const int cnt = min(kWave, e1 - base);
+        int ent = -1, g0 = 0;
+        if (lane < cnt) {
+            const int r = C[base + lane];
+            int slot = 0;
+            while (slot < kl && I[(int64_t)r * kl + slot] != c) ++slot;
+            if (slot < kl) {
+                ent = a.cl_entry0[j] + slot;
+                g0 = r * nodes;
+            }
+        }
+        for (int jj = 0; jj < cnt; ++jj) {
+            const int e = __builtin_amdgcn_readlane(ent, jj);
+            if (e < 0) continue;   // not a pick of that row: inconsistent lists, skip
+            const int64_t G0 = (int64_t)h * a.n2 + __builtin_amdgcn_readlane(g0, jj);
+            for (int s = 0; s < nodes; ++s) {
+                const float *pp = ws.partial + ((G0 + s) * a.ncoarse + e) * 2 * kHeadDim;
+                sk += pp[lane];
+                sv += pp[kHeadDim + lane];
+            }
         }
     }
-    ws.dpk[a.cl_grad_off[j] + ((int64_t)h * nl + c) * kHeadDim + dim] = sk;
-    ws.dpv[a.cl_grad_off[j] + ((int64_t)h * nl + c) * kHeadDim + dim] = sv;
+    ws.dpk[a.cl_grad_off[j] + ((int64_t)h * nl + c) * kHeadDim + lane] = sk;
+    ws.dpv[a.cl_grad_off[j] + ((int64_t)h * nl + c) * kHeadDim + lane] = sv;
 }
 
 // ================================================================ pass C
@@ -439,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_bf16_kernel(
     const int w = wave_id();
     const int lane = lane_id();
     const int g = lane >> 4, c16 = lane & 15;
-    const int64_t kb = (int64_t)blockIdx.x * 4 + w;
+    const int64_t kb = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + w;
     if (kb >= (int64_t)a.bh * a.n1) return;
     const int h = (int)(kb / a.n1);
     const int f = (int)(kb % a.n1);
@@ -458,30 +491,40 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_bf16_kernel(
     const int32_t *P = csr_ptr + (int64_t)h * (a.n1 + 1);
     const int32_t *C = csr_col + (int64_t)h * a.n1 * a.K1;
     const int e0 = __builtin_amdgcn_readfirstlane(P[f]), e1 = __builtin_amdgcn_readfirstlane(P[f + 1]);
-    for (int e = e0; e < e1; ++e) {
-        const int ib = __builtin_amdgcn_readfirstlane(C[e]);
+    // The query blocks of the segment are read 64 at a time into one register
+    // (lane j holds entry j), and the next pair's Q / dO / lse / D are loaded
+    // while the current pair is computed.
+    struct Pair {
+        bf16x8 qa0, qa1, da0, da1;
+        f32x4 l4, D4;
+    };
+    auto load_pair = [&](int ib, Pair &X) {
         const int64_t row = (int64_t)ib * kBlock + c16;
         const __bf16 *qr = q + head_off + row * kHeadDim;
         const __bf16 *dr = dout + head_off + row * kHeadDim;
-        const bf16x8 qa0 = load_bf16x8(qr + 8 * g), qa1 = load_bf16x8(qr + 32 + 8 * g);
-        const bf16x8 da0 = load_bf16x8(dr + 8 * g), da1 = load_bf16x8(dr + 32 + 8 * g);
-        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(lse + (int64_t)h * a.N + (int64_t)ib * kBlock + 4 * g);
-        const f32x4 D4 = *reinterpret_cast<const f32x4 *>(ws.D + (int64_t)h * a.N + (int64_t)ib * kBlock + 4 * g);
+        X.qa0 = load_bf16x8(qr + 8 * g);
+        X.qa1 = load_bf16x8(qr + 32 + 8 * g);
+        X.da0 = load_bf16x8(dr + 8 * g);
+        X.da1 = load_bf16x8(dr + 32 + 8 * g);
+        X.l4 = *reinterpret_cast<const f32x4 *>(lse + (int64_t)h * a.N + (int64_t)ib * kBlock + 4 * g);
+        X.D4 = *reinterpret_cast<const f32x4 *>(ws.D + (int64_t)h * a.N + (int64_t)ib * kBlock + 4 * g);
+    };
+    auto compute = [&](const Pair &X) {
         wave_lds_sync();
-        store_bf16x8(&lds_q[w][c16 * kTS + 8 * g], qa0);
-        store_bf16x8(&lds_q[w][c16 * kTS + 32 + 8 * g], qa1);
-        store_bf16x8(&lds_do[w][c16 * kTS + 8 * g], da0);
-        store_bf16x8(&lds_do[w][c16 * kTS + 32 + 8 * g], da1);
+        store_bf16x8(&lds_q[w][c16 * kTS + 8 * g], X.qa0);
+        store_bf16x8(&lds_q[w][c16 * kTS + 32 + 8 * g], X.qa1);
+        store_bf16x8(&lds_do[w][c16 * kTS + 8 * g], X.da0);
+        store_bf16x8(&lds_do[w][c16 * kTS + 32 + 8 * g], X.da1);
         // S = Q K^T: lane (key c16, queries 4g+i)
-        f32x4 s = mfma_bf16_32(qa0, kb0, f32x4{0.f, 0.f, 0.f, 0.f});
-        s = mfma_bf16_32(qa1, kb1, s);
-        f32x4 dp = mfma_bf16_32(da0, vb0, f32x4{0.f, 0.f, 0.f, 0.f});
-        dp = mfma_bf16_32(da1, vb1, dp);
+        f32x4 s = mfma_bf16_32(X.qa0, kb0, f32x4{0.f, 0.f, 0.f, 0.f});
+        s = mfma_bf16_32(X.qa1, kb1, s);
+        f32x4 dp = mfma_bf16_32(X.da0, vb0, f32x4{0.f, 0.f, 0.f, 0.f});
+        dp = mfma_bf16_32(X.da1, vb1, dp);
         float pp[4], ds[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            pp[i] = exp2f(s[i] * a.sl2 - l4[i] * kLog2e);
-            ds[i] = pp[i] * (dp[i] - D4[i]);
+            pp[i] = exp2f(s[i] * a.sl2 - X.l4[i] * kLog2e);
+            ds[i] = pp[i] * (dp[i] - X.D4[i]);
         }
         bf16x4 phi, plo, dhi, dlo;
         split4(pp, phi, plo);
@@ -491,8 +534,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_bf16_kernel(
         for (int dt = 0; dt < 4; ++dt) {
             const bf16x4 dT = lds_read_tr4(&lds_do[w][rofs + 16 * dt]);
             const bf16x4 qT = lds_read_tr4(&lds_q[w][rofs + 16 * dt]);
-            dva[dt] = mfma_bf16_16(plo, dT, mfma_bf16_16(phi, dT, dva[dt]));
-            dka[dt] = mfma_bf16_16(dlo, qT, mfma_bf16_16(dhi, qT, dka[dt]));
+            dva[dt] = mfma_bf16_32(cat8(phi, plo), cat8(dT, dT), dva[dt]);
+            dka[dt] = mfma_bf16_32(cat8(dhi, dlo), cat8(qT, qT), dka[dt]);
+        }
+    };
+    // two register sets in turn: the loads of one pair are in flight while
+    // the other is computed (the reads past the segment's end repeat its last
+    // pair and are not used)
+    for (int base = e0; base < e1; base += kWave) {
+        const int cnt = min(kWave, e1 - base);
+        const int colv = lane < cnt ? C[base + lane] : 0;
+        Pair A, Bp;
+        load_pair(__builtin_amdgcn_readlane(colv, 0), A);
+        for (int j = 0; j < cnt; j += 2) {
+            load_pair(__builtin_amdgcn_readlane(colv, min(j + 1, cnt - 1)), Bp);
+            compute(A);
+            load_pair(__builtin_amdgcn_readlane(colv, min(j + 2, cnt - 1)), A);
+            if (j + 1 < cnt) compute(Bp);
         }
     }
     // C layout: lane (dim 16dt + c16, keys 4g+i); add pooled-level gradients / B^l
@@ -690,12 +748,23 @@ hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, cons
     const BwdWs ws = carve_ws(g, a, wsp);
     if (g.bf16) {
         const int gph = (a.n1 + kBlock - 1) / kBlock;
-        hipLaunchKernelGGL(bwd_dq_bf16_kernel, dim3((unsigned)(g.bh * gph)), dim3(256), 0, s,
-                           (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx,
-                           lse, (const __bf16 *)dout, dq, ws, a);
+        const int nct = (a.ncoarse + kBlock - 1) / kBlock;
+        const dim3 grid((unsigned)(g.bh * gph));
+        if (nct == 0)
+            hipLaunchKernelGGL(bwd_dq_bf16_kernel<0>, grid, dim3(256), 0, s, (const __bf16 *)q,
+                               (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx, lse,
+                               (const __bf16 *)dout, dq, ws, a);
+        else if (nct == 1)
+            hipLaunchKernelGGL(bwd_dq_bf16_kernel<1>, grid, dim3(256), 0, s, (const __bf16 *)q,
+                               (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx, lse,
+                               (const __bf16 *)dout, dq, ws, a);
+        else
+            hipLaunchKernelGGL(bwd_dq_bf16_kernel<2>, grid, dim3(256), 0, s, (const __bf16 *)q,
+                               (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx, lse,
+                               (const __bf16 *)dout, dq, ws, a);
         for (int j = 0; j < a.ncl; ++j) {
-            const int64_t total = (int64_t)g.bh * a.cl_n[j] * kHeadDim;
-            hipLaunchKernelGGL(bwd_coarse_reduce_kernel, dim3((unsigned)((total + 255) / 256)),
+            const int64_t toks = (int64_t)g.bh * a.cl_n[j];
+            hipLaunchKernelGGL(bwd_coarse_reduce_kernel, dim3((unsigned)((toks + 3) / 4)),
                                dim3(256), 0, s, idx, csr_ptr, csr_col, ws, a, j);
         }
         const int64_t kbs = (int64_t)g.bh * a.n1;

@@ -87,6 +87,88 @@ __device__ __forceinline__ bool coarse_entry(const FwdArgs &a, const int32_t *__
     return true;
 }
 
+// Level slot j and pick number of coarse entry e (arithmetic only).
+__device__ __forceinline__ bool coarse_locate(const FwdArgs &a, int e, int &j, int &pick) {
+    j = 0;
+    pick = e;
+    while (j < a.ncl - 1 && pick >= a.cl_k[j]) {
+        pick -= a.cl_k[j];
+        ++j;
+    }
+    return e < a.ncoarse;
+}
+
+// A coarse pick can only be fully covered by the fine picks when K_1 reaches
+// the B^(l-1) level-1 blocks under it.
+__device__ __forceinline__ bool drop_possible(const FwdArgs &a) {
+    return a.drop && a.K1 >= kBlock;
+}
+
+// Coarse tile ct of query block ib, prefetched as raw float32 rows: the lane's
+// operand row (entry ct*16 + c16) of pooled K and its 16 V columns 16g..16g+15,
+// and the log2 weights of the score rows 4g+i (-inf where absent / dropped).
+struct CoarseRows {
+    f32x4 k0, k1, k2, k3;   // K row, dims 8g..8g+7 and 32+8g..32+8g+7
+    f32x4 v0, v1, v2, v3;   // V row, dims 16g..16g+15
+    float bias[4];
+};
+
+// Pick index of the lane's operand row of coarse tile ct (one read; issued
+// early so the pooled-row reads that depend on it do not wait behind later
+// loads).
+__device__ __forceinline__ int coarse_pick(const FwdArgs &a, const int32_t *__restrict__ idx, int h,
+                                           int ib, int ct, int c16) {
+    int j, pick;
+    const bool ok = coarse_locate(a, ct * kBlock + c16, j, pick);
+    const int js = ok ? j : 0, ps = ok ? pick : 0;
+    return idx[a.cl_idx_off[js] + ((int64_t)h * a.cl_n[js] + ib / a.cl_span[js]) * a.cl_k[js] + ps];
+}
+
+__device__ __forceinline__ void prefetch_coarse(const FwdArgs &a, const int32_t *__restrict__ idx,
+                                                const int32_t *__restrict__ fine,
+                                                const float *__restrict__ pk,
+                                                const float *__restrict__ pv, int h, int ib, int ct,
+                                                int c, int g, int c16, CoarseRows &R) {
+    int j, pick;
+    bool ok = coarse_locate(a, ct * kBlock + c16, j, pick);
+    const int js = ok ? j : 0;
+    // absent rows read a valid row of the same level and are zeroed below
+    const int64_t src = a.cl_pyr_off[js] + ((int64_t)h * a.cl_n[js] + c) * kHeadDim;
+    const f32x4 *ks = reinterpret_cast<const f32x4 *>(pk + src);
+    const f32x4 *vsrc = reinterpret_cast<const f32x4 *>(pv + src + 16 * g);
+    R.k0 = ks[2 * g];
+    R.k1 = ks[2 * g + 1];
+    R.k2 = ks[8 + 2 * g];
+    R.k3 = ks[8 + 2 * g + 1];
+    R.v0 = vsrc[0];
+    R.v1 = vsrc[1];
+    R.v2 = vsrc[2];
+    R.v3 = vsrc[3];
+    if (drop_possible(a)) {
+        int64_t r2;
+        float b2;
+        ok = coarse_entry(a, idx, fine, h, ib, ct * kBlock + c16, r2, b2);
+    }
+    if (!ok) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        R.k0 = R.k1 = R.k2 = R.k3 = R.v0 = R.v1 = R.v2 = R.v3 = z;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int j2, p2;
+        const bool ok2 = coarse_locate(a, ct * kBlock + 4 * g + i, j2, p2);
+        R.bias[i] = ok2 ? 4.0f * (float)(j2 + 2) : -INFINITY;
+    }
+    if (drop_possible(a)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int64_t r2;
+            float b2;
+            if (!coarse_entry(a, idx, fine, h, ib, ct * kBlock + 4 * g + i, r2, b2)) R.bias[i] = -INFINITY;
+        }
+    }
+}
+
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ pk, const float *__restrict__ pv, const int32_t *__restrict__ idx,
@@ -95,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     const int w = wave_id();
     const int lane = lane_id();
     const int g = lane >> 4, c16 = lane & 15;
-    const int64_t blk = (int64_t)blockIdx.x * 4 + w;
+    const int64_t blk = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + w;
     if (blk >= (int64_t)a.bh * a.n1) return;
     const int h = (int)(blk / a.n1);
     const int ib = (int)(blk % a.n1);
@@ -108,83 +190,60 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     const bf16x8 qa0 = load_bf16x8(qrow + 8 * g);
     const bf16x8 qa1 = load_bf16x8(qrow + 32 + 8 * g);
     const int32_t *fine = idx + blk * a.K1;
+    const int nct = (a.ncoarse + kBlock - 1) / kBlock;
 
     float m = -INFINITY, lsum = 0.f;
     f32x4 oacc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
     float bias[kFwdTiles][4];
     f32x4 st[kFwdTiles];
-    // ---- fine key blocks, weight 1
+    CoarseRows cr;
+    const int cpick0 = nct > 0 ? coarse_pick(a, idx, h, ib, 0, c16) : 0;
+
+    // ---- fine key blocks, weight 1.  All loads of a chunk are issued before
+    // any is consumed (tiles past the chunk's end re-read its last tile); the
+    // first coarse tile is fetched right after the first chunk's loads so its
+    // two dependent reads (pick index, then pooled rows) overlap them.
     for (int t0 = 0; t0 < a.K1; t0 += kFwdTiles) {
         const int nt = min(kFwdTiles, a.K1 - t0);
+        bf16x8 kr[kFwdTiles][2], vr[kFwdTiles][2];
+#pragma unroll
+        for (int t = 0; t < kFwdTiles; ++t) {
+            const int f = __builtin_amdgcn_readfirstlane(fine[t0 + min(t, nt - 1)]);
+            const __bf16 *kt = kh + (int64_t)f * kBlock * kHeadDim;
+            const __bf16 *vt = vh + (int64_t)f * kBlock * kHeadDim;
+            kr[t][0] = load_bf16x8(kt + c16 * kHeadDim + 8 * g);
+            kr[t][1] = load_bf16x8(kt + c16 * kHeadDim + 32 + 8 * g);
+            vr[t][0] = load_bf16x8(vt + lane * 8);              // 16-byte chunk `lane` of the tile
+            vr[t][1] = load_bf16x8(vt + (lane + kWave) * 8);    // chunk `lane + 64`
+        }
+        if (t0 == 0 && nct > 0) prefetch_coarse(a, idx, fine, pk, pv, h, ib, 0, cpick0, g, c16, cr);
 #pragma unroll
         for (int t = 0; t < kFwdTiles; ++t) {
             if (t < nt) {
-                const int f = __builtin_amdgcn_readfirstlane(fine[t0 + t]);
-                const __bf16 *kt = kh + (int64_t)f * kBlock * kHeadDim;
-                const __bf16 *vt = vh + (int64_t)f * kBlock * kHeadDim;
-                const bf16x8 ka0 = load_bf16x8(kt + c16 * kHeadDim + 8 * g);
-                const bf16x8 ka1 = load_bf16x8(kt + c16 * kHeadDim + 32 + 8 * g);
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
-                    const int ci = lane + kWave * r;  // 16-byte chunk of the 2 KB tile
-                    store_bf16x8(vw + t * kTileElems + (ci >> 3) * kVStride + (ci & 7) * 8,
-                                 load_bf16x8(vt + ci * 8));
+                    const int ci = lane + kWave * r;
+                    store_bf16x8(vw + t * kTileElems + (ci >> 3) * kVStride + (ci & 7) * 8, vr[t][r]);
                 }
-                f32x4 s = mfma_bf16_32(ka0, qa0, f32x4{0.f, 0.f, 0.f, 0.f});
-                s = mfma_bf16_32(ka1, qa1, s);
-                st[t] = s * a.sl2;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) bias[t][i] = 0.f;
+                st[t] = mfma_bf16_32(kr[t][1], qa1, mfma_bf16_32(kr[t][0], qa0, f32x4{0.f, 0.f, 0.f, 0.f})) * a.sl2;
             }
         }
-        softmax_pv_chunk(st, bias, nt, vw, m, lsum, oacc, g, c16);
+        softmax_pv_chunk<false>(st, bias, nt, vw, m, lsum, oacc, g, c16);
     }
-    // ---- coarse tokens of levels 2..ncl+1, weight B^l
-    const int nct = (a.ncoarse + kBlock - 1) / kBlock;
-    for (int t0 = 0; t0 < nct; t0 += kFwdTiles) {
-        const int nt = min(kFwdTiles, nct - t0);
+    // ---- coarse tokens of levels 2..ncl+1, weight B^l, one tile at a time
+    for (int ct = 0; ct < nct; ++ct) {
+        if (ct > 0) prefetch_coarse(a, idx, fine, pk, pv, h, ib, ct, coarse_pick(a, idx, h, ib, ct, c16), g, c16, cr);
+        __bf16 *vrow = vw + c16 * kVStride + 16 * g;
+        store_bf16x8(vrow, f32_to_bf16x8(cr.v0, cr.v1));
+        store_bf16x8(vrow + 8, f32_to_bf16x8(cr.v2, cr.v3));
+        const bf16x8 ka0 = f32_to_bf16x8(cr.k0, cr.k1);
+        const bf16x8 ka1 = f32_to_bf16x8(cr.k2, cr.k3);
+        st[0] = mfma_bf16_32(ka1, qa1, mfma_bf16_32(ka0, qa0, f32x4{0.f, 0.f, 0.f, 0.f})) * a.sl2;
 #pragma unroll
-        for (int t = 0; t < kFwdTiles; ++t) {
-            if (t < nt) {
-                // operand row: entry (t0+t)*16 + c16
-                int64_t roff = 0;
-                float b = 0.f;
-                const bool ok = coarse_entry(a, idx, fine, h, ib, (t0 + t) * kBlock + c16, roff, b);
-                f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, k2 = k0, k3 = k0;
-                f32x4 v0 = k0, v1 = k0, v2 = k0, v3 = k0;
-                if (ok) {
-                    const f32x4 *ks = reinterpret_cast<const f32x4 *>(pk + roff);
-                    const f32x4 *vsrc = reinterpret_cast<const f32x4 *>(pv + roff + 16 * g);
-                    k0 = ks[2 * g];
-                    k1 = ks[2 * g + 1];
-                    k2 = ks[8 + 2 * g];
-                    k3 = ks[8 + 2 * g + 1];
-                    v0 = vsrc[0];
-                    v1 = vsrc[1];
-                    v2 = vsrc[2];
-                    v3 = vsrc[3];
-                }
-                __bf16 *vrow = vw + t * kTileElems + c16 * kVStride + 16 * g;
-                store_bf16x8(vrow, f32_to_bf16x8(v0, v1));
-                store_bf16x8(vrow + 8, f32_to_bf16x8(v2, v3));
-                const bf16x8 ka0 = f32_to_bf16x8(k0, k1);
-                const bf16x8 ka1 = f32_to_bf16x8(k2, k3);
-                f32x4 s = mfma_bf16_32(ka0, qa0, f32x4{0.f, 0.f, 0.f, 0.f});
-                s = mfma_bf16_32(ka1, qa1, s);
-                st[t] = s * a.sl2;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    int64_t r2;
-                    float b2;
-                    const bool ok2 = coarse_entry(a, idx, fine, h, ib, (t0 + t) * kBlock + 4 * g + i, r2, b2);
-                    bias[t][i] = ok2 ? b2 : -INFINITY;
-                }
-            }
-        }
-        softmax_pv_chunk(st, bias, nt, vw, m, lsum, oacc, g, c16);
+        for (int i = 0; i < 4; ++i) bias[0][i] = cr.bias[i];
+        softmax_pv_chunk(st, bias, 1, vw, m, lsum, oacc, g, c16);
     }
     // ---- normalise and store
     lsum = sum4_groups(lsum);

@@ -14,6 +14,8 @@ constexpr int kTileElems = kBlock * kVStride;
 // log2 weight of those keys (-inf masks a key).  vw holds the nt V tiles
 // (row-major, kVStride) in LDS.  m / lsum / oacc are the running max, the
 // lane-partial denominator and O^T (lane: query l%16, dims 16dt+4(l/16)+i).
+// kBias = false ignores `bias` (all weights 1).
+template <bool kBias = true>
 __device__ __forceinline__ void softmax_pv_chunk(f32x4 (&st)[kFwdTiles], const float (&bias)[kFwdTiles][4],
                                                  int nt, const __bf16 *vw, float &m, float &lsum,
                                                  f32x4 (&oacc)[4], int g, int c16) {
@@ -22,7 +24,7 @@ __device__ __forceinline__ void softmax_pv_chunk(f32x4 (&st)[kFwdTiles], const f
     for (int t = 0; t < kFwdTiles; ++t)
         if (t < nt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[t][i] + bias[t][i]);
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[t][i] + (kBias ? bias[t][i] : 0.f));
     mx = max4_groups(mx);
     const float mnew = fmaxf(m, mx);
     const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
@@ -40,8 +42,8 @@ __device__ __forceinline__ void softmax_pv_chunk(f32x4 (&st)[kFwdTiles], const f
             float p0[4], p1[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p0[i] = exp2f(st[t][i] + bias[t][i] - msafe);
-                p1[i] = two ? exp2f(st[t + 1][i] + bias[t + 1][i] - msafe) : 0.f;
+                p0[i] = exp2f(st[t][i] + (kBias ? bias[t][i] : 0.f) - msafe);
+                p1[i] = two ? exp2f(st[t + 1][i] + (kBias ? bias[t + 1][i] : 0.f) - msafe) : 0.f;
                 lsum += p0[i] + p1[i];
             }
             const bf16x8 pb = {(__bf16)p0[0], (__bf16)p0[1], (__bf16)p0[2], (__bf16)p0[3],

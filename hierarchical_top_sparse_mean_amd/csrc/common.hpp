@@ -86,6 +86,17 @@ __device__ __forceinline__ float sum4_groups(float v) {
     return v;
 }
 
+// The dispatcher hands workgroup i to XCD i % 8, and every XCD has its own
+// L2.  Renumbering so that each XCD walks one contiguous range of the logical
+// grid keeps neighbouring work -- which gathers the same key/value tiles --
+// inside one L2.  Bijective for any grid size.
+constexpr int kNumXcd = 8;
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+    const int per = nblocks / kNumXcd, rem = nblocks % kNumXcd;
+    const int x = bid % kNumXcd, i = bid / kNumXcd;
+    return x * per + (x < rem ? x : rem) + i;
+}
+
 // Wave-scope ordering for data exchanged through LDS by lanes of one wave.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

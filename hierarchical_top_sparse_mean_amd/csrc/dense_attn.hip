@@ -29,8 +29,9 @@ __global__ __launch_bounds__(512) void dense_fwd_bf16_kernel(const __bf16 *__res
     const int w = wave_id();
     const int lane = lane_id();
     const int g = lane >> 4, c16 = lane & 15;
-    const int h = blockIdx.x / qtiles_per_head;
-    const int qt = blockIdx.x % qtiles_per_head;
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = bid / qtiles_per_head;
+    const int qt = bid % qtiles_per_head;
     const int64_t head_off = (int64_t)h * N * kHeadDim;
     const int q0 = qt * (kDenseWaves * kBlock) + w * kBlock;
     const bool active = q0 < N;
@@ -42,11 +43,7 @@ __global__ __launch_bounds__(512) void dense_fwd_bf16_kernel(const __bf16 *__res
     f32x4 oacc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float bias[kFwdTiles][4];
-#pragma unroll
-    for (int t = 0; t < kFwdTiles; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bias[t][i] = 0.f;
+    float bias[kFwdTiles][4];   // unused: every weight is 1
     f32x4 st[kFwdTiles];
 
     for (int k0 = 0; k0 < N; k0 += kDenseKeys) {
@@ -77,7 +74,7 @@ __global__ __launch_bounds__(512) void dense_fwd_bf16_kernel(const __bf16 *__res
                     st[t] = s * sl2;
                 }
             }
-            softmax_pv_chunk(st, bias, nt, vs, m, lsum, oacc, g, c16);
+            softmax_pv_chunk<false>(st, bias, nt, vs, m, lsum, oacc, g, c16);
         }
     }
     if (!active) return;

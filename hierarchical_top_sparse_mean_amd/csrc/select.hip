@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ q
                                                      int32_t *__restrict__ out, int n, int kout,
                                                      int kp, int groups_per_head,
                                                      int64_t groups_total) {
-    const int64_t gid = (int64_t)blockIdx.x * 4 + wave_id();
+    const int64_t gid = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + wave_id();
     if (gid >= groups_total) return;
     const int h = (int)(gid / groups_per_head);
     const int gi = (int)(gid % groups_per_head);
@@ -132,34 +132,36 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ q
 
     for (int t0 = 0; t0 < ntiles; t0 += kSelTilesPerChunk) {
         uint64_t keys[4 * kSelTilesPerChunk];
+        // every tile's rows are requested before the first is used; tiles past
+        // the end re-read the last tile and are masked out
+        float kf[kSelTilesPerChunk][16];
+        int base[kSelTilesPerChunk];
 #pragma unroll
         for (int t = 0; t < kSelTilesPerChunk; ++t) {
-            const int tile = t0 + t;
-            if (tile < ntiles) {
-                const int base = dense ? tile * kBlock : __builtin_amdgcn_readfirstlane(prow[tile]) * kBlock;
-                const int cand = base + col;
-                const bool cok = cand < n;
-                const f32x4 *src = reinterpret_cast<const f32x4 *>(kh + (int64_t)(cok ? cand : 0) * kHeadDim + 16 * g);
-                float kf[16];
+            const int tile = min(t0 + t, ntiles - 1);
+            base[t] = dense ? tile * kBlock : __builtin_amdgcn_readfirstlane(prow[tile]) * kBlock;
+            const int cand = base[t] + col;
+            const int64_t crow = cand < n ? cand : 0;
+            const f32x4 *src = reinterpret_cast<const f32x4 *>(kh + crow * kHeadDim + 16 * g);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    f32x4 tt = cok ? src[j] : f32x4{0.f, 0.f, 0.f, 0.f};
-                    kf[4 * j] = tt[0];
-                    kf[4 * j + 1] = tt[1];
-                    kf[4 * j + 2] = tt[2];
-                    kf[4 * j + 3] = tt[3];
-                }
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 tt = src[j];
+                kf[t][4 * j] = tt[0];
+                kf[t][4 * j + 1] = tt[1];
+                kf[t][4 * j + 2] = tt[2];
+                kf[t][4 * j + 3] = tt[3];
+            }
+        }
 #pragma unroll
-                for (int s = 0; s < 16; ++s) acc = mfma_f32_4(kf[s], qf[s], acc);
+        for (int t = 0; t < kSelTilesPerChunk; ++t) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int c = base + 4 * g + i;
-                    keys[4 * t + i] = (c < n) ? score_key(acc[i], (uint32_t)c) : 0ull;
-                }
-            } else {
+            for (int s = 0; s < 16; ++s) acc = mfma_f32_4(kf[t][s], qf[s], acc);
+            const bool live = t0 + t < ntiles;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) keys[4 * t + i] = 0ull;
+            for (int i = 0; i < 4; ++i) {
+                const int c = base[t] + 4 * g + i;
+                keys[4 * t + i] = (live && c < n) ? score_key(acc[i], (uint32_t)c) : 0ull;
             }
         }
 #pragma unroll

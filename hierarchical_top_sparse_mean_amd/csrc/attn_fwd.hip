@@ -258,6 +258,153 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     if (g == 0) lse[(int64_t)h * a.N + ib * kBlock + c16] = (m + log2f(lsum)) * kLn2;
 }
 
+// ------------------------------------------------------------ fast path
+// K_1 = KT fine tiles and at most 16 coarse entries (one tile) with no pick
+// that can be dropped (K_1 < B): the shape of every bf16 workload here.  The 4
+// query blocks of a workgroup lie under one level-2 node and share their
+// coarse picks, so the workgroup stages that coarse tile once in LDS as bf16
+// (pooled K rows for the MFMA operand, V rows for the transposing read).
+// Fine and coarse tiles form one softmax chunk: one max, no rescaling, and
+// every loop is unrolled.
+template <int KT>
+__global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
+    const float *__restrict__ pk, const float *__restrict__ pv, const int32_t *__restrict__ idx,
+    __bf16 *__restrict__ o, float *__restrict__ lse, FwdArgs a) {
+    static_assert(KT % 4 == 0 && KT <= kFwdTiles, "fine tiles are paired within halves");
+    constexpr int kHalf = KT / 2;   // V tiles staged at a time (LDS per wave)
+    __shared__ __attribute__((aligned(16))) __bf16 vs_all[4][kHalf * kTileElems];
+    __shared__ __attribute__((aligned(16))) __bf16 ck[kTileElems];
+    __shared__ __attribute__((aligned(16))) __bf16 cv[kTileElems];
+    __shared__ float cbias[kBlock];
+    const int w = wave_id();
+    const int lane = lane_id();
+    const int g = lane >> 4, c16 = lane & 15;
+    const int64_t blk0 = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * 4;   // all 4 blocks valid
+    const int64_t blk = blk0 + w;
+    const int h = (int)(blk0 / a.n1);
+    const int ib0 = (int)(blk0 % a.n1);
+    const int ib = ib0 + w;
+    const int64_t head_off = (int64_t)h * a.N * kHeadDim;
+    const __bf16 *kh = k + head_off;
+    const __bf16 *vh = v + head_off;
+    __bf16 *vw = vs_all[w];
+
+    // ---- this wave's loads: Q, then every fine K / V tile
+    const __bf16 *qrow = q + head_off + (int64_t)(ib * kBlock + c16) * kHeadDim;
+    const bf16x8 qa0 = load_bf16x8(qrow + 8 * g);
+    const bf16x8 qa1 = load_bf16x8(qrow + 32 + 8 * g);
+    const int32_t *fine = idx + blk * KT;
+    bf16x8 kr[KT][2], vr[KT][2];
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+        const int f = __builtin_amdgcn_readfirstlane(fine[t]);
+        const __bf16 *kt = kh + (int64_t)f * kBlock * kHeadDim;
+        const __bf16 *vt = vh + (int64_t)f * kBlock * kHeadDim;
+        kr[t][0] = load_bf16x8(kt + c16 * kHeadDim + 8 * g);
+        kr[t][1] = load_bf16x8(kt + c16 * kHeadDim + 32 + 8 * g);
+        vr[t][0] = load_bf16x8(vt + lane * 8);
+        vr[t][1] = load_bf16x8(vt + (lane + kWave) * 8);
+    }
+    // ---- coarse tile, staged by the whole workgroup: thread (entry e, quarter p)
+    {
+        const int e = threadIdx.x >> 4, part = threadIdx.x & 15;   // 16 entries x 16 x 4 columns
+        int j, pick;
+        const bool ok = coarse_locate(a, e, j, pick);
+        const int js = ok ? j : 0, ps = ok ? pick : 0;
+        const int anc = ib0 >> (4 * (js + 1));                       // ancestor at level js+2
+        const int c = idx[a.cl_idx_off[js] + ((int64_t)h * a.cl_n[js] + anc) * a.cl_k[js] + ps];
+        const int64_t row = a.cl_pyr_off[js] + ((int64_t)h * a.cl_n[js] + c) * kHeadDim + 4 * part;
+        f32x4 kk = *reinterpret_cast<const f32x4 *>(pk + row);
+        f32x4 vv = *reinterpret_cast<const f32x4 *>(pv + row);
+        if (!ok) kk = vv = f32x4{0.f, 0.f, 0.f, 0.f};
+        const bf16x4 kb = {(__bf16)kk[0], (__bf16)kk[1], (__bf16)kk[2], (__bf16)kk[3]};
+        const bf16x4 vb = {(__bf16)vv[0], (__bf16)vv[1], (__bf16)vv[2], (__bf16)vv[3]};
+        *reinterpret_cast<u32x2 *>(&ck[e * kVStride + 4 * part]) = __builtin_bit_cast(u32x2, kb);
+        *reinterpret_cast<u32x2 *>(&cv[e * kVStride + 4 * part]) = __builtin_bit_cast(u32x2, vb);
+        if (part == 0) cbias[e] = ok ? 4.0f * (float)(js + 2) : -INFINITY;
+    }
+    // ---- fine scores (V stays in registers until its half is staged)
+    f32x4 st[KT];
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+        st[t] = mfma_bf16_32(kr[t][1], qa1, mfma_bf16_32(kr[t][0], qa0, f32x4{0.f, 0.f, 0.f, 0.f})) * a.sl2;
+    __syncthreads();   // coarse tile staged
+    const __bf16 *ckr = ck + c16 * kVStride;
+    f32x4 sc = mfma_bf16_32(load_bf16x8(ckr + 32 + 8 * g), qa1,
+                            mfma_bf16_32(load_bf16x8(ckr + 8 * g), qa0, f32x4{0.f, 0.f, 0.f, 0.f})) * a.sl2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] += cbias[4 * g + i];
+    // ---- one softmax over all KT + 1 tiles
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[t][i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[i]);
+    mx = max4_groups(mx);
+    float lsum = 0.f;
+    f32x4 oacc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int rofs = (4 * g + (c16 >> 2)) * kVStride + 4 * (c16 & 3);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        wave_lds_sync();
+#pragma unroll
+        for (int t = 0; t < kHalf; ++t)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int ci = lane + kWave * r;
+                store_bf16x8(vw + t * kTileElems + (ci >> 3) * kVStride + (ci & 7) * 8, vr[half * kHalf + t][r]);
+            }
+        wave_lds_sync();
+#pragma unroll
+        for (int tp = 0; tp < kHalf / 2; ++tp) {
+            const int t0 = half * kHalf + 2 * tp;
+            float p0[4], p1[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p0[i] = exp2f(st[t0][i] - mx);
+                p1[i] = exp2f(st[t0 + 1][i] - mx);
+                lsum += p0[i] + p1[i];
+            }
+            const bf16x8 pb = {(__bf16)p0[0], (__bf16)p0[1], (__bf16)p0[2], (__bf16)p0[3],
+                               (__bf16)p1[0], (__bf16)p1[1], (__bf16)p1[2], (__bf16)p1[3]};
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const bf16x4 v0 = lds_read_tr4(vw + (2 * tp) * kTileElems + rofs + 16 * dt);
+                const bf16x4 v1 = lds_read_tr4(vw + (2 * tp + 1) * kTileElems + rofs + 16 * dt);
+                oacc[dt] = mfma_bf16_32(cat8(v0, v1), pb, oacc[dt]);
+            }
+        }
+    }
+    {
+        float pc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pc[i] = exp2f(sc[i] - mx);
+            lsum += pc[i];
+        }
+        const bf16x4 pcb = {(__bf16)pc[0], (__bf16)pc[1], (__bf16)pc[2], (__bf16)pc[3]};
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            oacc[dt] = mfma_bf16_16(lds_read_tr4(cv + rofs + 16 * dt), pcb, oacc[dt]);
+    }
+    // ---- normalise and store
+    lsum = sum4_groups(lsum);
+    const float inv = 1.0f / lsum;
+    __bf16 *orow = o + head_off + (int64_t)(ib * kBlock + c16) * kHeadDim + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        const f32x4 r = oacc[dt] * inv;
+        const bf16x4 rb = {(__bf16)r[0], (__bf16)r[1], (__bf16)r[2], (__bf16)r[3]};
+        *reinterpret_cast<u32x2 *>(orow + 16 * dt) = __builtin_bit_cast(u32x2, rb);
+    }
+    if (g == 0) lse[(int64_t)h * a.N + ib * kBlock + c16] = (mx + log2f(lsum)) * kLn2;
+}
+
 // ---------------------------------------------------------------- f32 path
 __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
@@ -314,9 +461,16 @@ hipError_t launch_attn_fwd(const Geometry &g, const void *q, const void *k, cons
     const FwdArgs a = make_fwd_args(g);
     if (g.bf16) {
         const int64_t blocks = (int64_t)g.bh * g.n[1];
-        hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3((unsigned)((blocks + 3) / 4)), dim3(256), 0,
-                           s, (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx,
-                           (__bf16 *)o, lse, a);
+        const bool fast = g.L >= 2 && a.K1 == 8 && a.ncoarse > 0 && a.ncoarse <= kBlock &&
+                          !(a.drop && a.K1 >= kBlock) && a.n1 % 4 == 0;
+        if (fast)
+            hipLaunchKernelGGL(attn_fwd_fast_kernel<8>, dim3((unsigned)(blocks / 4)), dim3(256), 0, s,
+                               (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx,
+                               (__bf16 *)o, lse, a);
+        else
+            hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3((unsigned)((blocks + 3) / 4)), dim3(256), 0,
+                               s, (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx,
+                               (__bf16 *)o, lse, a);
     } else {
         const int64_t total = (int64_t)g.bh * g.N;
         hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,

@@ -414,6 +414,241 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     }
 }
 
+// Pass A for the common shape: K_1 = 8 fine picks per query block and one
+// coarse tile (at most 16 coarse entries) that no block can drop (K_1 < B).
+// The 16 query blocks under a level-2 node share their coarse picks, so the
+// workgroup stages that tile once in LDS as bf16 together with its log2
+// weights.  Every wave streams the 32 fine tiles of its 4 query blocks
+// through two register sets without a break at block boundaries (the next
+// block's first tiles and its Q / dO are in flight while a block's coarse
+// part is computed); the wave's 32 fine picks are read once, one per lane.
+constexpr int kFastK1 = 8;
+constexpr int kFastTiles = 4 * kFastK1;   // fine tiles per wave
+constexpr int kPtS = 20;                  // float row stride of the P / dS exchange
+
+__global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
+    const float *__restrict__ pk, const float *__restrict__ pv, const int32_t *__restrict__ idx,
+    const float *__restrict__ lse, const __bf16 *__restrict__ dout, void *__restrict__ dq, BwdWs ws,
+    BwdArgs a) {
+    constexpr int kTileBytes = (3 * 4 + 2) * kTE * 2;          // K, Q, dO per wave + coarse K, V
+    constexpr int kRedBytes = 4 * 2 * kBlock * kHeadDim * 4;   // coarse partials of 4 waves
+    __shared__ __attribute__((aligned(16))) char smem[kTileBytes > kRedBytes ? kTileBytes : kRedBytes];
+    __shared__ float cbias[kBlock];
+    __shared__ __attribute__((aligned(16))) float lds_pt[4][2][kBlock * kPtS];  // coarse P, dS entry-major
+    typedef __bf16 Tile[kTE];
+    Tile *lds_k = reinterpret_cast<Tile *>(smem);
+    Tile *lds_q = lds_k + 4;
+    Tile *lds_do = lds_q + 4;
+    __bf16 *ck = reinterpret_cast<__bf16 *>(lds_do + 4);
+    __bf16 *cv = ck + kTE;
+    typedef float RedTile[2][kBlock * kHeadDim];
+    RedTile *lds_red = reinterpret_cast<RedTile *>(smem);
+
+    const int w = wave_id();
+    const int lane = lane_id();
+    const int g = lane >> 4, c16 = lane & 15;
+    const int gph = a.n1 / kBlock;
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = bid / gph;
+    const int G = bid % gph;
+    const int ib0 = G * kBlock;
+    const int64_t head_off = (int64_t)h * a.N * kHeadDim;
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+    // ---- coarse tile, staged by the whole workgroup: thread (entry e, quarter p)
+    {
+        const int e = threadIdx.x >> 4, part = threadIdx.x & 15;
+        int j = 0, pick = e;
+        while (j < a.ncl - 1 && pick >= a.cl_k[j]) {
+            pick -= a.cl_k[j];
+            ++j;
+        }
+        const bool ok = e < a.ncoarse;
+        const int js = ok ? j : 0, ps = ok ? pick : 0;
+        const int anc = ib0 >> (4 * (js + 1));   // ancestor at level js + 2
+        const int c = idx[a.cl_idx_off[js] + ((int64_t)h * a.cl_n[js] + anc) * a.cl_k[js] + ps];
+        const int64_t roff = a.cl_pyr_off[js] + ((int64_t)h * a.cl_n[js] + c) * kHeadDim + 4 * part;
+        f32x4 kk = *reinterpret_cast<const f32x4 *>(pk + roff);
+        f32x4 vv = *reinterpret_cast<const f32x4 *>(pv + roff);
+        if (!ok) kk = vv = zero4;
+        const bf16x4 kb = {(__bf16)kk[0], (__bf16)kk[1], (__bf16)kk[2], (__bf16)kk[3]};
+        const bf16x4 vb = {(__bf16)vv[0], (__bf16)vv[1], (__bf16)vv[2], (__bf16)vv[3]};
+        *reinterpret_cast<u32x2 *>(&ck[e * kTS + 4 * part]) = __builtin_bit_cast(u32x2, kb);
+        *reinterpret_cast<u32x2 *>(&cv[e * kTS + 4 * part]) = __builtin_bit_cast(u32x2, vb);
+        if (part == 0) cbias[e] = ok ? 4.0f * (float)(js + 2) : -INFINITY;
+    }
+
+    // ---- this wave's fine picks: lane u < 32 holds pick u % 8 of block u / 8
+    const int fidx = lane < kFastTiles ? idx[((int64_t)h * a.n1 + ib0 + w * 4) * kFastK1 + lane] : 0;
+    struct TileRegs {
+        bf16x8 ka0, ka1, va0, va1;
+    };
+    auto load_tile = [&](int u, TileRegs &R) {
+        const int f = __builtin_amdgcn_readlane(fidx, u);
+        const __bf16 *kt = k + head_off + (int64_t)f * kBlock * kHeadDim + c16 * kHeadDim;
+        const __bf16 *vt = v + head_off + (int64_t)f * kBlock * kHeadDim + c16 * kHeadDim;
+        R.ka0 = load_bf16x8(kt + 8 * g);
+        R.ka1 = load_bf16x8(kt + 32 + 8 * g);
+        R.va0 = load_bf16x8(vt + 8 * g);
+        R.va1 = load_bf16x8(vt + 32 + 8 * g);
+    };
+    struct QRegs {
+        bf16x8 qa0, qa1, da0, da1;
+        float lse2;
+    };
+    auto load_q = [&](int jb, QRegs &X) {
+        const int64_t row = (int64_t)(ib0 + w * 4 + jb) * kBlock + c16;
+        const __bf16 *qrow = q + head_off + row * kHeadDim;
+        const __bf16 *drow = dout + head_off + row * kHeadDim;
+        X.qa0 = load_bf16x8(qrow + 8 * g);
+        X.qa1 = load_bf16x8(qrow + 32 + 8 * g);
+        X.da0 = load_bf16x8(drow + 8 * g);
+        X.da1 = load_bf16x8(drow + 32 + 8 * g);
+        X.lse2 = lse[(int64_t)h * a.N + row] * kLog2e;
+    };
+    QRegs X;
+    load_q(0, X);
+    constexpr int PD = 2;   // tiles in flight
+    TileRegs R[PD];
+#pragma unroll
+    for (int r = 0; r < PD; ++r) load_tile(r, R[r]);
+
+    f32x4 dkc[4], dvc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        dkc[dt] = zero4;
+        dvc[dt] = zero4;
+    }
+    const int rofs = (4 * g + (c16 >> 2)) * kTS + 4 * (c16 & 3);  // transposed-read address
+    __syncthreads();   // coarse tile staged
+
+    for (int jb = 0; jb < 4; ++jb) {
+        const int64_t row = (int64_t)(ib0 + w * 4 + jb) * kBlock + c16;
+        const bf16x8 qa0 = X.qa0, qa1 = X.qa1, da0 = X.da0, da1 = X.da1;
+        const float lse2 = X.lse2;
+        wave_lds_sync();
+        store_bf16x8(&lds_q[w][c16 * kTS + 8 * g], qa0);
+        store_bf16x8(&lds_q[w][c16 * kTS + 32 + 8 * g], qa1);
+        store_bf16x8(&lds_do[w][c16 * kTS + 8 * g], da0);
+        store_bf16x8(&lds_do[w][c16 * kTS + 32 + 8 * g], da1);
+
+        // dQ = scale * (A - D B), A = sum_j P_j dP_j k_j, B = sum_j P_j k_j,
+        // D = sum_j P_j dP_j; the coarse entries come last, when D is complete.
+        f32x4 accA[4], accB[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            accA[dt] = zero4;
+            accB[dt] = zero4;
+        }
+        float dsum = 0.f;
+        auto fine_tile = [&](const TileRegs &R) {
+            wave_lds_sync();
+            store_bf16x8(&lds_k[w][c16 * kTS + 8 * g], R.ka0);
+            store_bf16x8(&lds_k[w][c16 * kTS + 32 + 8 * g], R.ka1);
+            const f32x4 s = mfma_bf16_32(R.ka1, qa1, mfma_bf16_32(R.ka0, qa0, zero4));
+            const f32x4 dp = mfma_bf16_32(R.va1, da1, mfma_bf16_32(R.va0, da0, zero4));
+            float p[4], x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] = exp2f(s[i] * a.sl2 - lse2);
+                x[i] = p[i] * dp[i];
+                dsum += x[i];
+            }
+            bf16x4 phi, plo, xhi, xlo;
+            split4(p, phi, plo);
+            split4(x, xhi, xlo);
+            const bf16x8 pcat = cat8(phi, plo), xcat = cat8(xhi, xlo);
+            wave_lds_sync();
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const bf16x4 kT = lds_read_tr4(&lds_k[w][rofs + 16 * dt]);
+                const bf16x8 kk = cat8(kT, kT);
+                accA[dt] = mfma_bf16_32(kk, xcat, accA[dt]);
+                accB[dt] = mfma_bf16_32(kk, pcat, accB[dt]);
+            }
+        };
+#pragma unroll
+        for (int t = 0; t < kFastK1; t += PD)
+#pragma unroll
+            for (int r = 0; r < PD; ++r) {
+                const int u = jb * kFastK1 + t + r;
+                fine_tile(R[r]);
+                if (u + PD < kFastTiles) load_tile(u + PD, R[r]);
+            }
+        // ---- coarse entries: lane (query c16, entries 4g+i)
+        const __bf16 *ckr = ck + c16 * kTS;
+        const __bf16 *cvr = cv + c16 * kTS;
+        f32x4 cs = mfma_bf16_32(load_bf16x8(ckr + 32 + 8 * g), qa1,
+                                mfma_bf16_32(load_bf16x8(ckr + 8 * g), qa0, zero4));
+        const f32x4 cdp = mfma_bf16_32(load_bf16x8(cvr + 32 + 8 * g), da1,
+                                       mfma_bf16_32(load_bf16x8(cvr + 8 * g), da0, zero4));
+        if (jb + 1 < 4) load_q(jb + 1, X);   // next block's Q / dO in flight from here
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            cs[i] = exp2f(cs[i] * a.sl2 + cbias[4 * g + i] - lse2);
+            dsum += cs[i] * cdp[i];
+        }
+        const float Dq = sum4_groups(dsum);
+        if (g == 0) ws.D[(int64_t)h * a.N + row] = Dq;
+        float ds[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ds[i] = cs[i] * (cdp[i] - Dq);
+        // P and dS go through LDS entry-major: read back, lane (entry c16,
+        // queries 4g+i) holds the operand of the coarse-partial contractions
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lds_pt[w][0][(4 * g + i) * kPtS + c16] = cs[i];
+            lds_pt[w][1][(4 * g + i) * kPtS + c16] = ds[i];
+        }
+        wave_lds_sync();
+        const f32x4 p2v = *reinterpret_cast<const f32x4 *>(&lds_pt[w][0][c16 * kPtS + 4 * g]);
+        const f32x4 d2v = *reinterpret_cast<const f32x4 *>(&lds_pt[w][1][c16 * kPtS + 4 * g]);
+        float ds2[4], p2[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p2[i] = p2v[i];
+            ds2[i] = d2v[i];
+        }
+        bf16x4 dhi, dlo, d2hi, d2lo, p2hi, p2lo;
+        split4(ds, dhi, dlo);
+        split4(ds2, d2hi, d2lo);
+        split4(p2, p2hi, p2lo);
+        const bf16x8 dcat = cat8(dhi, dlo), d2cat = cat8(d2hi, d2lo), p2cat = cat8(p2hi, p2lo);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const bf16x4 kT = lds_read_tr4(&ck[rofs + 16 * dt]);
+            accA[dt] = mfma_bf16_32(cat8(kT, kT), dcat, accA[dt]);   // + Kc^T dS_c
+            const bf16x4 qT = lds_read_tr4(&lds_q[w][rofs + 16 * dt]);
+            const bf16x4 dT = lds_read_tr4(&lds_do[w][rofs + 16 * dt]);
+            dkc[dt] = mfma_bf16_32(d2cat, cat8(qT, qT), dkc[dt]);
+            dvc[dt] = mfma_bf16_32(p2cat, cat8(dT, dT), dvc[dt]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            store_grad4(dq, head_off + row * kHeadDim + 16 * dt + 4 * g,
+                        (accA[dt] - Dq * accB[dt]) * a.scale, a.grad_bf16);
+    }
+    // ---- reduce the coarse partials over the 4 waves
+    __syncthreads();
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ent = 4 * g + i, dim = 16 * dt + c16;
+            lds_red[w][0][ent * kHeadDim + dim] = dkc[dt][i] * a.scale;
+            lds_red[w][1][ent * kHeadDim + dim] = dvc[dt][i];
+        }
+    __syncthreads();
+    float *part = ws.partial + ((int64_t)h * a.n2 + G) * a.ncoarse * 2 * kHeadDim;
+    for (int x = threadIdx.x; x < a.ncoarse * 2 * kHeadDim; x += 256) {
+        const int er = x / (2 * kHeadDim), kv = (x / kHeadDim) & 1, dim = x % kHeadDim;
+        const int oo = er * kHeadDim + dim;
+        part[x] = lds_red[0][kv][oo] + lds_red[1][kv][oo] + lds_red[2][kv][oo] + lds_red[3][kv][oo];
+    }
+}
+
 // ================================================================ pass B
 // One wave per pooled token c of level l (lanes = columns): the level-l rows
 // that picked c come from the CSR of I^(l); each lane looks up one row's slot
@@ -462,17 +697,20 @@ __global__ __launch_bounds__(256) void bwd_coarse_reduce_kernel(const int32_t *_
 }
 
 // ================================================================ pass C
-__global__ __launch_bounds__(256, 2) void bwd_dkv_bf16_kernel(
+// One wave per key block, in a workgroup of its own: key blocks differ widely
+// in how many query blocks picked them, and no wave waits for a slower
+// sibling before its slot is reused.
+__global__ __launch_bounds__(64, 4) void bwd_dkv_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ lse, const __bf16 *__restrict__ dout, const int32_t *__restrict__ csr_ptr,
     const int32_t *__restrict__ csr_col, void *__restrict__ dk, void *__restrict__ dv, BwdWs ws,
     BwdArgs a) {
-    __shared__ __attribute__((aligned(16))) __bf16 lds_q[4][kTE];
-    __shared__ __attribute__((aligned(16))) __bf16 lds_do[4][kTE];
-    const int w = wave_id();
+    __shared__ __attribute__((aligned(16))) __bf16 lds_q[1][kTE];
+    __shared__ __attribute__((aligned(16))) __bf16 lds_do[1][kTE];
+    constexpr int w = 0;
     const int lane = lane_id();
     const int g = lane >> 4, c16 = lane & 15;
-    const int64_t kb = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + w;
+    const int64_t kb = xcd_remap(blockIdx.x, gridDim.x);
     if (kb >= (int64_t)a.bh * a.n1) return;
     const int h = (int)(kb / a.n1);
     const int f = (int)(kb % a.n1);
@@ -546,12 +784,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_bf16_kernel(
         const int colv = lane < cnt ? C[base + lane] : 0;
         Pair A, Bp;
         load_pair(__builtin_amdgcn_readlane(colv, 0), A);
-        for (int j = 0; j < cnt; j += 2) {
-            load_pair(__builtin_amdgcn_readlane(colv, min(j + 1, cnt - 1)), Bp);
+        load_pair(__builtin_amdgcn_readlane(colv, min(1, cnt - 1)), Bp);
+        // both computes unconditional inside the loop: at its head the older
+        // set is always A, so the wait covers A's loads only
+        int j = 0;
+        for (; j + 2 <= cnt; j += 2) {
             compute(A);
             load_pair(__builtin_amdgcn_readlane(colv, min(j + 2, cnt - 1)), A);
-            if (j + 1 < cnt) compute(Bp);
+            compute(Bp);
+            load_pair(__builtin_amdgcn_readlane(colv, min(j + 3, cnt - 1)), Bp);
         }
+        if (j < cnt) compute(A);
     }
     // C layout: lane (dim 16dt + c16, keys 4g+i); add pooled-level gradients / B^l
 #pragma unroll
@@ -750,7 +993,13 @@ hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, cons
         const int gph = (a.n1 + kBlock - 1) / kBlock;
         const int nct = (a.ncoarse + kBlock - 1) / kBlock;
         const dim3 grid((unsigned)(g.bh * gph));
-        if (nct == 0)
+        const bool fast = g.L >= 2 && a.K1 == kFastK1 && nct == 1 && a.n1 % kBlock == 0 &&
+                          !(a.drop && a.K1 >= kBlock);
+        if (fast)
+            hipLaunchKernelGGL(bwd_dq_fast_kernel, grid, dim3(256), 0, s, (const __bf16 *)q,
+                               (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx, lse,
+                               (const __bf16 *)dout, dq, ws, a);
+        else if (nct == 0)
             hipLaunchKernelGGL(bwd_dq_bf16_kernel<0>, grid, dim3(256), 0, s, (const __bf16 *)q,
                                (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx, lse,
                                (const __bf16 *)dout, dq, ws, a);
@@ -768,7 +1017,7 @@ hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, cons
                                dim3(256), 0, s, idx, csr_ptr, csr_col, ws, a, j);
         }
         const int64_t kbs = (int64_t)g.bh * a.n1;
-        hipLaunchKernelGGL(bwd_dkv_bf16_kernel, dim3((unsigned)((kbs + 3) / 4)), dim3(256), 0, s,
+        hipLaunchKernelGGL(bwd_dkv_bf16_kernel, dim3((unsigned)kbs), dim3(kWave), 0, s,
                            (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, lse,
                            (const __bf16 *)dout, csr_ptr + g.ptr_off[1], csr_col + g.col_off[1], dk,
                            dv, ws, a);

@@ -135,7 +135,7 @@ __device__ __forceinline__ bool bwd_coarse_entry(const BwdArgs &a, const int32_t
 
 __device__ __forceinline__ void store_grad4(void *base, int64_t off, f32x4 v, int bf) {
     if (bf) {
-        const bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        const bf16x4 b = to_bf16x4(f32x4{v[0], v[1], v[2], v[3]});
         *reinterpret_cast<u32x2 *>((__bf16 *)base + off) = __builtin_bit_cast(u32x2, b);
     } else {
         *reinterpret_cast<f32x4 *>((float *)base + off) = v;
@@ -164,11 +164,14 @@ __device__ __forceinline__ float dot8(bf16x8 a, bf16x8 b) {
 // gradient contractions run as two bf16 MFMAs so that rounding dS or P to
 // bf16 does not limit the accuracy of sums over hundreds of queries.
 __device__ __forceinline__ void split4(const float (&x)[4], bf16x4 &hi, bf16x4 &lo) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        hi[i] = (__bf16)x[i];
-        lo[i] = (__bf16)(x[i] - (float)hi[i]);
-    }
+    const f32x4 xv = {x[0], x[1], x[2], x[3]};
+    hi = to_bf16x4(xv);
+    const u32x2 hb = __builtin_bit_cast(u32x2, hi);   // hi widened back by shifts
+    const f32x4 back = {__builtin_bit_cast(float, hb[0] << 16),
+                        __builtin_bit_cast(float, hb[0] & 0xffff0000u),
+                        __builtin_bit_cast(float, hb[1] << 16),
+                        __builtin_bit_cast(float, hb[1] & 0xffff0000u)};
+    lo = to_bf16x4(xv - back);
 }
 
 // Operand rows of coarse tile ct for query block ib: lane row = entry ct*16+c16.
@@ -307,7 +310,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
             float p[4], x[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p[i] = exp2f(s[i] * a.sl2 - lse2);
+                p[i] = fast_exp2(s[i] * a.sl2 - lse2);
                 x[i] = p[i] * dp[i];
                 dsum += x[i];
             }
@@ -342,7 +345,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
             cdp2[ct] = mfma_bf16_32(da1, T[ct].va1, mfma_bf16_32(da0, T[ct].va0, zero4));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                cs[ct][i] = exp2f(cs[ct][i] * a.sl2 + T[ct].bias4[i] - lse2);
+                cs[ct][i] = fast_exp2(cs[ct][i] * a.sl2 + T[ct].bias4[i] - lse2);
                 dsum += cs[ct][i] * cdp[ct][i];
             }
         }
@@ -364,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
                 ds[i] = cs[ct][i] * (cdp[ct][i] - Dq);
                 const float l2q = lds_row[w][0][4 * g + i];
                 const float Dqi = lds_row[w][1][4 * g + i];
-                p2[i] = exp2f(cs2[ct][i] * a.sl2 + T[ct].bias_row - l2q);
+                p2[i] = fast_exp2(cs2[ct][i] * a.sl2 + T[ct].bias_row - l2q);
                 ds2[i] = p2[i] * (cdp2[ct][i] - Dqi);
             }
             bf16x4 dhi, dlo, d2hi, d2lo, p2hi, p2lo;
@@ -431,14 +434,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
     const float *__restrict__ pk, const float *__restrict__ pv, const int32_t *__restrict__ idx,
     const float *__restrict__ lse, const __bf16 *__restrict__ dout, void *__restrict__ dq, BwdWs ws,
     BwdArgs a) {
-    constexpr int kTileBytes = (3 * 4 + 2) * kTE * 2;          // K, Q, dO per wave + coarse K, V
+    constexpr int kTileBytes = (4 * 4 + 2) * kTE * 2;          // K, V, Q, dO per wave + coarse K, V
     constexpr int kRedBytes = 4 * 2 * kBlock * kHeadDim * 4;   // coarse partials of 4 waves
     __shared__ __attribute__((aligned(16))) char smem[kTileBytes > kRedBytes ? kTileBytes : kRedBytes];
     __shared__ float cbias[kBlock];
     __shared__ __attribute__((aligned(16))) float lds_pt[4][2][kBlock * kPtS];  // coarse P, dS entry-major
     typedef __bf16 Tile[kTE];
     Tile *lds_k = reinterpret_cast<Tile *>(smem);
-    Tile *lds_q = lds_k + 4;
+    Tile *lds_v = lds_k + 4;
+    Tile *lds_q = lds_v + 4;
     Tile *lds_do = lds_q + 4;
     __bf16 *ck = reinterpret_cast<__bf16 *>(lds_do + 4);
     __bf16 *cv = ck + kTE;
@@ -472,8 +476,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
         f32x4 kk = *reinterpret_cast<const f32x4 *>(pk + roff);
         f32x4 vv = *reinterpret_cast<const f32x4 *>(pv + roff);
         if (!ok) kk = vv = zero4;
-        const bf16x4 kb = {(__bf16)kk[0], (__bf16)kk[1], (__bf16)kk[2], (__bf16)kk[3]};
-        const bf16x4 vb = {(__bf16)vv[0], (__bf16)vv[1], (__bf16)vv[2], (__bf16)vv[3]};
+        const bf16x4 kb = to_bf16x4(f32x4{kk[0], kk[1], kk[2], kk[3]});
+        const bf16x4 vb = to_bf16x4(f32x4{vv[0], vv[1], vv[2], vv[3]});
         *reinterpret_cast<u32x2 *>(&ck[e * kTS + 4 * part]) = __builtin_bit_cast(u32x2, kb);
         *reinterpret_cast<u32x2 *>(&cv[e * kTS + 4 * part]) = __builtin_bit_cast(u32x2, vb);
         if (part == 0) cbias[e] = ok ? 4.0f * (float)(js + 2) : -INFINITY;
@@ -484,28 +488,36 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
     struct TileRegs {
         bf16x8 ka0, ka1, va0, va1;
     };
+    // Global loads read whole 128-byte rows (lane l: row l / 8 and l / 8 + 8,
+    // 16-byte chunk l % 8); the rows pass through LDS, from where the MFMA
+    // operands (lane: row c16, dims 8g.. and 32+8g..) are read back.
+    const int lrow = lane >> 3, lcol = (lane & 7) * 8;
+    auto stage_rows = [&](__bf16 *dst, bf16x8 r0, bf16x8 r1) {
+        store_bf16x8(dst + lrow * kTS + lcol, r0);
+        store_bf16x8(dst + (lrow + 8) * kTS + lcol, r1);
+    };
     auto load_tile = [&](int u, TileRegs &R) {
         const int f = __builtin_amdgcn_readlane(fidx, u);
-        const __bf16 *kt = k + head_off + (int64_t)f * kBlock * kHeadDim + c16 * kHeadDim;
-        const __bf16 *vt = v + head_off + (int64_t)f * kBlock * kHeadDim + c16 * kHeadDim;
-        R.ka0 = load_bf16x8(kt + 8 * g);
-        R.ka1 = load_bf16x8(kt + 32 + 8 * g);
-        R.va0 = load_bf16x8(vt + 8 * g);
-        R.va1 = load_bf16x8(vt + 32 + 8 * g);
+        const __bf16 *kt = k + head_off + (int64_t)f * kBlock * kHeadDim;
+        const __bf16 *vt = v + head_off + (int64_t)f * kBlock * kHeadDim;
+        R.ka0 = load_bf16x8(kt + lane * 8);
+        R.ka1 = load_bf16x8(kt + (lane + kWave) * 8);
+        R.va0 = load_bf16x8(vt + lane * 8);
+        R.va1 = load_bf16x8(vt + (lane + kWave) * 8);
     };
     struct QRegs {
         bf16x8 qa0, qa1, da0, da1;
         float lse2;
     };
     auto load_q = [&](int jb, QRegs &X) {
-        const int64_t row = (int64_t)(ib0 + w * 4 + jb) * kBlock + c16;
-        const __bf16 *qrow = q + head_off + row * kHeadDim;
-        const __bf16 *drow = dout + head_off + row * kHeadDim;
-        X.qa0 = load_bf16x8(qrow + 8 * g);
-        X.qa1 = load_bf16x8(qrow + 32 + 8 * g);
-        X.da0 = load_bf16x8(drow + 8 * g);
-        X.da1 = load_bf16x8(drow + 32 + 8 * g);
-        X.lse2 = lse[(int64_t)h * a.N + row] * kLog2e;
+        const int64_t row0 = (int64_t)(ib0 + w * 4 + jb) * kBlock;
+        const __bf16 *qb = q + head_off + row0 * kHeadDim;
+        const __bf16 *db = dout + head_off + row0 * kHeadDim;
+        X.qa0 = load_bf16x8(qb + lane * 8);
+        X.qa1 = load_bf16x8(qb + (lane + kWave) * 8);
+        X.da0 = load_bf16x8(db + lane * 8);
+        X.da1 = load_bf16x8(db + (lane + kWave) * 8);
+        X.lse2 = lse[(int64_t)h * a.N + row0 + c16] * kLog2e;
     };
     QRegs X;
     load_q(0, X);
@@ -525,13 +537,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
 
     for (int jb = 0; jb < 4; ++jb) {
         const int64_t row = (int64_t)(ib0 + w * 4 + jb) * kBlock + c16;
-        const bf16x8 qa0 = X.qa0, qa1 = X.qa1, da0 = X.da0, da1 = X.da1;
         const float lse2 = X.lse2;
         wave_lds_sync();
-        store_bf16x8(&lds_q[w][c16 * kTS + 8 * g], qa0);
-        store_bf16x8(&lds_q[w][c16 * kTS + 32 + 8 * g], qa1);
-        store_bf16x8(&lds_do[w][c16 * kTS + 8 * g], da0);
-        store_bf16x8(&lds_do[w][c16 * kTS + 32 + 8 * g], da1);
+        stage_rows(lds_q[w], X.qa0, X.qa1);
+        stage_rows(lds_do[w], X.da0, X.da1);
+        wave_lds_sync();
+        const bf16x8 qa0 = load_bf16x8(&lds_q[w][c16 * kTS + 8 * g]);
+        const bf16x8 qa1 = load_bf16x8(&lds_q[w][c16 * kTS + 32 + 8 * g]);
+        const bf16x8 da0 = load_bf16x8(&lds_do[w][c16 * kTS + 8 * g]);
+        const bf16x8 da1 = load_bf16x8(&lds_do[w][c16 * kTS + 32 + 8 * g]);
 
         // dQ = scale * (A - D B), A = sum_j P_j dP_j k_j, B = sum_j P_j k_j,
         // D = sum_j P_j dP_j; the coarse entries come last, when D is complete.
@@ -544,14 +558,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
         float dsum = 0.f;
         auto fine_tile = [&](const TileRegs &R) {
             wave_lds_sync();
-            store_bf16x8(&lds_k[w][c16 * kTS + 8 * g], R.ka0);
-            store_bf16x8(&lds_k[w][c16 * kTS + 32 + 8 * g], R.ka1);
-            const f32x4 s = mfma_bf16_32(R.ka1, qa1, mfma_bf16_32(R.ka0, qa0, zero4));
-            const f32x4 dp = mfma_bf16_32(R.va1, da1, mfma_bf16_32(R.va0, da0, zero4));
+            stage_rows(lds_k[w], R.ka0, R.ka1);
+            stage_rows(lds_v[w], R.va0, R.va1);
+            wave_lds_sync();
+            const __bf16 *kr = &lds_k[w][c16 * kTS + 8 * g];
+            const __bf16 *vr = &lds_v[w][c16 * kTS + 8 * g];
+            const f32x4 s = mfma_bf16_32(load_bf16x8(kr + 32), qa1, mfma_bf16_32(load_bf16x8(kr), qa0, zero4));
+            const f32x4 dp = mfma_bf16_32(load_bf16x8(vr + 32), da1, mfma_bf16_32(load_bf16x8(vr), da0, zero4));
             float p[4], x[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p[i] = exp2f(s[i] * a.sl2 - lse2);
+                p[i] = fast_exp2(s[i] * a.sl2 - lse2);
                 x[i] = p[i] * dp[i];
                 dsum += x[i];
             }
@@ -559,7 +576,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
             split4(p, phi, plo);
             split4(x, xhi, xlo);
             const bf16x8 pcat = cat8(phi, plo), xcat = cat8(xhi, xlo);
-            wave_lds_sync();
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
                 const bf16x4 kT = lds_read_tr4(&lds_k[w][rofs + 16 * dt]);
@@ -586,7 +602,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
         if (jb + 1 < 4) load_q(jb + 1, X);   // next block's Q / dO in flight from here
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            cs[i] = exp2f(cs[i] * a.sl2 + cbias[4 * g + i] - lse2);
+            cs[i] = fast_exp2(cs[i] * a.sl2 + cbias[4 * g + i] - lse2);
             dsum += cs[i] * cdp[i];
         }
         const float Dq = sum4_groups(dsum);
@@ -699,15 +715,18 @@ __global__ __launch_bounds__(256) void bwd_coarse_reduce_kernel(const int32_t *_
 // ================================================================ pass C
 // One wave per key block, in a workgroup of its own: key blocks differ widely
 // in how many query blocks picked them, and no wave waits for a slower
-// sibling before its slot is reused.
-__global__ __launch_bounds__(64, 4) void bwd_dkv_bf16_kernel(
+// sibling before its slot is reused.  The query blocks of the key's CSR
+// segment stream through a ring of kDkvDepth register sets, so that several
+// blocks' Q / dO are in flight while one is computed.
+constexpr int kDkvDepth = 4;
+__global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ lse, const __bf16 *__restrict__ dout, const int32_t *__restrict__ csr_ptr,
     const int32_t *__restrict__ csr_col, void *__restrict__ dk, void *__restrict__ dv, BwdWs ws,
     BwdArgs a) {
-    __shared__ __attribute__((aligned(16))) __bf16 lds_q[1][kTE];
-    __shared__ __attribute__((aligned(16))) __bf16 lds_do[1][kTE];
-    constexpr int w = 0;
+    __shared__ __attribute__((aligned(16))) __bf16 lds_q[kTE];
+    __shared__ __attribute__((aligned(16))) __bf16 lds_do[kTE];
+    __shared__ __attribute__((aligned(16))) float lds_ld[2 * kBlock];   // lse, D of the block's queries
     const int lane = lane_id();
     const int g = lane >> 4, c16 = lane & 15;
     const int64_t kb = xcd_remap(blockIdx.x, gridDim.x);
@@ -729,72 +748,81 @@ __global__ __launch_bounds__(64, 4) void bwd_dkv_bf16_kernel(
     const int32_t *P = csr_ptr + (int64_t)h * (a.n1 + 1);
     const int32_t *C = csr_col + (int64_t)h * a.n1 * a.K1;
     const int e0 = __builtin_amdgcn_readfirstlane(P[f]), e1 = __builtin_amdgcn_readfirstlane(P[f + 1]);
-    // The query blocks of the segment are read 64 at a time into one register
-    // (lane j holds entry j), and the next pair's Q / dO / lse / D are loaded
-    // while the current pair is computed.
+    // Per query block: its Q / dO tiles loaded as whole 128-byte rows per
+    // instruction (lane l: rows l / 8 and l / 8 + 8, 16-byte chunk l % 8),
+    // which pass through LDS before the MFMA operand rows are read back; and
+    // one float per lane (lanes 0-15 the queries' lse, 16-31 their D).
     struct Pair {
         bf16x8 qa0, qa1, da0, da1;
-        f32x4 l4, D4;
+        float ld;
     };
+    const float *ld_src = lane < kBlock ? lse : ws.D;
+    const int lrow = lane >> 3, lcol = (lane & 7) * 8;
     auto load_pair = [&](int ib, Pair &X) {
-        const int64_t row = (int64_t)ib * kBlock + c16;
-        const __bf16 *qr = q + head_off + row * kHeadDim;
-        const __bf16 *dr = dout + head_off + row * kHeadDim;
-        X.qa0 = load_bf16x8(qr + 8 * g);
-        X.qa1 = load_bf16x8(qr + 32 + 8 * g);
-        X.da0 = load_bf16x8(dr + 8 * g);
-        X.da1 = load_bf16x8(dr + 32 + 8 * g);
-        X.l4 = *reinterpret_cast<const f32x4 *>(lse + (int64_t)h * a.N + (int64_t)ib * kBlock + 4 * g);
-        X.D4 = *reinterpret_cast<const f32x4 *>(ws.D + (int64_t)h * a.N + (int64_t)ib * kBlock + 4 * g);
+        const __bf16 *qr = q + head_off + (int64_t)ib * kBlock * kHeadDim;
+        const __bf16 *dr = dout + head_off + (int64_t)ib * kBlock * kHeadDim;
+        X.qa0 = load_bf16x8(qr + lane * 8);
+        X.qa1 = load_bf16x8(qr + (lane + kWave) * 8);
+        X.da0 = load_bf16x8(dr + lane * 8);
+        X.da1 = load_bf16x8(dr + (lane + kWave) * 8);
+        X.ld = ld_src[(int64_t)h * a.N + (int64_t)ib * kBlock + c16];
     };
     auto compute = [&](const Pair &X) {
         wave_lds_sync();
-        store_bf16x8(&lds_q[w][c16 * kTS + 8 * g], X.qa0);
-        store_bf16x8(&lds_q[w][c16 * kTS + 32 + 8 * g], X.qa1);
-        store_bf16x8(&lds_do[w][c16 * kTS + 8 * g], X.da0);
-        store_bf16x8(&lds_do[w][c16 * kTS + 32 + 8 * g], X.da1);
-        // S = Q K^T: lane (key c16, queries 4g+i)
-        f32x4 s = mfma_bf16_32(X.qa0, kb0, f32x4{0.f, 0.f, 0.f, 0.f});
-        s = mfma_bf16_32(X.qa1, kb1, s);
-        f32x4 dp = mfma_bf16_32(X.da0, vb0, f32x4{0.f, 0.f, 0.f, 0.f});
-        dp = mfma_bf16_32(X.da1, vb1, dp);
+        store_bf16x8(&lds_q[lrow * kTS + lcol], X.qa0);
+        store_bf16x8(&lds_q[(lrow + 8) * kTS + lcol], X.qa1);
+        store_bf16x8(&lds_do[lrow * kTS + lcol], X.da0);
+        store_bf16x8(&lds_do[(lrow + 8) * kTS + lcol], X.da1);
+        if (lane < 2 * kBlock) lds_ld[lane] = X.ld;
+        wave_lds_sync();
+        const bf16x8 qa0 = load_bf16x8(&lds_q[c16 * kTS + 8 * g]);
+        const bf16x8 qa1 = load_bf16x8(&lds_q[c16 * kTS + 32 + 8 * g]);
+        const bf16x8 da0 = load_bf16x8(&lds_do[c16 * kTS + 8 * g]);
+        const bf16x8 da1 = load_bf16x8(&lds_do[c16 * kTS + 32 + 8 * g]);
+        f32x4 s = mfma_bf16_32(qa0, kb0, f32x4{0.f, 0.f, 0.f, 0.f});
+        s = mfma_bf16_32(qa1, kb1, s);
+        f32x4 dp = mfma_bf16_32(da0, vb0, f32x4{0.f, 0.f, 0.f, 0.f});
+        dp = mfma_bf16_32(da1, vb1, dp);
+        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lds_ld[4 * g]);
+        const f32x4 D4 = *reinterpret_cast<const f32x4 *>(&lds_ld[kBlock + 4 * g]);
         float pp[4], ds[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            pp[i] = exp2f(s[i] * a.sl2 - X.l4[i] * kLog2e);
-            ds[i] = pp[i] * (dp[i] - X.D4[i]);
+            pp[i] = fast_exp2(s[i] * a.sl2 - l4[i] * kLog2e);
+            ds[i] = pp[i] * (dp[i] - D4[i]);
         }
         bf16x4 phi, plo, dhi, dlo;
         split4(pp, phi, plo);
         split4(ds, dhi, dlo);
-        wave_lds_sync();
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-            const bf16x4 dT = lds_read_tr4(&lds_do[w][rofs + 16 * dt]);
-            const bf16x4 qT = lds_read_tr4(&lds_q[w][rofs + 16 * dt]);
+            const bf16x4 dT = lds_read_tr4(&lds_do[rofs + 16 * dt]);
+            const bf16x4 qT = lds_read_tr4(&lds_q[rofs + 16 * dt]);
             dva[dt] = mfma_bf16_32(cat8(phi, plo), cat8(dT, dT), dva[dt]);
             dka[dt] = mfma_bf16_32(cat8(dhi, dlo), cat8(qT, qT), dka[dt]);
         }
     };
-    // two register sets in turn: the loads of one pair are in flight while
-    // the other is computed (the reads past the segment's end repeat its last
-    // pair and are not used)
+    // The segment's query blocks are read 64 at a time into one register
+    // (lane j holds entry j).  Ring: set r holds entry j + r; after computing
+    // it, set r is refilled with entry j + r + kDkvDepth, so at the loop head
+    // the set needed next is always the oldest one in flight.
     for (int base = e0; base < e1; base += kWave) {
         const int cnt = min(kWave, e1 - base);
         const int colv = lane < cnt ? C[base + lane] : 0;
-        Pair A, Bp;
-        load_pair(__builtin_amdgcn_readlane(colv, 0), A);
-        load_pair(__builtin_amdgcn_readlane(colv, min(1, cnt - 1)), Bp);
-        // both computes unconditional inside the loop: at its head the older
-        // set is always A, so the wait covers A's loads only
+        Pair R[kDkvDepth];
+#pragma unroll
+        for (int r = 0; r < kDkvDepth; ++r)
+            load_pair(__builtin_amdgcn_readlane(colv, min(r, cnt - 1)), R[r]);
         int j = 0;
-        for (; j + 2 <= cnt; j += 2) {
-            compute(A);
-            load_pair(__builtin_amdgcn_readlane(colv, min(j + 2, cnt - 1)), A);
-            compute(Bp);
-            load_pair(__builtin_amdgcn_readlane(colv, min(j + 3, cnt - 1)), Bp);
-        }
-        if (j < cnt) compute(A);
+        for (; j + kDkvDepth <= cnt; j += kDkvDepth)
+#pragma unroll
+            for (int r = 0; r < kDkvDepth; ++r) {
+                compute(R[r]);
+                load_pair(__builtin_amdgcn_readlane(colv, min(j + kDkvDepth + r, cnt - 1)), R[r]);
+            }
+#pragma unroll
+        for (int r = 0; r < kDkvDepth - 1; ++r)
+            if (j + r < cnt) compute(R[r]);
     }
     // C layout: lane (dim 16dt + c16, keys 4g+i); add pooled-level gradients / B^l
 #pragma unroll

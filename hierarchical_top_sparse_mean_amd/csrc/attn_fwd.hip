@@ -252,7 +252,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
         const f32x4 r = oacc[dt] * inv;
-        const bf16x4 rb = {(__bf16)r[0], (__bf16)r[1], (__bf16)r[2], (__bf16)r[3]};
+        const bf16x4 rb = to_bf16x4(f32x4{r[0], r[1], r[2], r[3]});
         *reinterpret_cast<u32x2 *>(orow + 16 * dt) = __builtin_bit_cast(u32x2, rb);
     }
     if (g == 0) lse[(int64_t)h * a.N + ib * kBlock + c16] = (m + log2f(lsum)) * kLn2;
@@ -318,8 +318,8 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
         f32x4 kk = *reinterpret_cast<const f32x4 *>(pk + row);
         f32x4 vv = *reinterpret_cast<const f32x4 *>(pv + row);
         if (!ok) kk = vv = f32x4{0.f, 0.f, 0.f, 0.f};
-        const bf16x4 kb = {(__bf16)kk[0], (__bf16)kk[1], (__bf16)kk[2], (__bf16)kk[3]};
-        const bf16x4 vb = {(__bf16)vv[0], (__bf16)vv[1], (__bf16)vv[2], (__bf16)vv[3]};
+        const bf16x4 kb = to_bf16x4(f32x4{kk[0], kk[1], kk[2], kk[3]});
+        const bf16x4 vb = to_bf16x4(f32x4{vv[0], vv[1], vv[2], vv[3]});
         *reinterpret_cast<u32x2 *>(&ck[e * kVStride + 4 * part]) = __builtin_bit_cast(u32x2, kb);
         *reinterpret_cast<u32x2 *>(&cv[e * kVStride + 4 * part]) = __builtin_bit_cast(u32x2, vb);
         if (part == 0) cbias[e] = ok ? 4.0f * (float)(js + 2) : -INFINITY;
@@ -366,12 +366,12 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
             float p0[4], p1[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p0[i] = exp2f(st[t0][i] - mx);
-                p1[i] = exp2f(st[t0 + 1][i] - mx);
+                p0[i] = fast_exp2(st[t0][i] - mx);
+                p1[i] = fast_exp2(st[t0 + 1][i] - mx);
                 lsum += p0[i] + p1[i];
             }
-            const bf16x8 pb = {(__bf16)p0[0], (__bf16)p0[1], (__bf16)p0[2], (__bf16)p0[3],
-                               (__bf16)p1[0], (__bf16)p1[1], (__bf16)p1[2], (__bf16)p1[3]};
+            const bf16x8 pb = cat8(to_bf16x4(f32x4{p0[0], p0[1], p0[2], p0[3]}),
+                                   to_bf16x4(f32x4{p1[0], p1[1], p1[2], p1[3]}));
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
                 const bf16x4 v0 = lds_read_tr4(vw + (2 * tp) * kTileElems + rofs + 16 * dt);
@@ -384,10 +384,10 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
         float pc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            pc[i] = exp2f(sc[i] - mx);
+            pc[i] = fast_exp2(sc[i] - mx);
             lsum += pc[i];
         }
-        const bf16x4 pcb = {(__bf16)pc[0], (__bf16)pc[1], (__bf16)pc[2], (__bf16)pc[3]};
+        const bf16x4 pcb = to_bf16x4(f32x4{pc[0], pc[1], pc[2], pc[3]});
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
             oacc[dt] = mfma_bf16_16(lds_read_tr4(cv + rofs + 16 * dt), pcb, oacc[dt]);
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
         const f32x4 r = oacc[dt] * inv;
-        const bf16x4 rb = {(__bf16)r[0], (__bf16)r[1], (__bf16)r[2], (__bf16)r[3]};
+        const bf16x4 rb = to_bf16x4(f32x4{r[0], r[1], r[2], r[3]});
         *reinterpret_cast<u32x2 *>(orow + 16 * dt) = __builtin_bit_cast(u32x2, rb);
     }
     if (g == 0) lse[(int64_t)h * a.N + ib * kBlock + c16] = (mx + log2f(lsum)) * kLn2;

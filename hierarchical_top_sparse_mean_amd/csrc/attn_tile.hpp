@@ -28,7 +28,7 @@ __device__ __forceinline__ void softmax_pv_chunk(f32x4 (&st)[kFwdTiles], const f
     mx = max4_groups(mx);
     const float mnew = fmaxf(m, mx);
     const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
-    const float alpha = exp2f(m - msafe);
+    const float alpha = fast_exp2(m - msafe);
     m = mnew;
     lsum *= alpha;
 #pragma unroll
@@ -42,12 +42,12 @@ __device__ __forceinline__ void softmax_pv_chunk(f32x4 (&st)[kFwdTiles], const f
             float p0[4], p1[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p0[i] = exp2f(st[t][i] + (kBias ? bias[t][i] : 0.f) - msafe);
-                p1[i] = two ? exp2f(st[t + 1][i] + (kBias ? bias[t + 1][i] : 0.f) - msafe) : 0.f;
+                p0[i] = fast_exp2(st[t][i] + (kBias ? bias[t][i] : 0.f) - msafe);
+                p1[i] = two ? fast_exp2(st[t + 1][i] + (kBias ? bias[t + 1][i] : 0.f) - msafe) : 0.f;
                 lsum += p0[i] + p1[i];
             }
-            const bf16x8 pb = {(__bf16)p0[0], (__bf16)p0[1], (__bf16)p0[2], (__bf16)p0[3],
-                               (__bf16)p1[0], (__bf16)p1[1], (__bf16)p1[2], (__bf16)p1[3]};
+            const bf16x8 pb = cat8(to_bf16x4(f32x4{p0[0], p0[1], p0[2], p0[3]}),
+                                   to_bf16x4(f32x4{p1[0], p1[1], p1[2], p1[3]}));
             const int rofs = (4 * g + (c16 >> 2)) * kVStride + 4 * (c16 & 3);
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {

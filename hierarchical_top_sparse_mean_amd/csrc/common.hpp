@@ -48,8 +48,16 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16 *p) {
 }
 
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
-    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+
+// 2^x on the transcendental unit (v_exp_f32) without the library's range
+// scaling: results below 2^-126 may flush to zero, which only ever concerns
+// softmax weights that are negligible next to the row's largest.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round-to-nearest bf16 of four floats, two per v_cvt_pk_bf16_f32.
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const __bf16 *p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
@@ -59,8 +67,7 @@ __device__ __forceinline__ void store_bf16x8(__bf16 *p, bf16x8 v) {
 }
 
 __device__ __forceinline__ bf16x8 f32_to_bf16x8(f32x4 a, f32x4 b) {
-    return bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
-                  (__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]};
+    return cat8(to_bf16x4(a), to_bf16x4(b));
 }
 
 __device__ __forceinline__ int wave_id() {

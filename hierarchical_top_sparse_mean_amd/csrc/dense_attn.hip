@@ -84,7 +84,7 @@ __global__ __launch_bounds__(512) void dense_fwd_bf16_kernel(const __bf16 *__res
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
         const f32x4 r = oacc[dt] * inv;
-        const bf16x4 rb = {(__bf16)r[0], (__bf16)r[1], (__bf16)r[2], (__bf16)r[3]};
+        const bf16x4 rb = to_bf16x4(f32x4{r[0], r[1], r[2], r[3]});
         *reinterpret_cast<u32x2 *>(orow + 16 * dt) = __builtin_bit_cast(u32x2, rb);
     }
     if (g == 0) lse[(int64_t)h * N + q0 + c16] = (m + log2f(lsum)) * kLn2;

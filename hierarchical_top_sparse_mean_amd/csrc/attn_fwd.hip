@@ -274,6 +274,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
     static_assert(KT % 4 == 0 && KT <= kFwdTiles, "fine tiles are paired within halves");
     constexpr int kHalf = KT / 2;   // V tiles staged at a time (LDS per wave)
     __shared__ __attribute__((aligned(16))) __bf16 vs_all[4][kHalf * kTileElems];
+    __shared__ __attribute__((aligned(16))) __bf16 qs_all[4][kTileElems];
     __shared__ __attribute__((aligned(16))) __bf16 ck[kTileElems];
     __shared__ __attribute__((aligned(16))) __bf16 cv[kTileElems];
     __shared__ float cbias[kBlock];
@@ -290,10 +291,12 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
     const __bf16 *vh = v + head_off;
     __bf16 *vw = vs_all[w];
 
-    // ---- this wave's loads: Q, then every fine K / V tile
-    const __bf16 *qrow = q + head_off + (int64_t)(ib * kBlock + c16) * kHeadDim;
-    const bf16x8 qa0 = load_bf16x8(qrow + 8 * g);
-    const bf16x8 qa1 = load_bf16x8(qrow + 32 + 8 * g);
+    // ---- this wave's loads: Q, then every fine K / V tile, each as whole
+    // 128-byte rows per instruction (lane l: rows l / 8 and l / 8 + 8, 16-byte
+    // chunk l % 8); rows reach the MFMA operand layout through LDS
+    const __bf16 *qb = q + head_off + (int64_t)ib * kBlock * kHeadDim;
+    const bf16x8 qr0 = load_bf16x8(qb + lane * 8);
+    const bf16x8 qr1 = load_bf16x8(qb + (lane + kWave) * 8);
     const int32_t *fine = idx + blk * KT;
     bf16x8 kr[KT][2], vr[KT][2];
 #pragma unroll
@@ -301,11 +304,15 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
         const int f = __builtin_amdgcn_readfirstlane(fine[t]);
         const __bf16 *kt = kh + (int64_t)f * kBlock * kHeadDim;
         const __bf16 *vt = vh + (int64_t)f * kBlock * kHeadDim;
-        kr[t][0] = load_bf16x8(kt + c16 * kHeadDim + 8 * g);
-        kr[t][1] = load_bf16x8(kt + c16 * kHeadDim + 32 + 8 * g);
+        kr[t][0] = load_bf16x8(kt + lane * 8);
+        kr[t][1] = load_bf16x8(kt + (lane + kWave) * 8);
         vr[t][0] = load_bf16x8(vt + lane * 8);
         vr[t][1] = load_bf16x8(vt + (lane + kWave) * 8);
     }
+    auto stage_rows = [&](__bf16 *dst, bf16x8 r0, bf16x8 r1) {
+        store_bf16x8(dst + (lane >> 3) * kVStride + (lane & 7) * 8, r0);
+        store_bf16x8(dst + ((lane >> 3) + 8) * kVStride + (lane & 7) * 8, r1);
+    };
     // ---- coarse tile, staged by the whole workgroup: thread (entry e, quarter p)
     {
         const int e = threadIdx.x >> 4, part = threadIdx.x & 15;   // 16 entries x 16 x 4 columns
@@ -324,11 +331,34 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
         *reinterpret_cast<u32x2 *>(&cv[e * kVStride + 4 * part]) = __builtin_bit_cast(u32x2, vb);
         if (part == 0) cbias[e] = ok ? 4.0f * (float)(js + 2) : -INFINITY;
     }
-    // ---- fine scores (V stays in registers until its half is staged)
-    f32x4 st[KT];
+    // ---- fine scores: K tiles pass through the V staging slots, kHalf at a
+    // time (V stays in registers until its half is staged)
+    __bf16 *qw = qs_all[w];
+    auto stage_k_half = [&](int half) {
 #pragma unroll
-    for (int t = 0; t < KT; ++t)
-        st[t] = mfma_bf16_32(kr[t][1], qa1, mfma_bf16_32(kr[t][0], qa0, f32x4{0.f, 0.f, 0.f, 0.f})) * a.sl2;
+        for (int t = 0; t < kHalf; ++t)
+            stage_rows(vw + t * kTileElems, kr[half * kHalf + t][0], kr[half * kHalf + t][1]);
+    };
+    stage_rows(qw, qr0, qr1);
+    stage_k_half(0);
+    wave_lds_sync();
+    const bf16x8 qa0 = load_bf16x8(qw + c16 * kVStride + 8 * g);
+    const bf16x8 qa1 = load_bf16x8(qw + c16 * kVStride + 32 + 8 * g);
+    f32x4 st[KT];
+    auto score_half = [&](int half) {
+#pragma unroll
+        for (int t = 0; t < kHalf; ++t) {
+            const __bf16 *kro = vw + t * kTileElems + c16 * kVStride + 8 * g;
+            st[half * kHalf + t] =
+                mfma_bf16_32(load_bf16x8(kro + 32), qa1,
+                             mfma_bf16_32(load_bf16x8(kro), qa0, f32x4{0.f, 0.f, 0.f, 0.f})) * a.sl2;
+        }
+    };
+    score_half(0);
+    wave_lds_sync();
+    stage_k_half(1);
+    wave_lds_sync();
+    score_half(1);
     __syncthreads();   // coarse tile staged
     const __bf16 *ckr = ck + c16 * kVStride;
     f32x4 sc = mfma_bf16_32(load_bf16x8(ckr + 32 + 8 * g), qa1,

@@ -140,8 +140,9 @@ int llsa_attn_fwd(const llsa_problem *p, const void *q, const void *k, const voi
  *      so ptr[n_cols] = n_rows * k; csr_col [n_batch, n_rows * k]: the rows
  *      that picked key c, ascending, at csr_col[ptr[c] .. ptr[c+1]).
  * workspace: at least llsa_index_transpose_workspace(...) bytes of device
- *      memory (may be NULL when that is 0).
- * An index outside [0, n_cols) is not detected; its row is then undefined.
+ *      memory (per-range key histograms and a staging copy of csr_col).
+ * An index outside [0, n_cols) is skipped: it is not listed, and ptr[n_cols]
+ * then counts only the listed picks.  The output is deterministic.
  */
 size_t llsa_index_transpose_workspace(int32_t n_batch, int32_t n_rows, int32_t k,
                                       int32_t n_cols);

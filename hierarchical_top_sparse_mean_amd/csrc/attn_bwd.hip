@@ -690,21 +690,48 @@ __global__ __launch_bounds__(256) void bwd_coarse_reduce_kernel(const int32_t *_
         int ent = -1, g0 = 0;
         if (lane < cnt) {
             const int r = C[base + lane];
-            int slot = 0;
-            while (slot < kl && I[(int64_t)r * kl + slot] != c) ++slot;
+            const int32_t *row = I + (int64_t)r * kl;
+            int slot = kl;
+            if (kl == 8) {   // the whole row in two loads (rows are 32-byte aligned)
+                const i32x4 lo = *reinterpret_cast<const i32x4 *>(row);
+                const i32x4 hi = *reinterpret_cast<const i32x4 *>(row + 4);
+#pragma unroll
+                for (int i = 3; i >= 0; --i) {
+                    slot = hi[i] == c ? 4 + i : slot;
+                }
+#pragma unroll
+                for (int i = 3; i >= 0; --i) {
+                    slot = lo[i] == c ? i : slot;
+                }
+            } else {
+                for (int i = kl - 1; i >= 0; --i) slot = row[i] == c ? i : slot;
+            }
             if (slot < kl) {
                 ent = a.cl_entry0[j] + slot;
                 g0 = r * nodes;
             }
         }
-        for (int jj = 0; jj < cnt; ++jj) {
-            const int e = __builtin_amdgcn_readlane(ent, jj);
-            if (e < 0) continue;   // not a pick of that row: inconsistent lists, skip
-            const int64_t G0 = (int64_t)h * a.n2 + __builtin_amdgcn_readlane(g0, jj);
+        // eight rows at a time: all their partial rows are requested before
+        // any is added (an entry that is not a pick of its row, which only
+        // inconsistent lists produce, contributes nothing)
+        for (int j0 = 0; j0 < cnt; j0 += 8) {
             for (int s = 0; s < nodes; ++s) {
-                const float *pp = ws.partial + ((G0 + s) * a.ncoarse + e) * 2 * kHeadDim;
-                sk += pp[lane];
-                sv += pp[kHeadDim + lane];
+                float pk8[8], pv8[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int jj = min(j0 + u, cnt - 1);
+                    const int e = __builtin_amdgcn_readlane(ent, jj);
+                    const int64_t G0 = (int64_t)h * a.n2 + __builtin_amdgcn_readlane(g0, jj);
+                    const float *pp = ws.partial + ((G0 + s) * a.ncoarse + max(e, 0)) * 2 * kHeadDim;
+                    const bool use = j0 + u < cnt && e >= 0;
+                    pk8[u] = use ? pp[lane] : 0.f;
+                    pv8[u] = use ? pp[kHeadDim + lane] : 0.f;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    sk += pk8[u];
+                    sv += pv8[u];
+                }
             }
         }
     }

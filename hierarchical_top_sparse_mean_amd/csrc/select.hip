@@ -90,14 +90,21 @@ constexpr int kSelTilesPerChunk = 8;
 // parent == nullptr: coarsest level, candidates 0..n-1, row groups are
 // 16-row slices.  Otherwise: row group p = the 16 children of parent p,
 // candidates = children of parent[p][0..kp).
-template <int KM>
+// SPLIT = 4: the four waves of a workgroup share one row group and take a
+// quarter of its candidate tiles each (the coarsest level has few groups);
+// their lists are merged through LDS at the end.
+template <int KM, int SPLIT>
 __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ ql,
                                                      const float *__restrict__ kl,
                                                      const int32_t *__restrict__ parent,
                                                      int32_t *__restrict__ out, int n, int kout,
                                                      int kp, int groups_per_head,
                                                      int64_t groups_total) {
-    const int64_t gid = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + wave_id();
+    static_assert(SPLIT == 1 || SPLIT == 4, "a row group takes one wave or the whole workgroup");
+    __shared__ uint64_t part_best[SPLIT == 1 ? 1 : SPLIT][kBlock][KM];
+    const int part = SPLIT == 1 ? 0 : wave_id();
+    const int64_t gid = SPLIT == 1 ? (int64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + wave_id()
+                                   : (int64_t)xcd_remap(blockIdx.x, gridDim.x);
     if (gid >= groups_total) return;
     const int h = (int)(gid / groups_per_head);
     const int gi = (int)(gid % groups_per_head);
@@ -130,7 +137,8 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ q
 #pragma unroll
     for (int i = 0; i < KM; ++i) best[i] = 0;
 
-    for (int t0 = 0; t0 < ntiles; t0 += kSelTilesPerChunk) {
+    const int tb = part * ntiles / SPLIT, te = (part + 1) * ntiles / SPLIT;
+    for (int t0 = tb; t0 < te; t0 += kSelTilesPerChunk) {
         uint64_t keys[4 * kSelTilesPerChunk];
         // every tile's rows are requested before the first is used; tiles past
         // the end re-read the last tile and are masked out
@@ -138,7 +146,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ q
         int base[kSelTilesPerChunk];
 #pragma unroll
         for (int t = 0; t < kSelTilesPerChunk; ++t) {
-            const int tile = min(t0 + t, ntiles - 1);
+            const int tile = min(t0 + t, te - 1);
             base[t] = dense ? tile * kBlock : __builtin_amdgcn_readfirstlane(prow[tile]) * kBlock;
             const int cand = base[t] + col;
             const int64_t crow = cand < n ? cand : 0;
@@ -157,7 +165,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ q
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 16; ++s) acc = mfma_f32_4(kf[t][s], qf[s], acc);
-            const bool live = t0 + t < ntiles;
+            const bool live = t0 + t < te;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int c = base[t] + 4 * g + i;
@@ -174,16 +182,31 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ q
         }
     }
     // the 4 lanes holding one query merge their lists
+    auto merge_lanes = [&]() {
 #pragma unroll
-    for (int m = 16; m <= 32; m <<= 1) {
-        uint64_t other[KM];
+        for (int m = 16; m <= 32; m <<= 1) {
+            uint64_t other[KM];
 #pragma unroll
-        for (int i = 0; i < KM; ++i) {
-            const uint32_t lo = shfl_xor_u((uint32_t)best[i], m);
-            const uint32_t hi = shfl_xor_u((uint32_t)(best[i] >> 32), m);
-            other[i] = ((uint64_t)hi << 32) | lo;
+            for (int i = 0; i < KM; ++i) {
+                const uint32_t lo = shfl_xor_u((uint32_t)best[i], m);
+                const uint32_t hi = shfl_xor_u((uint32_t)(best[i] >> 32), m);
+                other[i] = ((uint64_t)hi << 32) | lo;
+            }
+            merge_top<KM>(best, other);
         }
-        merge_top<KM>(best, other);
+    };
+    merge_lanes();
+    if constexpr (SPLIT > 1) {
+        // part w's list of query c16 -> LDS; wave 0 merges lane group g = part g
+        if (g == 0) {
+#pragma unroll
+            for (int i = 0; i < KM; ++i) part_best[part][col][i] = best[i];
+        }
+        __syncthreads();
+        if (part != 0) return;
+#pragma unroll
+        for (int i = 0; i < KM; ++i) best[i] = part_best[g][col][i];
+        merge_lanes();
     }
     uint32_t sel[KM];
 #pragma unroll
@@ -197,24 +220,35 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ q
     }
 }
 
+template <int KM>
+static void launch_level(const Geometry &g, int l, const float *pq, const float *pk, int32_t *idx,
+                         hipStream_t s) {
+    const bool dense = (l == g.L);
+    const int n = g.n[l];
+    const int gph = dense ? (n + kBlock - 1) / kBlock : n / kBlock;
+    const int64_t total = (int64_t)g.bh * gph;
+    const int32_t *parent = dense ? nullptr : idx + g.idx_off[l + 1];
+    const int kp = dense ? 0 : g.kl[l + 1];
+    const int ntiles = dense ? gph : kp;
+    // split a row group over the workgroup when groups are too few to fill
+    // the chip and each has tiles enough for four waves
+    if (total < 1024 && ntiles >= 4 * 2)
+        hipLaunchKernelGGL((select_kernel<KM, 4>), dim3((unsigned)total), dim3(256), 0, s,
+                           pq + g.pyr_off[l], pk + g.pyr_off[l], parent, idx + g.idx_off[l], n,
+                           g.kl[l], kp, gph, total);
+    else
+        hipLaunchKernelGGL((select_kernel<KM, 1>), dim3((unsigned)((total + 3) / 4)), dim3(256), 0,
+                           s, pq + g.pyr_off[l], pk + g.pyr_off[l], parent, idx + g.idx_off[l], n,
+                           g.kl[l], kp, gph, total);
+}
+
 hipError_t launch_select(const Geometry &g, const float *pq, const float *pk, int32_t *idx,
                          hipStream_t s) {
     for (int l = g.L; l >= 1; --l) {
-        const bool dense = (l == g.L);
-        const int n = g.n[l];
-        const int gph = dense ? (n + kBlock - 1) / kBlock : n / kBlock;
-        const int64_t total = (int64_t)g.bh * gph;
-        const int32_t *parent = dense ? nullptr : idx + g.idx_off[l + 1];
-        const int kp = dense ? 0 : g.kl[l + 1];
-        const dim3 grid((unsigned)((total + 3) / 4));
         if (g.K <= 8)
-            hipLaunchKernelGGL(select_kernel<8>, grid, dim3(256), 0, s, pq + g.pyr_off[l],
-                               pk + g.pyr_off[l], parent, idx + g.idx_off[l], n, g.kl[l], kp, gph,
-                               total);
+            launch_level<8>(g, l, pq, pk, idx, s);
         else
-            hipLaunchKernelGGL(select_kernel<16>, grid, dim3(256), 0, s, pq + g.pyr_off[l],
-                               pk + g.pyr_off[l], parent, idx + g.idx_off[l], n, g.kl[l], kp, gph,
-                               total);
+            launch_level<16>(g, l, pq, pk, idx, s);
     }
     return hipGetLastError();
 }

@@ -235,6 +235,25 @@ def main():
                  "bf16_mfma_frac": round(dflops / dms / 1e9 / BF16_PEAK_TFLOPS, 4),
                  "llsa_fwd_ms": round(llsa_fwd, 4),
                  "speedup_fwd": round(dms / llsa_fwd, 2)}
+        if w.backward:
+            # dense backward (dQ pass, then dK/dV pass); float32 gradients like the sparse path
+            gq, gk, gv = (torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+            wsb = L.llsa_dense_attn_bwd_workspace(p)
+            wsd = torch.empty(wsb, dtype=torch.uint8, device=dev)
+            L.llsa_dense_attn_bwd(p, q, k, v, o_d, lse_d, dout, gq, gk, gv, wsd, wsb)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                L.llsa_dense_attn_bwd(p, q, k, v, o_d, lse_d, dout, gq, gk, gv, wsd, wsb)
+            e1.record()
+            torch.cuda.synchronize()
+            bms = e0.elapsed_time(e1) / reps
+            dense.update({"bwd_ms": round(bms, 3),
+                          "bwd_TFLOP/s": round(2.5 * dflops / bms / 1e9, 1),
+                          "fwd_bwd_ms": round(dms + bms, 3),
+                          "llsa_fwd_bwd_ms": round(ms_per_step, 4),
+                          "speedup_fwd_bwd": round((dms + bms) / ms_per_step, 2)})
+            del gq, gk, gv, wsd
         del o_d, lse_d
 
     cpu = None

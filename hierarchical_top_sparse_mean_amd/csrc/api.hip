@@ -202,6 +202,30 @@ int llsa_dense_attn_fwd(const llsa_problem *p, const void *q, const void *k, con
     return status_of(llsa::launch_dense_fwd((int)bh, p->seq_len, scale, q, k, v, o, lse, (hipStream_t)stream));
 }
 
+int llsa_dense_attn_bwd(const llsa_problem *p, const void *q, const void *k, const void *v,
+                        const void *o, const float *lse, const void *dout, float *dq, float *dk,
+                        float *dv, void *workspace, size_t workspace_bytes, void *stream) {
+    if (p == nullptr) return LLSA_ERR_INVALID;
+    if (p->batch <= 0 || p->heads <= 0 || p->seq_len <= 0 || p->head_dim <= 0) return LLSA_ERR_INVALID;
+    if (!(p->scale >= 0.0f) || isinf(p->scale)) return LLSA_ERR_INVALID;
+    if (p->head_dim != 64 || p->dtype != LLSA_BF16 || p->seq_len % 16 != 0) return LLSA_ERR_UNSUPPORTED;
+    const int64_t bh = (int64_t)p->batch * p->heads;
+    if (bh * p->seq_len >= ((int64_t)1 << 31)) return LLSA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+        !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return LLSA_ERR_INVALID;
+    if (workspace == nullptr || workspace_bytes < llsa_dense_attn_bwd_workspace(p))
+        return LLSA_ERR_WORKSPACE;
+    const float scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
+    return status_of(llsa::launch_dense_bwd((int)bh, p->seq_len, scale, q, k, v, o, lse, dout, dq,
+                                            dk, dv, (float *)workspace, (hipStream_t)stream));
+}
+
+size_t llsa_dense_attn_bwd_workspace(const llsa_problem *p) {
+    if (p == nullptr || p->batch <= 0 || p->heads <= 0 || p->seq_len <= 0) return 0;
+    return sizeof(float) * (size_t)p->batch * p->heads * p->seq_len;
+}
+
 const char *llsa_strerror(int status) {
     switch (status) {
     case LLSA_OK: return "ok";

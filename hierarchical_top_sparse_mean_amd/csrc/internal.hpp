@@ -44,5 +44,8 @@ hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, cons
                            void *ws, hipStream_t s);
 hipError_t launch_dense_fwd(int bh, int N, float scale, const void *q, const void *k,
                             const void *v, void *o, float *lse, hipStream_t s);
+hipError_t launch_dense_bwd(int bh, int N, float scale, const void *q, const void *k,
+                            const void *v, const void *o, const float *lse, const void *dout,
+                            float *dq, float *dk, float *dv, float *Dws, hipStream_t s);
 
 }  // namespace llsa

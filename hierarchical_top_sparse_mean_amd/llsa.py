@@ -60,10 +60,15 @@ def _load():
     L.llsa_attn_bwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, _c_sz, _vp]
     L.llsa_dense_attn_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.llsa_dense_attn_bwd_workspace.argtypes = [P]
+    L.llsa_dense_attn_bwd_workspace.restype = _c_sz
+    L.llsa_dense_attn_bwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz,
+                                      _vp]
     L.llsa_strerror.argtypes = [ctypes.c_int]
     L.llsa_strerror.restype = ctypes.c_char_p
     for name in ("llsa_sizes_query", "llsa_pool", "llsa_select", "llsa_attn_fwd",
-                 "llsa_index_transpose", "llsa_attn_bwd", "llsa_dense_attn_fwd"):
+                 "llsa_index_transpose", "llsa_attn_bwd", "llsa_dense_attn_fwd",
+                 "llsa_dense_attn_bwd"):
         getattr(L, name).restype = ctypes.c_int
     return L
 
@@ -143,6 +148,18 @@ def llsa_attn_bwd(p, q, k, v, pyr_k, pyr_v, idx, csr_ptr, csr_col, o, lse, dout,
 def llsa_dense_attn_fwd(p, q, k, v, o, lse, stream=None):
     _check("llsa_dense_attn_fwd", lib.llsa_dense_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
                                                           _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def llsa_dense_attn_bwd_workspace(p) -> int:
+    return int(lib.llsa_dense_attn_bwd_workspace(ctypes.byref(p)))
+
+
+def llsa_dense_attn_bwd(p, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
+                        stream=None):
+    _check("llsa_dense_attn_bwd",
+           lib.llsa_dense_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                   _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                   workspace_bytes, _stream(stream)))
 
 
 # --------------------------------------------------------------- buffers --

@@ -181,6 +181,21 @@ int llsa_attn_bwd(const llsa_problem *p, const void *q, const void *k, const voi
 int llsa_dense_attn_fwd(const llsa_problem *p, const void *q, const void *k, const void *v,
                         void *o, float *lse, void *stream);
 
+/*
+ * Dense backward comparator of llsa_dense_attn_fwd for the loss <O, dO>: a
+ * query-major pass computes D = rowsum(dO * O) and dQ, a key-major pass dK
+ * and dV, over all keys (no sparsity).  Same supported set as the forward.
+ * In : q, k, v, o, dout [batch, heads, seq_len, 64] bf16; lse from
+ *      llsa_dense_attn_fwd.
+ * Out: dq, dk, dv float32 [batch, heads, seq_len, 64].
+ * workspace: at least llsa_dense_attn_bwd_workspace(p) bytes (D, float32
+ *      per query).
+ */
+size_t llsa_dense_attn_bwd_workspace(const llsa_problem *p);
+int llsa_dense_attn_bwd(const llsa_problem *p, const void *q, const void *k, const void *v,
+                        const void *o, const float *lse, const void *dout, float *dq, float *dk,
+                        float *dv, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static string). */
 const char *llsa_strerror(int status);
 

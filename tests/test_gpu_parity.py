@@ -171,3 +171,36 @@ def test_dense_comparator_matches_oracle_dense():
     want_lse = (m[..., 0] + np.log(pr.sum(-1)))
     assert np.abs(o.float().cpu().numpy().reshape(2, N, 64) - want).max() <= 2e-2
     assert np.abs(lse.cpu().numpy().reshape(2, N) - want_lse).max() <= 2e-2
+
+
+@pytest.mark.parametrize("N", [1024, 1040])
+def test_dense_backward_comparator_matches_textbook_gradients(N):
+    # the dense backward comparator against the textbook softmax-attention
+    # gradients of <O, dO> in float64 (1040 tokens: a partial last tile step)
+    _log(f"[parity] dense backward comparator N={N}")
+    from hierarchical_top_sparse_mean_amd.inputs import make_inputs
+    q, k, v, do = make_inputs(1, 2, N, 64, torch.bfloat16, N == 1024, True, 3)
+    p = L.problem(1, 2, N, dtype=torch.bfloat16)
+    dev = [x.cuda() for x in (q, k, v, do)]
+    o = torch.empty(1, 2, N, 64, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(2 * N, dtype=torch.float32, device="cuda")
+    L.llsa_dense_attn_fwd(p, dev[0], dev[1], dev[2], o, lse)
+    grads = [torch.empty(1, 2, N, 64, dtype=torch.float32, device="cuda") for _ in range(3)]
+    ws_bytes = L.llsa_dense_attn_bwd_workspace(p)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    L.llsa_dense_attn_bwd(p, dev[0], dev[1], dev[2], o, lse, dev[3], *grads, ws, ws_bytes)
+    torch.cuda.synchronize()
+    Q, K, V, dO = (x.double().numpy().reshape(2, N, 64) for x in (q, k, v, do))
+    s = np.einsum("hqd,hkd->hqk", Q, K) / 8.0
+    pr = np.exp(s - s.max(-1, keepdims=True))
+    pr /= pr.sum(-1, keepdims=True)
+    O = np.einsum("hqk,hkd->hqd", pr, V)
+    dP = np.einsum("hqd,hkd->hqk", dO, V)
+    dS = pr * (dP - (dO * O).sum(-1, keepdims=True))
+    want = {"dq": np.einsum("hqk,hkd->hqd", dS, K) / 8.0,
+            "dk": np.einsum("hqk,hqd->hkd", dS, Q) / 8.0,
+            "dv": np.einsum("hqk,hqd->hkd", pr, dO)}
+    for name, got in zip(("dq", "dk", "dv"), grads):
+        err = np.abs(got.cpu().numpy().reshape(2, N, 64) - want[name]).max()
+        _log(f"[parity]   {name} max abs err {err:.3g}")
+        assert err <= 2e-2, name

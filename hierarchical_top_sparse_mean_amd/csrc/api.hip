@@ -41,7 +41,7 @@ int make_geometry(const llsa_problem *p, Geometry *g, llsa_sizes *sz) {
     const int Le = p->enrich < 0 ? L - 1 : p->enrich;
     if (p->enrich < -1 || Le > L - 1) return LLSA_ERR_INVALID;
     if (p->head_dim != 64 || p->block != 16) return LLSA_ERR_UNSUPPORTED;
-    if (p->topk > 16) return LLSA_ERR_UNSUPPORTED;
+    if (p->topk > 32) return LLSA_ERR_UNSUPPORTED;
     const int64_t bh = (int64_t)p->batch * p->heads;
     if (bh * p->seq_len * p->head_dim >= ((int64_t)1 << 40) || bh * p->seq_len >= ((int64_t)1 << 31) ||
         bh > (1 << 30))

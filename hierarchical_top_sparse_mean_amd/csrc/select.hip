@@ -138,38 +138,43 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ q
     for (int i = 0; i < KM; ++i) best[i] = 0;
 
     const int tb = part * ntiles / SPLIT, te = (part + 1) * ntiles / SPLIT;
+    // candidate tiles are read LB at a time (all of a batch before the first
+    // is used); KM = 32 halves the batch to stay within the register budget
+    constexpr int LB = KM > 16 ? kSelTilesPerChunk / 2 : kSelTilesPerChunk;
     for (int t0 = tb; t0 < te; t0 += kSelTilesPerChunk) {
         uint64_t keys[4 * kSelTilesPerChunk];
-        // every tile's rows are requested before the first is used; tiles past
-        // the end re-read the last tile and are masked out
-        float kf[kSelTilesPerChunk][16];
-        int base[kSelTilesPerChunk];
 #pragma unroll
-        for (int t = 0; t < kSelTilesPerChunk; ++t) {
-            const int tile = min(t0 + t, te - 1);
-            base[t] = dense ? tile * kBlock : __builtin_amdgcn_readfirstlane(prow[tile]) * kBlock;
-            const int cand = base[t] + col;
-            const int64_t crow = cand < n ? cand : 0;
-            const f32x4 *src = reinterpret_cast<const f32x4 *>(kh + crow * kHeadDim + 16 * g);
+        for (int hb = 0; hb < kSelTilesPerChunk; hb += LB) {
+            // tiles past the end re-read the last tile and are masked out
+            float kf[LB][16];
+            int base[LB];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f32x4 tt = src[j];
-                kf[t][4 * j] = tt[0];
-                kf[t][4 * j + 1] = tt[1];
-                kf[t][4 * j + 2] = tt[2];
-                kf[t][4 * j + 3] = tt[3];
+            for (int t = 0; t < LB; ++t) {
+                const int tile = min(t0 + hb + t, te - 1);
+                base[t] = dense ? tile * kBlock : __builtin_amdgcn_readfirstlane(prow[tile]) * kBlock;
+                const int cand = base[t] + col;
+                const int64_t crow = cand < n ? cand : 0;
+                const f32x4 *src = reinterpret_cast<const f32x4 *>(kh + crow * kHeadDim + 16 * g);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 tt = src[j];
+                    kf[t][4 * j] = tt[0];
+                    kf[t][4 * j + 1] = tt[1];
+                    kf[t][4 * j + 2] = tt[2];
+                    kf[t][4 * j + 3] = tt[3];
+                }
             }
-        }
 #pragma unroll
-        for (int t = 0; t < kSelTilesPerChunk; ++t) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < LB; ++t) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 16; ++s) acc = mfma_f32_4(kf[t][s], qf[s], acc);
-            const bool live = t0 + t < te;
+                for (int s = 0; s < 16; ++s) acc = mfma_f32_4(kf[t][s], qf[s], acc);
+                const bool live = t0 + hb + t < te;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int c = base[t] + 4 * g + i;
-                keys[4 * t + i] = (live && c < n) ? score_key(acc[i], (uint32_t)c) : 0ull;
+                for (int i = 0; i < 4; ++i) {
+                    const int c = base[t] + 4 * g + i;
+                    keys[4 * (hb + t) + i] = (live && c < n) ? score_key(acc[i], (uint32_t)c) : 0ull;
+                }
             }
         }
 #pragma unroll
@@ -247,8 +252,10 @@ hipError_t launch_select(const Geometry &g, const float *pq, const float *pk, in
     for (int l = g.L; l >= 1; --l) {
         if (g.K <= 8)
             launch_level<8>(g, l, pq, pk, idx, s);
-        else
+        else if (g.K <= 16)
             launch_level<16>(g, l, pq, pk, idx, s);
+        else
+            launch_level<32>(g, l, pq, pk, idx, s);
     }
     return hipGetLastError();
 }

@@ -29,7 +29,7 @@
  *    call; on an error status nothing is launched and no output is touched.
  *    Launch failures are reported as LLSA_ERR_HIP.
  *  - Supported set: head_dim = 64, block = 16, 1 <= levels <= 6,
- *    1 <= topk <= 16, dtype LLSA_F32 or LLSA_BF16, non-causal.  Other values
+ *    1 <= topk <= 32, dtype LLSA_F32 or LLSA_BF16, non-causal.  Other values
  *    give LLSA_ERR_UNSUPPORTED.
  */
 #ifndef LLSA_H

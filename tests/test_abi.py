@@ -70,7 +70,7 @@ def test_picks_clamped_to_candidates():
     (dict(scale=-1.0), L.LLSA_ERR_INVALID),
     (dict(head_dim=128), L.LLSA_ERR_UNSUPPORTED),
     (dict(block=32, seq_len=32 * 32 * 4), L.LLSA_ERR_UNSUPPORTED),
-    (dict(topk=17), L.LLSA_ERR_UNSUPPORTED),
+    (dict(topk=33), L.LLSA_ERR_UNSUPPORTED),
     (dict(levels=7, seq_len=16 ** 5), L.LLSA_ERR_UNSUPPORTED),
 ])
 def test_sizes_query_rejects(kw, status):

@@ -51,7 +51,11 @@ EDGE = [
     (1, 2, 8192, torch.float32, 3, 2, 2, True, {}),
     (1, 2, 4096, torch.bfloat16, 2, 8, 0, True, {}),       # no enrichment
     (1, 2, 4096, torch.bfloat16, 2, 1, 1, True, {}),       # K = 1
-    (1, 2, 4096, torch.bfloat16, 2, 16, 1, True, {}),      # K = 16 (largest supported)
+    (1, 2, 4096, torch.bfloat16, 2, 16, 1, True, {}),      # K = 16
+    (1, 2, 4096, torch.bfloat16, 1, 20, 0, True, {}),      # single level, K = 20
+    (1, 2, 4096, torch.bfloat16, 1, 32, 0, True, {}),      # single level, K = 32 (largest)
+    (1, 2, 4096, torch.bfloat16, 2, 32, 1, True, {}),      # K = 32 with enrichment (2 coarse tiles)
+    (1, 1, 2048, torch.float32, 2, 24, 1, True, {}),
     (1, 2, 4096, torch.bfloat16, 2, 3, 1, True, {"drop_covered": False}),
     (2, 2, 2048, torch.bfloat16, 2, 4, 1, True, {"grad_dtype": torch.bfloat16}),
     (1, 1, 256, torch.bfloat16, 2, 16, 1, True, {}),       # K = all blocks (dense reduction)

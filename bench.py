@@ -101,46 +101,18 @@ def cpu_baseline(w, max_heads):
                       f"pool+select+fwd+transpose+bwd in fp64 ({dt:.1f} s)"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="n65536_bf16")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=16)
-    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
-                    help="only run a plain device-to-device copy of MIB MiB (HBM counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the operator shards by (batch, head) with no "
-              "communication, and this build runs on a single MI355X; use --gpus 1.",
-              file=sys.stderr)
-        sys.exit(2)
-
+def time_workload(L, w, steps, warmup, dev, grad_bf16=False):
+    """Runs `warmup` untimed and `steps` timed steps of the whole path on
+    workload `w` (inputs resident on the GPU); returns the inputs, problem,
+    buffers, sizes, the mean per-call milliseconds (HIP events on the current
+    stream) and the wall-clock milliseconds per step."""
     import torch
-    from hierarchical_top_sparse_mean_amd import llsa as L
-    from hierarchical_top_sparse_mean_amd.inputs import WORKLOADS, workload_inputs
-
-    w = WORKLOADS[args.workload]
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda", 0)
-    if args.copy_probe:
-        n = args.copy_probe * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
-                          "launches": 3}))
-        return
+    from hierarchical_top_sparse_mean_amd.inputs import workload_inputs
     q, k, v, dout = workload_inputs(w)
     q, k, v = q.to(dev), k.to(dev), v.to(dev)
     dout = dout.to(dev) if dout is not None else None
     p = L.problem(w.batch, w.heads, w.seq_len, w.head_dim, w.block, w.levels, w.topk, w.enrich,
-                  w.dtype, torch.float32)
+                  w.dtype, torch.bfloat16 if grad_bf16 else torch.float32)
     B = L.Buffers(p, backward=w.backward)
     s = B.s
     bh = w.bh
@@ -167,20 +139,101 @@ def main():
                             dout, B.dq, B.dk, B.dv, B.ws, B.ws.numel())
             mark(5)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     nev = len(calls) + 1
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    per_call = {c: sum(events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)) / args.steps
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    per_call = {c: sum(events[i][j].elapsed_time(events[i][j + 1]) for i in range(steps)) / steps
                 for j, c in enumerate(calls)}
+    return q, k, v, dout, p, B, s, per_call, ms_per_step
+
+
+def sweep_workloads():
+    """The workload table plus the variations the scaling study asks for, all
+    at the 65536-token shape unless named otherwise: more pooling steps,
+    no enrichment, wider selection, single-level selection (quadratic in the
+    number of blocks) and bfloat16 gradients."""
+    from dataclasses import replace
+    from hierarchical_top_sparse_mean_amd.inputs import WORKLOADS
+    base = WORKLOADS["n65536_bf16"]
+    out = [(w, False) for w in WORKLOADS.values()]
+    out += [
+        (replace(base, name="n65536_L3_Le2", levels=3, enrich=2), False),
+        (replace(base, name="n65536_Le0", enrich=0), False),
+        (replace(base, name="n65536_K16", topk=16), False),
+        (replace(base, name="n65536_L1_K8", levels=1, enrich=0), False),
+        (replace(base, name="n65536_L1_K20", levels=1, topk=20, enrich=0), False),
+        (replace(base, name="n65536_L1_K32", levels=1, topk=32, enrich=0), False),
+        (base, True),   # bfloat16 gradients
+    ]
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="n65536_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every workload and variation (one JSON line each) instead of the bench line")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the operator shards by (batch, head) with no "
+              "communication, and this build runs on a single MI355X; use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from hierarchical_top_sparse_mean_amd import llsa as L
+    from hierarchical_top_sparse_mean_amd.inputs import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    if args.sweep:
+        for sw, gbf in sweep_workloads():
+            _, _, _, _, _, _, ss, pc, msps = time_workload(L, sw, args.steps, args.warmup, dev, gbf)
+            alg, nkv = algorithmic(sw, ss)
+            tok = sw.batch * sw.seq_len
+            rec = {"sweep": sw.name + ("_gradbf16" if gbf else ""), "describe": sw.describe(),
+                   "keys_per_query_block": nkv, "ms_per_step": round(msps, 4),
+                   "tokens_per_s": round(tok / (msps / 1e3), 1),
+                   # per token and head: selection + attention forward, the part whose
+                   # cost the method makes log-linear in N
+                   "ns_per_token_head_select_attn":
+                       round((pc["select"] + pc["attn_fwd"]) * 1e6 / (tok * sw.heads), 4),
+                   "calls": {c: {"ms": round(v, 4), "GB/s": round(alg[c]["bytes"] / v / 1e6, 1)}
+                             for c, v in pc.items()}}
+            print(json.dumps(rec), flush=True)
+            torch.cuda.empty_cache()
+        return
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                          "launches": 3}))
+        return
+    q, k, v, dout, p, B, s, per_call, ms_per_step = time_workload(L, w, args.steps, args.warmup, dev)
+    bh = w.bh
+    calls = list(per_call)
     tokens = w.batch * w.seq_len
     value = tokens / (ms_per_step / 1e3)
 

@@ -874,81 +874,88 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
 }
 
 // ================================================================ f32 path
-// Pass A (f32): one thread per query.
+// Float32 inputs (the small exact-parity configurations): one wave per token,
+// lane = dimension; every dot product is a butterfly sum across the wave, and
+// keys are visited in a fixed order, so the results are reproducible.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m, kWave);
+    return x;
+}
+
+// Pass A (f32): one wave per query token.
 __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ pk, const float *__restrict__ pv, const int32_t *__restrict__ idx,
     const float *__restrict__ o, const float *__restrict__ lse, const float *__restrict__ dout,
     void *__restrict__ dq, BwdWs ws, BwdArgs a) {
-    const int64_t tq = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t tq = (int64_t)blockIdx.x * 4 + wave_id();
     if (tq >= (int64_t)a.bh * a.N) return;
+    const int lane = lane_id();
     const int h = (int)(tq / a.N);
     const int tok = (int)(tq % a.N);
     const int ib = tok / kBlock;
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
-    const float *qv = q + head_off + (int64_t)tok * kHeadDim;
-    const float *gv = dout + head_off + (int64_t)tok * kHeadDim;
-    const float *ov = o + head_off + (int64_t)tok * kHeadDim;
-    float D = 0.f;
-    for (int e = 0; e < kHeadDim; ++e) D = fmaf(gv[e], ov[e], D);
-    ws.D[tq] = D;
+    const int64_t row = head_off + (int64_t)tok * kHeadDim + lane;
+    const float qx = q[row], gx = dout[row];
+    const float D = wave_sum(gx * o[row]);
+    if (lane == 0) ws.D[tq] = D;
     const float lse2 = lse[tq] * kLog2e;
-    float acc[kHeadDim];
-#pragma unroll
-    for (int e = 0; e < kHeadDim; ++e) acc[e] = 0.f;
-    auto visit = [&](const float *kr, const float *vr, float bias) {
-        float s = 0.f, dp = 0.f;
-        for (int e = 0; e < kHeadDim; ++e) {
-            s = fmaf(qv[e], kr[e], s);
-            dp = fmaf(gv[e], vr[e], dp);
-        }
+    float acc = 0.f;
+    auto visit = [&](float kx, float vx, float bias) {
+        const float s = wave_sum(qx * kx);
+        const float dp = wave_sum(gx * vx);
         const float p = exp2f(s * a.sl2 + bias - lse2);
-        const float ds = p * (dp - D);
-#pragma unroll
-        for (int e = 0; e < kHeadDim; ++e) acc[e] = fmaf(ds, kr[e], acc[e]);
+        acc = fmaf(p * (dp - D), kx, acc);
     };
     const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
-    for (int j = 0; j < a.K1; ++j)
+    for (int j = 0; j < a.K1; ++j) {
+        const int64_t u0 = (int64_t)__builtin_amdgcn_readfirstlane(fine[j]) * kBlock;
+        float kx[kBlock], vx[kBlock];
+#pragma unroll
         for (int t = 0; t < kBlock; ++t) {
-            const int64_t u = (int64_t)fine[j] * kBlock + t;
-            visit(k + head_off + u * kHeadDim, v + head_off + u * kHeadDim, 0.f);
+            kx[t] = k[head_off + (u0 + t) * kHeadDim + lane];
+            vx[t] = v[head_off + (u0 + t) * kHeadDim + lane];
         }
+#pragma unroll
+        for (int t = 0; t < kBlock; ++t) visit(kx[t], vx[t], 0.f);
+    }
     for (int e = 0; e < a.ncoarse; ++e) {
         int jl, c;
         float b;
         if (bwd_coarse_entry(a, idx, fine, h, ib, e, jl, c, b)) {
-            const int64_t roff = a.cl_pyr_off[jl] + ((int64_t)h * a.cl_n[jl] + c) * kHeadDim;
-            visit(pk + roff, pv + roff, b);
+            const int64_t roff = a.cl_pyr_off[jl] + ((int64_t)h * a.cl_n[jl] + c) * kHeadDim + lane;
+            visit(pk[roff], pv[roff], b);
         }
     }
-    for (int e = 0; e < kHeadDim; ++e) store_grad1(dq, head_off + (int64_t)tok * kHeadDim + e, acc[e] * a.scale, a.grad_bf16);
+    store_grad1(dq, row, acc * a.scale, a.grad_bf16);
 }
 
-// Pooled-token gradients (f32): one thread per (level, pooled token); walks
-// the CSR of I^(l) and every query block under each row that picked it.
-__global__ __launch_bounds__(64) void bwd_coarse_f32_kernel(
+// Pooled-token gradients (f32): one wave per (level, pooled token).  The wave
+// walks the CSR of I^(l) and every query block under each row that picked the
+// token, a block's 16 query rows at a time.
+
+__global__ __launch_bounds__(256) void bwd_coarse_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ pk, const float *__restrict__ pv,
     const int32_t *__restrict__ idx, const float *__restrict__ lse, const float *__restrict__ dout,
     const int32_t *__restrict__ csr_ptr, const int32_t *__restrict__ csr_col, BwdWs ws, BwdArgs a,
     int j) {
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave_id();
     const int nl = a.cl_n[j], kl = a.cl_k[j], span = a.cl_span[j];
     if (t >= (int64_t)a.bh * nl) return;
+    const int lane = lane_id();
     const int h = (int)(t / nl);
     const int c = (int)(t % nl);
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
     const int64_t roff = a.cl_pyr_off[j] + ((int64_t)h * nl + c) * kHeadDim;
-    const float *kr = pk + roff, *vr = pv + roff;
+    const float kx = pk[roff + lane], vx = pv[roff + lane];
     const float bias = 4.0f * (float)(j + 2);
-    float gk[kHeadDim], gvv[kHeadDim];
-    for (int e = 0; e < kHeadDim; ++e) {
-        gk[e] = 0.f;
-        gvv[e] = 0.f;
-    }
+    float gk = 0.f, gv = 0.f;
     const int32_t *P = csr_ptr + a.cl_ptr_off[j] + (int64_t)h * (nl + 1);
     const int32_t *C = csr_col + a.cl_col_off[j] + (int64_t)h * nl * kl;
-    for (int e = P[c]; e < P[c + 1]; ++e) {
-        const int r = C[e];
+    const int e0 = __builtin_amdgcn_readfirstlane(P[c]), e1 = __builtin_amdgcn_readfirstlane(P[c + 1]);
+    for (int e = e0; e < e1; ++e) {
+        const int r = __builtin_amdgcn_readfirstlane(C[e]);
         for (int ib = r * span; ib < (r + 1) * span; ++ib) {
             const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
             if (a.drop && a.K1 >= span) {
@@ -956,85 +963,78 @@ __global__ __launch_bounds__(64) void bwd_coarse_f32_kernel(
                 for (int ff = 0; ff < a.K1; ++ff) cov += (fine[ff] / span == c) ? 1 : 0;
                 if (cov == span) continue;
             }
+            float qx[kBlock], gx[kBlock];
+#pragma unroll
             for (int tt = 0; tt < kBlock; ++tt) {
                 const int64_t tok = (int64_t)ib * kBlock + tt;
-                const float *qv = q + head_off + tok * kHeadDim;
-                const float *gv = dout + head_off + tok * kHeadDim;
-                float s = 0.f, dp = 0.f;
-                for (int x = 0; x < kHeadDim; ++x) {
-                    s = fmaf(qv[x], kr[x], s);
-                    dp = fmaf(gv[x], vr[x], dp);
-                }
-                const float p = exp2f(s * a.sl2 + bias - lse[(int64_t)h * a.N + tok] * kLog2e);
-                const float ds = p * (dp - ws.D[(int64_t)h * a.N + tok]);
-                for (int x = 0; x < kHeadDim; ++x) {
-                    gk[x] = fmaf(ds, qv[x], gk[x]);
-                    gvv[x] = fmaf(p, gv[x], gvv[x]);
-                }
+                qx[tt] = q[head_off + tok * kHeadDim + lane];
+                gx[tt] = dout[head_off + tok * kHeadDim + lane];
+            }
+#pragma unroll
+            for (int tt = 0; tt < kBlock; ++tt) {
+                const int64_t tok = (int64_t)h * a.N + (int64_t)ib * kBlock + tt;
+                const float s = wave_sum(qx[tt] * kx);
+                const float dp = wave_sum(gx[tt] * vx);
+                const float p = exp2f(s * a.sl2 + bias - lse[tok] * kLog2e);
+                const float ds = p * (dp - ws.D[tok]);
+                gk = fmaf(ds, qx[tt], gk);
+                gv = fmaf(p, gx[tt], gv);
             }
         }
     }
-    for (int x = 0; x < kHeadDim; ++x) {
-        ws.dpk[a.cl_grad_off[j] + ((int64_t)h * nl + c) * kHeadDim + x] = gk[x] * a.scale;
-        ws.dpv[a.cl_grad_off[j] + ((int64_t)h * nl + c) * kHeadDim + x] = gvv[x];
-    }
+    ws.dpk[a.cl_grad_off[j] + ((int64_t)h * nl + c) * kHeadDim + lane] = gk * a.scale;
+    ws.dpv[a.cl_grad_off[j] + ((int64_t)h * nl + c) * kHeadDim + lane] = gv;
 }
 
-// Pass C (f32): one thread per key token.
+// Pass C (f32): one wave per key token.
 __global__ __launch_bounds__(256) void bwd_dkv_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ lse, const float *__restrict__ dout, const int32_t *__restrict__ csr_ptr,
     const int32_t *__restrict__ csr_col, void *__restrict__ dk, void *__restrict__ dv, BwdWs ws,
     BwdArgs a) {
-    const int64_t tu = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t tu = (int64_t)blockIdx.x * 4 + wave_id();
     if (tu >= (int64_t)a.bh * a.N) return;
+    const int lane = lane_id();
     const int h = (int)(tu / a.N);
     const int u = (int)(tu % a.N);
     const int f = u / kBlock;
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
-    const float *kr = k + head_off + (int64_t)u * kHeadDim;
-    const float *vr = v + head_off + (int64_t)u * kHeadDim;
-    float gk[kHeadDim], gvv[kHeadDim];
-    for (int e = 0; e < kHeadDim; ++e) {
-        gk[e] = 0.f;
-        gvv[e] = 0.f;
-    }
+    const int64_t row = head_off + (int64_t)u * kHeadDim + lane;
+    const float kx = k[row], vx = v[row];
+    float gk = 0.f, gv = 0.f;
     const int32_t *P = csr_ptr + (int64_t)h * (a.n1 + 1);
     const int32_t *C = csr_col + (int64_t)h * a.n1 * a.K1;
-    for (int e = P[f]; e < P[f + 1]; ++e) {
-        const int ib = C[e];
+    const int e0 = __builtin_amdgcn_readfirstlane(P[f]), e1 = __builtin_amdgcn_readfirstlane(P[f + 1]);
+    for (int e = e0; e < e1; ++e) {
+        const int ib = __builtin_amdgcn_readfirstlane(C[e]);
+        float qx[kBlock], gx[kBlock];
+#pragma unroll
         for (int tt = 0; tt < kBlock; ++tt) {
             const int64_t tok = (int64_t)ib * kBlock + tt;
-            const float *qv = q + head_off + tok * kHeadDim;
-            const float *gv = dout + head_off + tok * kHeadDim;
-            float s = 0.f, dp = 0.f;
-            for (int x = 0; x < kHeadDim; ++x) {
-                s = fmaf(qv[x], kr[x], s);
-                dp = fmaf(gv[x], vr[x], dp);
-            }
-            const float p = exp2f(s * a.sl2 - lse[(int64_t)h * a.N + tok] * kLog2e);
-            const float ds = p * (dp - ws.D[(int64_t)h * a.N + tok]);
-            for (int x = 0; x < kHeadDim; ++x) {
-                gk[x] = fmaf(ds, qv[x], gk[x]);
-                gvv[x] = fmaf(p, gv[x], gvv[x]);
-            }
+            qx[tt] = q[head_off + tok * kHeadDim + lane];
+            gx[tt] = dout[head_off + tok * kHeadDim + lane];
+        }
+#pragma unroll
+        for (int tt = 0; tt < kBlock; ++tt) {
+            const int64_t tok = (int64_t)h * a.N + (int64_t)ib * kBlock + tt;
+            const float s = wave_sum(qx[tt] * kx);
+            const float dp = wave_sum(gx[tt] * vx);
+            const float p = exp2f(s * a.sl2 - lse[tok] * kLog2e);
+            gk = fmaf(p * (dp - ws.D[tok]), qx[tt], gk);
+            gv = fmaf(p, gx[tt], gv);
         }
     }
-    for (int x = 0; x < kHeadDim; ++x) gk[x] *= a.scale;
+    gk *= a.scale;
     float inv = 1.f;
     for (int j = 0; j < a.ncl; ++j) {
         inv *= (1.0f / kBlock);
         const int c = f / a.cl_span[j];
-        const int64_t off = a.cl_grad_off[j] + ((int64_t)h * a.cl_n[j] + c) * kHeadDim;
-        for (int x = 0; x < kHeadDim; ++x) {
-            gk[x] += ws.dpk[off + x] * (inv * (1.0f / kBlock));
-            gvv[x] += ws.dpv[off + x] * (inv * (1.0f / kBlock));
-        }
+        const int64_t off = a.cl_grad_off[j] + ((int64_t)h * a.cl_n[j] + c) * kHeadDim + lane;
+        gk += ws.dpk[off] * (inv * (1.0f / kBlock));
+        gv += ws.dpv[off] * (inv * (1.0f / kBlock));
     }
-    for (int x = 0; x < kHeadDim; ++x) {
-        store_grad1(dk, head_off + (int64_t)u * kHeadDim + x, gk[x], a.grad_bf16);
-        store_grad1(dv, head_off + (int64_t)u * kHeadDim + x, gvv[x], a.grad_bf16);
-    }
+    store_grad1(dk, row, gk, a.grad_bf16);
+    store_grad1(dv, row, gv, a.grad_bf16);
 }
 
 hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, const void *v,
@@ -1078,16 +1078,16 @@ hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, cons
                            dv, ws, a);
     } else {
         const int64_t total = (int64_t)g.bh * g.N;
-        hipLaunchKernelGGL(bwd_dq_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+        hipLaunchKernelGGL(bwd_dq_f32_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s,
                            (const float *)q, (const float *)k, (const float *)v, pk, pv, idx,
                            (const float *)o, lse, (const float *)dout, dq, ws, a);
         for (int j = 0; j < a.ncl; ++j) {
             const int64_t nt = (int64_t)g.bh * a.cl_n[j];
-            hipLaunchKernelGGL(bwd_coarse_f32_kernel, dim3((unsigned)((nt + 63) / 64)), dim3(64), 0,
+            hipLaunchKernelGGL(bwd_coarse_f32_kernel, dim3((unsigned)((nt + 3) / 4)), dim3(256), 0,
                                s, (const float *)q, pk, pv, idx, lse, (const float *)dout, csr_ptr,
                                csr_col, ws, a, j);
         }
-        hipLaunchKernelGGL(bwd_dkv_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+        hipLaunchKernelGGL(bwd_dkv_f32_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0,
                            s, (const float *)q, (const float *)k, (const float *)v, lse,
                            (const float *)dout, csr_ptr + g.ptr_off[1], csr_col + g.col_off[1], dk,
                            dv, ws, a);

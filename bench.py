@@ -101,7 +101,7 @@ def cpu_baseline(w, max_heads):
                       f"pool+select+fwd+transpose+bwd in fp64 ({dt:.1f} s)"}
 
 
-def time_workload(L, w, steps, warmup, dev, grad_bf16=False):
+def time_workload(L, w, steps, warmup, dev, grad_bf16=False, token_order=0):
     """Runs `warmup` untimed and `steps` timed steps of the whole path on
     workload `w` (inputs resident on the GPU); returns the inputs, problem,
     buffers, sizes, the mean per-call milliseconds (HIP events on the current
@@ -112,7 +112,7 @@ def time_workload(L, w, steps, warmup, dev, grad_bf16=False):
     q, k, v = q.to(dev), k.to(dev), v.to(dev)
     dout = dout.to(dev) if dout is not None else None
     p = L.problem(w.batch, w.heads, w.seq_len, w.head_dim, w.block, w.levels, w.topk, w.enrich,
-                  w.dtype, torch.bfloat16 if grad_bf16 else torch.float32)
+                  w.dtype, torch.bfloat16 if grad_bf16 else torch.float32, token_order=token_order)
     B = L.Buffers(p, backward=w.backward)
     s = B.s
     bh = w.bh
@@ -164,15 +164,16 @@ def sweep_workloads():
     from dataclasses import replace
     from hierarchical_top_sparse_mean_amd.inputs import WORKLOADS
     base = WORKLOADS["n65536_bf16"]
-    out = [(w, False) for w in WORKLOADS.values()]
+    out = [(w, "") for w in WORKLOADS.values()]
     out += [
-        (replace(base, name="n65536_L3_Le2", levels=3, enrich=2), False),
-        (replace(base, name="n65536_Le0", enrich=0), False),
-        (replace(base, name="n65536_K16", topk=16), False),
-        (replace(base, name="n65536_L1_K8", levels=1, enrich=0), False),
-        (replace(base, name="n65536_L1_K20", levels=1, topk=20, enrich=0), False),
-        (replace(base, name="n65536_L1_K32", levels=1, topk=32, enrich=0), False),
-        (base, True),   # bfloat16 gradients
+        (replace(base, name="n65536_L3_Le2", levels=3, enrich=2), ""),
+        (replace(base, name="n65536_Le0", enrich=0), ""),
+        (replace(base, name="n65536_K16", topk=16), ""),
+        (replace(base, name="n65536_L1_K8", levels=1, enrich=0), ""),
+        (replace(base, name="n65536_L1_K20", levels=1, topk=20, enrich=0), ""),
+        (replace(base, name="n65536_L1_K32", levels=1, topk=32, enrich=0), ""),
+        (base, "grad_bf16"),
+        (base, "patch_order"),   # the image tokens read as nested 2D patches
     ]
     return out
 
@@ -205,11 +206,12 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     if args.sweep:
-        for sw, gbf in sweep_workloads():
-            _, _, _, _, _, _, ss, pc, msps = time_workload(L, sw, args.steps, args.warmup, dev, gbf)
+        for sw, var in sweep_workloads():
+            _, _, _, _, _, _, ss, pc, msps = time_workload(L, sw, args.steps, args.warmup, dev,
+                                                          var == "grad_bf16", int(var == "patch_order"))
             alg, nkv = algorithmic(sw, ss)
             tok = sw.batch * sw.seq_len
-            rec = {"sweep": sw.name + ("_gradbf16" if gbf else ""), "describe": sw.describe(),
+            rec = {"sweep": sw.name + ("_" + var if var else ""), "describe": sw.describe(),
                    "keys_per_query_block": nkv, "ms_per_step": round(msps, 4),
                    "tokens_per_s": round(tok / (msps / 1e3), 1),
                    # per token and head: selection + attention forward, the part whose

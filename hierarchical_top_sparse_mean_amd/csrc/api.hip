@@ -28,6 +28,12 @@ int make_geometry(const llsa_problem *p, Geometry *g, llsa_sizes *sz) {
     if (p->dtype != LLSA_F32 && p->dtype != LLSA_BF16) return LLSA_ERR_INVALID;
     if (p->grad_dtype != LLSA_F32 && p->grad_dtype != LLSA_BF16) return LLSA_ERR_INVALID;
     if (p->drop_covered != 0 && p->drop_covered != 1) return LLSA_ERR_INVALID;
+    if (p->token_order != 0 && p->token_order != 1) return LLSA_ERR_INVALID;
+    int log2S = 0;
+    if (p->token_order == 1) {   // a square image with a power-of-two side
+        while (log2S < 16 && ((int64_t)1 << (2 * log2S)) < p->seq_len) ++log2S;
+        if (((int64_t)1 << (2 * log2S)) != p->seq_len) return LLSA_ERR_INVALID;
+    }
     if (!(p->scale >= 0.0f) || isinf(p->scale)) return LLSA_ERR_INVALID;
     if (p->levels > LLSA_MAX_LEVELS) return LLSA_ERR_UNSUPPORTED;
     // divisibility by block^levels (checked in 64 bits before anything else)
@@ -78,6 +84,8 @@ int make_geometry(const llsa_problem *p, Geometry *g, llsa_sizes *sz) {
         }
     }
     g->scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
+    g->order = p->token_order;
+    g->log2S = log2S;
     g->drop_covered = p->drop_covered;
     g->bf16 = p->dtype == LLSA_BF16;
     g->grad_bf16 = p->grad_dtype == LLSA_BF16;

@@ -39,6 +39,7 @@ struct BwdArgs {
     float scale, sl2;
     int drop;
     int grad_bf16;
+    TokMap tm;   // storage row of a sequence position (D stays in sequence order)
 };
 
 struct BwdWs {
@@ -77,6 +78,7 @@ static BwdArgs make_bwd_args(const Geometry &g) {
     a.sl2 = g.scale * kLog2e;
     a.drop = g.drop_covered;
     a.grad_bf16 = g.grad_bf16 ? 1 : 0;
+    a.tm = TokMap{g.order, g.log2S};
     return a;
 }
 
@@ -264,14 +266,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     for (int jb = 0; jb < 4; ++jb) {
         const int ib = G * kBlock + w * 4 + jb;
         if (ib >= a.n1) break;
-        const int64_t row = (int64_t)ib * kBlock + c16;
-        const __bf16 *qrow = q + head_off + row * kHeadDim;
-        const __bf16 *drow = dout + head_off + row * kHeadDim;
+        const int64_t row = (int64_t)ib * kBlock + c16;          // sequence position
+        const int64_t srow = tok_row(a.tm, ib * kBlock + c16);   // its storage row
+        const __bf16 *qrow = q + head_off + srow * kHeadDim;
+        const __bf16 *drow = dout + head_off + srow * kHeadDim;
         const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
         auto load_tile = [&](int t, TileRegs &R) {
             const int f = __builtin_amdgcn_readfirstlane(fine[min(t, a.K1 - 1)]);
-            const __bf16 *kt = k + head_off + (int64_t)f * kBlock * kHeadDim + c16 * kHeadDim;
-            const __bf16 *vt = v + head_off + (int64_t)f * kBlock * kHeadDim + c16 * kHeadDim;
+            const int64_t kr = (int64_t)tok_row(a.tm, f * kBlock + c16) * kHeadDim;
+            const __bf16 *kt = k + head_off + kr;
+            const __bf16 *vt = v + head_off + kr;
             R.ka0 = load_bf16x8(kt + 8 * g);
             R.ka1 = load_bf16x8(kt + 32 + 8 * g);
             R.va0 = load_bf16x8(vt + 8 * g);
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
         };
         const bf16x8 qa0 = load_bf16x8(qrow + 8 * g), qa1 = load_bf16x8(qrow + 32 + 8 * g);
         const bf16x8 da0 = load_bf16x8(drow + 8 * g), da1 = load_bf16x8(drow + 32 + 8 * g);
-        const float lse2 = lse[(int64_t)h * a.N + row] * kLog2e;
+        const float lse2 = lse[(int64_t)h * a.N + srow] * kLog2e;
         TileRegs RA, RB;
         load_tile(0, RA);
         load_tile(1, RB);
@@ -390,7 +394,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
         for (int dt = 0; dt < 4; ++dt) dqacc[dt] = accA[dt] - Dq * accB[dt];
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
-            store_grad4(dq, head_off + row * kHeadDim + 16 * dt + 4 * g, dqacc[dt] * a.scale, a.grad_bf16);
+            store_grad4(dq, head_off + srow * kHeadDim + 16 * dt + 4 * g, dqacc[dt] * a.scale, a.grad_bf16);
         wave_lds_sync();
     }
     // ---- reduce the coarse partials over the 4 waves, one coarse tile at a time
@@ -429,6 +433,7 @@ constexpr int kFastK1 = 8;
 constexpr int kFastTiles = 4 * kFastK1;   // fine tiles per wave
 constexpr int kPtS = 20;                  // float row stride of the P / dS exchange
 
+template <int ORD>
 __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ pk, const float *__restrict__ pv, const int32_t *__restrict__ idx,
@@ -496,28 +501,28 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
         store_bf16x8(dst + lrow * kTS + lcol, r0);
         store_bf16x8(dst + (lrow + 8) * kTS + lcol, r1);
     };
+    // element offset (within the head) of row r of sequence block b
+    auto trow = [&](int b, int r) { return (int64_t)tok_row_o<ORD>(a.tm, b * kBlock + r) * kHeadDim; };
     auto load_tile = [&](int u, TileRegs &R) {
         const int f = __builtin_amdgcn_readlane(fidx, u);
-        const __bf16 *kt = k + head_off + (int64_t)f * kBlock * kHeadDim;
-        const __bf16 *vt = v + head_off + (int64_t)f * kBlock * kHeadDim;
-        R.ka0 = load_bf16x8(kt + lane * 8);
-        R.ka1 = load_bf16x8(kt + (lane + kWave) * 8);
-        R.va0 = load_bf16x8(vt + lane * 8);
-        R.va1 = load_bf16x8(vt + (lane + kWave) * 8);
+        const int64_t o0 = head_off + trow(f, lrow) + lcol, o1 = head_off + trow(f, lrow + 8) + lcol;
+        R.ka0 = load_bf16x8(k + o0);
+        R.ka1 = load_bf16x8(k + o1);
+        R.va0 = load_bf16x8(v + o0);
+        R.va1 = load_bf16x8(v + o1);
     };
     struct QRegs {
         bf16x8 qa0, qa1, da0, da1;
         float lse2;
     };
     auto load_q = [&](int jb, QRegs &X) {
-        const int64_t row0 = (int64_t)(ib0 + w * 4 + jb) * kBlock;
-        const __bf16 *qb = q + head_off + row0 * kHeadDim;
-        const __bf16 *db = dout + head_off + row0 * kHeadDim;
-        X.qa0 = load_bf16x8(qb + lane * 8);
-        X.qa1 = load_bf16x8(qb + (lane + kWave) * 8);
-        X.da0 = load_bf16x8(db + lane * 8);
-        X.da1 = load_bf16x8(db + (lane + kWave) * 8);
-        X.lse2 = lse[(int64_t)h * a.N + row0 + c16] * kLog2e;
+        const int b = ib0 + w * 4 + jb;
+        const int64_t o0 = head_off + trow(b, lrow) + lcol, o1 = head_off + trow(b, lrow + 8) + lcol;
+        X.qa0 = load_bf16x8(q + o0);
+        X.qa1 = load_bf16x8(q + o1);
+        X.da0 = load_bf16x8(dout + o0);
+        X.da1 = load_bf16x8(dout + o1);
+        X.lse2 = lse[(int64_t)h * a.N + tok_row_o<ORD>(a.tm, b * kBlock + c16)] * kLog2e;
     };
     QRegs X;
     load_q(0, X);
@@ -643,7 +648,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
         }
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
-            store_grad4(dq, head_off + row * kHeadDim + 16 * dt + 4 * g,
+            store_grad4(dq, head_off + trow(ib0 + w * 4 + jb, c16) + 16 * dt + 4 * g,
                         (accA[dt] - Dq * accB[dt]) * a.scale, a.grad_bf16);
     }
     // ---- reduce the coarse partials over the 4 waves
@@ -746,6 +751,7 @@ __global__ __launch_bounds__(256) void bwd_coarse_reduce_kernel(const int32_t *_
 // segment stream through a ring of kDkvDepth register sets, so that several
 // blocks' Q / dO are in flight while one is computed.
 constexpr int kDkvDepth = 4;
+template <int ORD>
 __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ lse, const __bf16 *__restrict__ dout, const int32_t *__restrict__ csr_ptr,
@@ -761,8 +767,10 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
     const int h = (int)(kb / a.n1);
     const int f = (int)(kb % a.n1);
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
-    const __bf16 *krow = k + head_off + ((int64_t)f * kBlock + c16) * kHeadDim;
-    const __bf16 *vrow = v + head_off + ((int64_t)f * kBlock + c16) * kHeadDim;
+    // element offset (within the head) of row r of sequence block b
+    auto trow = [&](int b, int r) { return (int64_t)tok_row_o<ORD>(a.tm, b * kBlock + r) * kHeadDim; };
+    const __bf16 *krow = k + head_off + trow(f, c16);
+    const __bf16 *vrow = v + head_off + trow(f, c16);
     const bf16x8 kb0 = load_bf16x8(krow + 8 * g), kb1 = load_bf16x8(krow + 32 + 8 * g);
     const bf16x8 vb0 = load_bf16x8(vrow + 8 * g), vb1 = load_bf16x8(vrow + 32 + 8 * g);
     f32x4 dka[4], dva[4];
@@ -786,13 +794,14 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
     const float *ld_src = lane < kBlock ? lse : ws.D;
     const int lrow = lane >> 3, lcol = (lane & 7) * 8;
     auto load_pair = [&](int ib, Pair &X) {
-        const __bf16 *qr = q + head_off + (int64_t)ib * kBlock * kHeadDim;
-        const __bf16 *dr = dout + head_off + (int64_t)ib * kBlock * kHeadDim;
-        X.qa0 = load_bf16x8(qr + lane * 8);
-        X.qa1 = load_bf16x8(qr + (lane + kWave) * 8);
-        X.da0 = load_bf16x8(dr + lane * 8);
-        X.da1 = load_bf16x8(dr + (lane + kWave) * 8);
-        X.ld = ld_src[(int64_t)h * a.N + (int64_t)ib * kBlock + c16];
+        const int64_t o0 = head_off + trow(ib, lrow) + lcol, o1 = head_off + trow(ib, lrow + 8) + lcol;
+        X.qa0 = load_bf16x8(q + o0);
+        X.qa1 = load_bf16x8(q + o1);
+        X.da0 = load_bf16x8(dout + o0);
+        X.da1 = load_bf16x8(dout + o1);
+        // lse is stored by token row, D by sequence position
+        const int pos = ib * kBlock + c16;
+        X.ld = ld_src[(int64_t)h * a.N + (lane < kBlock ? tok_row_o<ORD>(a.tm, pos) : pos)];
     };
     auto compute = [&](const Pair &X) {
         wave_lds_sync();
@@ -866,7 +875,7 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t off = head_off + ((int64_t)f * kBlock + 4 * g + i) * kHeadDim + dim;
+            const int64_t off = head_off + trow(f, 4 * g + i) + dim;
             store_grad1(dk, off, dka[dt][i] * a.scale + ck, a.grad_bf16);
             store_grad1(dv, off, dva[dt][i] + cv, a.grad_bf16);
         }
@@ -896,11 +905,12 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(
     const int tok = (int)(tq % a.N);
     const int ib = tok / kBlock;
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
-    const int64_t row = head_off + (int64_t)tok * kHeadDim + lane;
+    const int64_t srow = tok_row(a.tm, tok);
+    const int64_t row = head_off + srow * kHeadDim + lane;
     const float qx = q[row], gx = dout[row];
     const float D = wave_sum(gx * o[row]);
-    if (lane == 0) ws.D[tq] = D;
-    const float lse2 = lse[tq] * kLog2e;
+    if (lane == 0) ws.D[tq] = D;   // by sequence position
+    const float lse2 = lse[(int64_t)h * a.N + srow] * kLog2e;
     float acc = 0.f;
     auto visit = [&](float kx, float vx, float bias) {
         const float s = wave_sum(qx * kx);
@@ -910,12 +920,13 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(
     };
     const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
     for (int j = 0; j < a.K1; ++j) {
-        const int64_t u0 = (int64_t)__builtin_amdgcn_readfirstlane(fine[j]) * kBlock;
+        const int u0 = __builtin_amdgcn_readfirstlane(fine[j]) * kBlock;
         float kx[kBlock], vx[kBlock];
 #pragma unroll
         for (int t = 0; t < kBlock; ++t) {
-            kx[t] = k[head_off + (u0 + t) * kHeadDim + lane];
-            vx[t] = v[head_off + (u0 + t) * kHeadDim + lane];
+            const int64_t kr = head_off + (int64_t)tok_row(a.tm, u0 + t) * kHeadDim + lane;
+            kx[t] = k[kr];
+            vx[t] = v[kr];
         }
 #pragma unroll
         for (int t = 0; t < kBlock; ++t) visit(kx[t], vx[t], 0.f);
@@ -964,18 +975,19 @@ __global__ __launch_bounds__(256) void bwd_coarse_f32_kernel(
                 if (cov == span) continue;
             }
             float qx[kBlock], gx[kBlock];
+            int64_t srow[kBlock];
 #pragma unroll
             for (int tt = 0; tt < kBlock; ++tt) {
-                const int64_t tok = (int64_t)ib * kBlock + tt;
-                qx[tt] = q[head_off + tok * kHeadDim + lane];
-                gx[tt] = dout[head_off + tok * kHeadDim + lane];
+                srow[tt] = tok_row(a.tm, ib * kBlock + tt);
+                qx[tt] = q[head_off + srow[tt] * kHeadDim + lane];
+                gx[tt] = dout[head_off + srow[tt] * kHeadDim + lane];
             }
 #pragma unroll
             for (int tt = 0; tt < kBlock; ++tt) {
                 const int64_t tok = (int64_t)h * a.N + (int64_t)ib * kBlock + tt;
                 const float s = wave_sum(qx[tt] * kx);
                 const float dp = wave_sum(gx[tt] * vx);
-                const float p = exp2f(s * a.sl2 + bias - lse[tok] * kLog2e);
+                const float p = exp2f(s * a.sl2 + bias - lse[(int64_t)h * a.N + srow[tt]] * kLog2e);
                 const float ds = p * (dp - ws.D[tok]);
                 gk = fmaf(ds, qx[tt], gk);
                 gv = fmaf(p, gx[tt], gv);
@@ -999,7 +1011,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_f32_kernel(
     const int u = (int)(tu % a.N);
     const int f = u / kBlock;
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
-    const int64_t row = head_off + (int64_t)u * kHeadDim + lane;
+    const int64_t row = head_off + (int64_t)tok_row(a.tm, u) * kHeadDim + lane;
     const float kx = k[row], vx = v[row];
     float gk = 0.f, gv = 0.f;
     const int32_t *P = csr_ptr + (int64_t)h * (a.n1 + 1);
@@ -1008,18 +1020,19 @@ __global__ __launch_bounds__(256) void bwd_dkv_f32_kernel(
     for (int e = e0; e < e1; ++e) {
         const int ib = __builtin_amdgcn_readfirstlane(C[e]);
         float qx[kBlock], gx[kBlock];
+        int64_t srow[kBlock];
 #pragma unroll
         for (int tt = 0; tt < kBlock; ++tt) {
-            const int64_t tok = (int64_t)ib * kBlock + tt;
-            qx[tt] = q[head_off + tok * kHeadDim + lane];
-            gx[tt] = dout[head_off + tok * kHeadDim + lane];
+            srow[tt] = tok_row(a.tm, ib * kBlock + tt);
+            qx[tt] = q[head_off + srow[tt] * kHeadDim + lane];
+            gx[tt] = dout[head_off + srow[tt] * kHeadDim + lane];
         }
 #pragma unroll
         for (int tt = 0; tt < kBlock; ++tt) {
             const int64_t tok = (int64_t)h * a.N + (int64_t)ib * kBlock + tt;
             const float s = wave_sum(qx[tt] * kx);
             const float dp = wave_sum(gx[tt] * vx);
-            const float p = exp2f(s * a.sl2 - lse[tok] * kLog2e);
+            const float p = exp2f(s * a.sl2 - lse[(int64_t)h * a.N + srow[tt]] * kLog2e);
             gk = fmaf(p * (dp - ws.D[tok]), qx[tt], gk);
             gv = fmaf(p, gx[tt], gv);
         }
@@ -1050,8 +1063,12 @@ hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, cons
         const dim3 grid((unsigned)(g.bh * gph));
         const bool fast = g.L >= 2 && a.K1 == kFastK1 && nct == 1 && a.n1 % kBlock == 0 &&
                           !(a.drop && a.K1 >= kBlock);
-        if (fast)
-            hipLaunchKernelGGL(bwd_dq_fast_kernel, grid, dim3(256), 0, s, (const __bf16 *)q,
+        if (fast && g.order == 0)
+            hipLaunchKernelGGL(bwd_dq_fast_kernel<0>, grid, dim3(256), 0, s, (const __bf16 *)q,
+                               (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx, lse,
+                               (const __bf16 *)dout, dq, ws, a);
+        else if (fast)
+            hipLaunchKernelGGL(bwd_dq_fast_kernel<1>, grid, dim3(256), 0, s, (const __bf16 *)q,
                                (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx, lse,
                                (const __bf16 *)dout, dq, ws, a);
         else if (nct == 0)
@@ -1072,10 +1089,16 @@ hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, cons
                                dim3(256), 0, s, idx, csr_ptr, csr_col, ws, a, j);
         }
         const int64_t kbs = (int64_t)g.bh * a.n1;
-        hipLaunchKernelGGL(bwd_dkv_bf16_kernel, dim3((unsigned)kbs), dim3(kWave), 0, s,
-                           (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, lse,
-                           (const __bf16 *)dout, csr_ptr + g.ptr_off[1], csr_col + g.col_off[1], dk,
-                           dv, ws, a);
+        if (g.order == 0)
+            hipLaunchKernelGGL(bwd_dkv_bf16_kernel<0>, dim3((unsigned)kbs), dim3(kWave), 0, s,
+                               (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, lse,
+                               (const __bf16 *)dout, csr_ptr + g.ptr_off[1], csr_col + g.col_off[1],
+                               dk, dv, ws, a);
+        else
+            hipLaunchKernelGGL(bwd_dkv_bf16_kernel<1>, dim3((unsigned)kbs), dim3(kWave), 0, s,
+                               (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, lse,
+                               (const __bf16 *)dout, csr_ptr + g.ptr_off[1], csr_col + g.col_off[1],
+                               dk, dv, ws, a);
     } else {
         const int64_t total = (int64_t)g.bh * g.N;
         hipLaunchKernelGGL(bwd_dq_f32_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s,

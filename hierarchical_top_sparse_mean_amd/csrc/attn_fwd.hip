@@ -35,6 +35,7 @@ struct FwdArgs {
     int64_t cl_pyr_off[kMaxCoarseLevels];      // pyramid offset of the level
     float sl2;                                 // scale * log2(e)
     int drop;                                  // drop fully covered coarse picks
+    TokMap tm;                                 // storage row of a sequence position
 };
 
 static FwdArgs make_fwd_args(const Geometry &g) {
@@ -58,6 +59,7 @@ static FwdArgs make_fwd_args(const Geometry &g) {
     }
     a.sl2 = g.scale * kLog2e;
     a.drop = g.drop_covered;
+    a.tm = TokMap{g.order, g.log2S};
     return a;
 }
 
@@ -186,7 +188,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     const __bf16 *vh = v + head_off;
     __bf16 *vw = vs_all[w];
 
-    const __bf16 *qrow = q + head_off + (int64_t)(ib * kBlock + c16) * kHeadDim;
+    // element offset (within the head) of row r of sequence block b
+    auto trow = [&](int b, int r) { return (int64_t)tok_row(a.tm, b * kBlock + r) * kHeadDim; };
+    const __bf16 *qrow = q + head_off + trow(ib, c16);
     const bf16x8 qa0 = load_bf16x8(qrow + 8 * g);
     const bf16x8 qa1 = load_bf16x8(qrow + 32 + 8 * g);
     const int32_t *fine = idx + blk * a.K1;
@@ -211,12 +215,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
         for (int t = 0; t < kFwdTiles; ++t) {
             const int f = __builtin_amdgcn_readfirstlane(fine[t0 + min(t, nt - 1)]);
-            const __bf16 *kt = kh + (int64_t)f * kBlock * kHeadDim;
-            const __bf16 *vt = vh + (int64_t)f * kBlock * kHeadDim;
-            kr[t][0] = load_bf16x8(kt + c16 * kHeadDim + 8 * g);
-            kr[t][1] = load_bf16x8(kt + c16 * kHeadDim + 32 + 8 * g);
-            vr[t][0] = load_bf16x8(vt + lane * 8);              // 16-byte chunk `lane` of the tile
-            vr[t][1] = load_bf16x8(vt + (lane + kWave) * 8);    // chunk `lane + 64`
+            const __bf16 *kt = kh + trow(f, c16);
+            kr[t][0] = load_bf16x8(kt + 8 * g);
+            kr[t][1] = load_bf16x8(kt + 32 + 8 * g);
+            // 16-byte chunks `lane` and `lane + 64` of the tile: rows lane/8 and lane/8 + 8
+            vr[t][0] = load_bf16x8(vh + trow(f, lane >> 3) + (lane & 7) * 8);
+            vr[t][1] = load_bf16x8(vh + trow(f, (lane >> 3) + 8) + (lane & 7) * 8);
         }
         if (t0 == 0 && nct > 0) prefetch_coarse(a, idx, fine, pk, pv, h, ib, 0, cpick0, g, c16, cr);
 #pragma unroll
@@ -248,14 +252,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     // ---- normalise and store
     lsum = sum4_groups(lsum);
     const float inv = 1.0f / lsum;
-    __bf16 *orow = o + head_off + (int64_t)(ib * kBlock + c16) * kHeadDim + 4 * g;
+    __bf16 *orow = o + head_off + trow(ib, c16) + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
         const f32x4 r = oacc[dt] * inv;
         const bf16x4 rb = to_bf16x4(f32x4{r[0], r[1], r[2], r[3]});
         *reinterpret_cast<u32x2 *>(orow + 16 * dt) = __builtin_bit_cast(u32x2, rb);
     }
-    if (g == 0) lse[(int64_t)h * a.N + ib * kBlock + c16] = (m + log2f(lsum)) * kLn2;
+    if (g == 0) lse[(int64_t)h * a.N + tok_row(a.tm, ib * kBlock + c16)] = (m + log2f(lsum)) * kLn2;
 }
 
 // ------------------------------------------------------------ fast path
@@ -266,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
 // (pooled K rows for the MFMA operand, V rows for the transposing read).
 // Fine and coarse tiles form one softmax chunk: one max, no rescaling, and
 // every loop is unrolled.
-template <int KT>
+template <int KT, int ORD>
 __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ pk, const float *__restrict__ pv, const int32_t *__restrict__ idx,
@@ -294,20 +298,21 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
     // ---- this wave's loads: Q, then every fine K / V tile, each as whole
     // 128-byte rows per instruction (lane l: rows l / 8 and l / 8 + 8, 16-byte
     // chunk l % 8); rows reach the MFMA operand layout through LDS
-    const __bf16 *qb = q + head_off + (int64_t)ib * kBlock * kHeadDim;
-    const bf16x8 qr0 = load_bf16x8(qb + lane * 8);
-    const bf16x8 qr1 = load_bf16x8(qb + (lane + kWave) * 8);
+    // element offset (within the head) of row r of sequence block b
+    auto trow = [&](int b, int r) { return (int64_t)tok_row_o<ORD>(a.tm, b * kBlock + r) * kHeadDim; };
+    const int lr = lane >> 3, lc = (lane & 7) * 8;
+    const bf16x8 qr0 = load_bf16x8(q + head_off + trow(ib, lr) + lc);
+    const bf16x8 qr1 = load_bf16x8(q + head_off + trow(ib, lr + 8) + lc);
     const int32_t *fine = idx + blk * KT;
     bf16x8 kr[KT][2], vr[KT][2];
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
         const int f = __builtin_amdgcn_readfirstlane(fine[t]);
-        const __bf16 *kt = kh + (int64_t)f * kBlock * kHeadDim;
-        const __bf16 *vt = vh + (int64_t)f * kBlock * kHeadDim;
-        kr[t][0] = load_bf16x8(kt + lane * 8);
-        kr[t][1] = load_bf16x8(kt + (lane + kWave) * 8);
-        vr[t][0] = load_bf16x8(vt + lane * 8);
-        vr[t][1] = load_bf16x8(vt + (lane + kWave) * 8);
+        const int64_t o0 = trow(f, lr) + lc, o1 = trow(f, lr + 8) + lc;
+        kr[t][0] = load_bf16x8(kh + o0);
+        kr[t][1] = load_bf16x8(kh + o1);
+        vr[t][0] = load_bf16x8(vh + o0);
+        vr[t][1] = load_bf16x8(vh + o1);
     }
     auto stage_rows = [&](__bf16 *dst, bf16x8 r0, bf16x8 r1) {
         store_bf16x8(dst + (lane >> 3) * kVStride + (lane & 7) * 8, r0);
@@ -425,14 +430,14 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
     // ---- normalise and store
     lsum = sum4_groups(lsum);
     const float inv = 1.0f / lsum;
-    __bf16 *orow = o + head_off + (int64_t)(ib * kBlock + c16) * kHeadDim + 4 * g;
+    __bf16 *orow = o + head_off + trow(ib, c16) + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
         const f32x4 r = oacc[dt] * inv;
         const bf16x4 rb = to_bf16x4(f32x4{r[0], r[1], r[2], r[3]});
         *reinterpret_cast<u32x2 *>(orow + 16 * dt) = __builtin_bit_cast(u32x2, rb);
     }
-    if (g == 0) lse[(int64_t)h * a.N + ib * kBlock + c16] = (mx + log2f(lsum)) * kLn2;
+    if (g == 0) lse[(int64_t)h * a.N + tok_row_o<ORD>(a.tm, ib * kBlock + c16)] = (mx + log2f(lsum)) * kLn2;
 }
 
 // ---------------------------------------------------------------- f32 path
@@ -449,7 +454,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
     float qv[kHeadDim], acc[kHeadDim];
 #pragma unroll
     for (int e = 0; e < kHeadDim; ++e) {
-        qv[e] = q[head_off + (int64_t)tok * kHeadDim + e];
+        qv[e] = q[head_off + (int64_t)tok_row(a.tm, tok) * kHeadDim + e];
         acc[e] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
@@ -470,7 +475,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
     for (int j = 0; j < a.K1; ++j) {
         const int f = fine[j];
         for (int t = 0; t < kBlock; ++t) {
-            const int64_t u = (int64_t)f * kBlock + t;
+            const int64_t u = tok_row(a.tm, f * kBlock + t);
             attend(k + head_off + u * kHeadDim, v + head_off + u * kHeadDim, 0.f);
         }
     }
@@ -480,9 +485,10 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
         if (coarse_entry(a, idx, fine, h, ib, e, roff, b)) attend(pk + roff, pv + roff, b);
     }
     const float inv = 1.0f / l;
+    const int64_t orow = (int64_t)tok_row(a.tm, tok);
 #pragma unroll
-    for (int e = 0; e < kHeadDim; ++e) o[head_off + (int64_t)tok * kHeadDim + e] = acc[e] * inv;
-    lse[tq] = (m + log2f(l)) * kLn2;
+    for (int e = 0; e < kHeadDim; ++e) o[head_off + orow * kHeadDim + e] = acc[e] * inv;
+    lse[(int64_t)h * a.N + orow] = (m + log2f(l)) * kLn2;
 }
 
 hipError_t launch_attn_fwd(const Geometry &g, const void *q, const void *k, const void *v,
@@ -493,9 +499,13 @@ hipError_t launch_attn_fwd(const Geometry &g, const void *q, const void *k, cons
         const int64_t blocks = (int64_t)g.bh * g.n[1];
         const bool fast = g.L >= 2 && a.K1 == 8 && a.ncoarse > 0 && a.ncoarse <= kBlock &&
                           !(a.drop && a.K1 >= kBlock) && a.n1 % 4 == 0;
-        if (fast)
-            hipLaunchKernelGGL(attn_fwd_fast_kernel<8>, dim3((unsigned)(blocks / 4)), dim3(256), 0, s,
-                               (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx,
+        if (fast && g.order == 0)
+            hipLaunchKernelGGL((attn_fwd_fast_kernel<8, 0>), dim3((unsigned)(blocks / 4)), dim3(256), 0,
+                               s, (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx,
+                               (__bf16 *)o, lse, a);
+        else if (fast)
+            hipLaunchKernelGGL((attn_fwd_fast_kernel<8, 1>), dim3((unsigned)(blocks / 4)), dim3(256), 0,
+                               s, (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx,
                                (__bf16 *)o, lse, a);
         else
             hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3((unsigned)((blocks + 3) / 4)), dim3(256), 0,

@@ -105,6 +105,43 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
     return x * per + (x < rem ? x : rem) + i;
 }
 
+// Token order of the [.., seq_len, ..] tensors (Q, K, V, O, dO, dQ, dK, dV,
+// lse).  order 0: the sequence as stored.  order 1: the tensors hold an
+// S x S image in raster order, and the method runs on the sequence of nested
+// 2^i x 2^i patches (Z order: position t has x in the even and y in the odd
+// bits of t), so 16 consecutive positions are a 4 x 4 patch and a level-l
+// token pools a 4^l x 4^l patch ("Trainable Log-linear Sparse Attention for
+// Efficient Diffusion Transformers", explainer "Step 5: Index Reordering for
+// Images").  Pyramids, index lists and CSR are in sequence order either way.
+struct TokMap {
+    int order;   // 0 or 1
+    int log2S;   // image side, order 1 only
+};
+
+__device__ __forceinline__ uint32_t compact_even_bits(uint32_t v) {
+    v &= 0x55555555u;
+    v = (v | (v >> 1)) & 0x33333333u;
+    v = (v | (v >> 2)) & 0x0f0f0f0fu;
+    v = (v | (v >> 4)) & 0x00ff00ffu;
+    v = (v | (v >> 8)) & 0x0000ffffu;
+    return v;
+}
+
+// Storage row (within one head) of sequence position t; ORD fixes the order
+// at compile time for the hot kernels, tok_row() reads it from m.
+template <int ORD>
+__device__ __forceinline__ int tok_row_o(const TokMap &m, int t) {
+    if constexpr (ORD == 0) {
+        return t;
+    } else {
+        const uint32_t x = compact_even_bits((uint32_t)t), y = compact_even_bits((uint32_t)t >> 1);
+        return (int)((y << m.log2S) | x);
+    }
+}
+__device__ __forceinline__ int tok_row(const TokMap &m, int t) {
+    return m.order == 0 ? t : tok_row_o<1>(m, t);
+}
+
 // Wave-scope ordering for data exchanged through LDS by lanes of one wave.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -24,6 +24,8 @@ struct Geometry {
     int drop_covered;
     bool bf16;                       // input dtype
     bool grad_bf16;                  // gradient dtype
+    int order;                       // token order (0: as stored, 1: 2D patch order)
+    int log2S;                       // image side for order 1
 };
 
 hipError_t launch_pool(const Geometry &g, const void *q, const void *k, const void *v,

@@ -33,12 +33,13 @@ __device__ __forceinline__ void chunk_to_f32(u32x4 r, float *o, float *) {
     o[3] = v[3];
 }
 
-template <typename T>
+template <typename T, int ORD>
 __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                    const T *__restrict__ v, float *__restrict__ pq,
                                                    float *__restrict__ pk, float *__restrict__ pv,
                                                    int64_t total_blocks, int wg_per_tensor,
-                                                   int do_level2, int64_t level2_off) {
+                                                   int do_level2, int64_t level2_off, int n1,
+                                                   TokMap tm) {
     constexpr int EPC = ElemTraits<T>::kPerChunk;  // elements per 16-byte chunk
     constexpr int CPR = kHeadDim / EPC;            // chunks per row
     constexpr int BPW = kWave / CPR;               // level-1 blocks per wave
@@ -59,11 +60,15 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ q, cons
 #pragma unroll
     for (int j = 0; j < EPC; ++j) acc[j] = 0.f;
     if (blk < total_blocks) {
-        const T *src = x + blk * kBlock * kHeadDim + c * EPC;
+        // block blk of head h: sequence positions lb*16 .. lb*16+15
+        const int64_t h = blk / n1;
+        const int lb = (int)(blk % n1);
+        const T *src = x + h * (int64_t)n1 * kBlock * kHeadDim + c * EPC;
         u32x4 r[kBlock];
 #pragma unroll
         for (int t = 0; t < kBlock; ++t)
-            r[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + t * kHeadDim));
+            r[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                src + (int64_t)tok_row_o<ORD>(tm, lb * kBlock + t) * kHeadDim));
 #pragma unroll
         for (int t = 0; t < kBlock; ++t) {
             float f[EPC];
@@ -122,8 +127,13 @@ static void launch_pool_t(const Geometry &g, const T *q, const T *k, const T *v,
     const int64_t total_blocks = (int64_t)g.bh * g.n[1];
     const int wg_per_tensor = (int)((total_blocks + BPG - 1) / BPG);
     const int do2 = g.L >= 2 ? 1 : 0;
-    hipLaunchKernelGGL(pool_kernel<T>, dim3(3 * wg_per_tensor), dim3(256), 0, s, q, k, v, pq, pk,
-                       pv, total_blocks, wg_per_tensor, do2, g.pyr_off[2]);
+    const TokMap tm{g.order, g.log2S};
+    if (g.order == 0)
+        hipLaunchKernelGGL((pool_kernel<T, 0>), dim3(3 * wg_per_tensor), dim3(256), 0, s, q, k, v,
+                           pq, pk, pv, total_blocks, wg_per_tensor, do2, g.pyr_off[2], g.n[1], tm);
+    else
+        hipLaunchKernelGGL((pool_kernel<T, 1>), dim3(3 * wg_per_tensor), dim3(256), 0, s, q, k, v,
+                           pq, pk, pv, total_blocks, wg_per_tensor, do2, g.pyr_off[2], g.n[1], tm);
 }
 
 hipError_t launch_pool(const Geometry &g, const void *q, const void *k, const void *v, float *pq,

@@ -25,7 +25,7 @@ class Problem(ctypes.Structure):
     _fields_ = [("batch", _c_i32), ("heads", _c_i32), ("seq_len", _c_i32), ("head_dim", _c_i32),
                 ("block", _c_i32), ("levels", _c_i32), ("topk", _c_i32), ("enrich", _c_i32),
                 ("dtype", _c_i32), ("grad_dtype", _c_i32), ("scale", _c_f32),
-                ("drop_covered", _c_i32)]
+                ("drop_covered", _c_i32), ("token_order", _c_i32)]
 
 
 class Sizes(ctypes.Structure):
@@ -77,10 +77,12 @@ lib = _load()
 
 
 def problem(batch, heads, seq_len, head_dim=64, block=16, levels=2, topk=8, enrich=-1,
-            dtype=torch.bfloat16, grad_dtype=torch.float32, scale=0.0, drop_covered=True) -> Problem:
+            dtype=torch.bfloat16, grad_dtype=torch.float32, scale=0.0, drop_covered=True,
+            token_order=0) -> Problem:
     code = {torch.float32: LLSA_F32, torch.bfloat16: LLSA_BF16}
     return Problem(batch, heads, seq_len, head_dim, block, levels, topk, enrich,
-                   code.get(dtype, -1), code.get(grad_dtype, -1), float(scale), int(drop_covered))
+                   code.get(dtype, -1), code.get(grad_dtype, -1), float(scale), int(drop_covered),
+                   int(token_order))
 
 
 def _ptr(t):

@@ -66,6 +66,12 @@ typedef struct llsa_problem {
     int32_t drop_covered; /* 1: leave out a coarse pick whose level-1 children are all
                              fine picks of the query block (then K = all blocks is exactly
                              dense attention); 0: keep every coarse pick                  */
+    int32_t token_order;  /* 0: the sequence as stored.  1: seq_len = S*S pixels of an
+                             image stored in raster order (S a power of two); the method
+                             runs on the nested 2^i x 2^i patch sequence (Z order), so a
+                             level-l token pools a 4^l x 4^l patch.  Q, K, V, O, dO, dQ,
+                             dK, dV and lse stay in raster order; pyramids, index lists
+                             and CSR are in patch-sequence order                          */
 } llsa_problem;
 
 typedef struct llsa_sizes {

@@ -31,11 +31,32 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
+def patch_order(N):
+    """Storage row (raster order of an S x S image) of every position of the
+    nested-patch sequence: position t has x in its even bits and y in its odd
+    bits (Z order), so 4^i consecutive positions form a 2^i x 2^i patch."""
+    S = int(round(N ** 0.5))
+    assert S * S == N and S & (S - 1) == 0
+    t = np.arange(N, dtype=np.int64)
+    x = np.zeros(N, dtype=np.int64)
+    y = np.zeros(N, dtype=np.int64)
+    for b in range(S.bit_length()):
+        x |= ((t >> (2 * b)) & 1) << b
+        y |= ((t >> (2 * b + 1)) & 1) << b
+    return y * S + x
+
+
+def seq_perm(c):
+    """Storage row of each sequence position for case c."""
+    return patch_order(c.N) if c.token_order else np.arange(c.N)
+
+
 class Case:
     """One problem: seeded inputs on the host, a problem descriptor, flags."""
 
     def __init__(self, batch, heads, N, dtype, L_, K, Le=-1, q=None, k=None, v=None, dout=None,
-                 backward=True, drop_covered=True, grad_dtype=torch.float32, seed=0, sinus=False):
+                 backward=True, drop_covered=True, grad_dtype=torch.float32, seed=0, sinus=False,
+                 token_order=0):
         from hierarchical_top_sparse_mean_amd.inputs import make_inputs
         self.batch, self.heads, self.N, self.dtype, self.L, self.K = batch, heads, N, dtype, L_, K
         self.Le = L_ - 1 if Le < 0 else Le
@@ -47,7 +68,9 @@ class Case:
         self.v = gv if v is None else v.to(dtype)
         self.dout = (gd if dout is None else dout.to(dtype)) if backward else None
         self.scale = 1.0 / 8.0
-        self.p = L.problem(batch, heads, N, 64, 16, L_, K, Le, dtype, grad_dtype, 0.0, drop_covered)
+        self.token_order = token_order
+        self.p = L.problem(batch, heads, N, 64, 16, L_, K, Le, dtype, grad_dtype, 0.0, drop_covered,
+                           token_order)
 
     @property
     def bh(self):
@@ -92,28 +115,30 @@ def run_gpu(c: Case):
                         c.dout.cuda(), B.dq, B.dk, B.dv, B.ws, B.ws.numel())
     torch.cuda.synchronize()
     bh, N = c.bh, c.N
+    perm = seq_perm(c)   # token tensors are compared in sequence order
     res["pyr_q"] = [to_np(B.pyramid_level(B.pyr_q, l)) for l in range(1, c.L + 1)]
     res["pyr_k"] = [to_np(B.pyramid_level(B.pyr_k, l)) for l in range(1, c.L + 1)]
     res["pyr_v"] = [to_np(B.pyramid_level(B.pyr_v, l)) for l in range(1, c.L + 1)]
     res["idx"] = [B.index_level(l).cpu().numpy() for l in range(1, c.L + 1)]
-    res["o"] = to_np(B.o).reshape(bh, N, 64)
-    res["lse"] = to_np(B.lse).reshape(bh, N)
+    res["o"] = to_np(B.o).reshape(bh, N, 64)[:, perm]
+    res["lse"] = to_np(B.lse).reshape(bh, N)[:, perm]
     if c.backward:
         res["csr"] = [tuple(t.cpu().numpy() for t in B.csr_level(l)) for l in range(1, s.enrich + 2)]
-        res["dq"] = to_np(B.dq).reshape(bh, N, 64)
-        res["dk"] = to_np(B.dk).reshape(bh, N, 64)
-        res["dv"] = to_np(B.dv).reshape(bh, N, 64)
+        res["dq"] = to_np(B.dq).reshape(bh, N, 64)[:, perm]
+        res["dk"] = to_np(B.dk).reshape(bh, N, 64)[:, perm]
+        res["dv"] = to_np(B.dv).reshape(bh, N, 64)[:, perm]
     return res
 
 
 def run_oracle(c: Case):
     bh, N = c.bh, c.N
-    q = c.q.double().numpy().reshape(bh, N, 64)
-    k = c.k.double().numpy().reshape(bh, N, 64)
-    v = c.v.double().numpy().reshape(bh, N, 64)
+    perm = seq_perm(c)   # the oracle runs on the sequence (patch order: permuted rows)
+    q = c.q.double().numpy().reshape(bh, N, 64)[:, perm]
+    k = c.k.double().numpy().reshape(bh, N, 64)[:, perm]
+    v = c.v.double().numpy().reshape(bh, N, 64)[:, perm]
     r = O.forward_all(q, k, v, 16, c.L, c.K, c.Le, c.scale, c.drop)
     if c.backward:
-        d = c.dout.double().numpy().reshape(bh, N, 64)
+        d = c.dout.double().numpy().reshape(bh, N, 64)[:, perm]
         r["dq"], r["dk"], r["dv"] = O.attn_bwd(q, k, v, r["pyr_k"], r["pyr_v"], r["idx"], d, 16,
                                                c.K, c.Le, c.scale, c.drop)
         r["csr"] = [O.transpose(r["idx"][l - 1], N // 16 ** l) for l in range(1, c.Le + 2)]

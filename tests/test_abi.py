@@ -71,6 +71,8 @@ def test_picks_clamped_to_candidates():
     (dict(head_dim=128), L.LLSA_ERR_UNSUPPORTED),
     (dict(block=32, seq_len=32 * 32 * 4), L.LLSA_ERR_UNSUPPORTED),
     (dict(topk=33), L.LLSA_ERR_UNSUPPORTED),
+    (dict(token_order=2), L.LLSA_ERR_INVALID),
+    (dict(token_order=1, seq_len=2048), L.LLSA_ERR_INVALID),    # not a square image
     (dict(levels=7, seq_len=16 ** 5), L.LLSA_ERR_UNSUPPORTED),
 ])
 def test_sizes_query_rejects(kw, status):
@@ -141,3 +143,18 @@ def test_sinusoid_values():
         float(torch.sin(torch.tensor(2 * torch.pi * 4 / 16 + 2 * torch.pi / 64))), abs=1e-6)
     # constant along a raster row for the (0, 1) channels
     assert torch.allclose(s[16:32, 0], s[16, 0].expand(16))
+
+
+def test_patch_order_is_a_nested_permutation():
+    # the 2D patch order used by the parity tests: a permutation whose runs of
+    # 4^i positions are 2^i x 2^i patches of the raster image
+    from parity_util import patch_order
+    N, S = 4096, 64
+    perm = patch_order(N)
+    assert sorted(perm.tolist()) == list(range(N))
+    for side in (2, 4, 16):
+        runs = perm.reshape(-1, side * side)
+        ys, xs = runs // S, runs % S
+        assert ((ys.max(1) - ys.min(1)) == side - 1).all()
+        assert ((xs.max(1) - xs.min(1)) == side - 1).all()
+    assert perm[:4].tolist() == [0, 1, S, S + 1]

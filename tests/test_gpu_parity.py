@@ -20,7 +20,7 @@ from hierarchical_top_sparse_mean_amd import llsa as L  # noqa: E402
 from hierarchical_top_sparse_mean_amd.inputs import WORKLOADS  # noqa: E402
 from oracle import oracle as O  # noqa: E402
 
-from parity_util import Case, check_case, check_csr_valid, run_gpu  # noqa: E402
+from parity_util import Case, check_case, check_csr_valid, run_gpu, to_np  # noqa: E402
 
 
 def _log(msg):
@@ -58,12 +58,16 @@ EDGE = [
     (1, 1, 2048, torch.float32, 2, 24, 1, True, {}),
     (1, 2, 4096, torch.bfloat16, 2, 3, 1, True, {"drop_covered": False}),
     (2, 2, 2048, torch.bfloat16, 2, 4, 1, True, {"grad_dtype": torch.bfloat16}),
+    (1, 2, 4096, torch.bfloat16, 2, 8, 1, True, {"token_order": 1}),   # 2D patch order
+    (1, 2, 4096, torch.bfloat16, 2, 16, 1, True, {"token_order": 1}),  # patch order, generic path
+    (1, 2, 1024, torch.float32, 2, 2, 1, True, {"token_order": 1}),
+    (1, 2, 4096, torch.bfloat16, 3, 2, 2, True, {"token_order": 1}),
     (1, 1, 256, torch.bfloat16, 2, 16, 1, True, {}),       # K = all blocks (dense reduction)
     (1, 1, 256, torch.float32, 2, 16, 1, True, {}),
 ]
 
 
-@pytest.mark.parametrize("case", EDGE, ids=[f"b{e[0]}h{e[1]}N{e[2]}{str(e[3])[6:]}L{e[4]}K{e[5]}Le{e[6]}{'-'.join(e[8])}" for e in EDGE])
+@pytest.mark.parametrize("case", EDGE, ids=[f"b{e[0]}h{e[1]}N{e[2]}{str(e[3])[6:]}L{e[4]}K{e[5]}Le{e[6]}{'-'.join(f'{k}{v}' for k, v in e[8].items())}" for e in EDGE])
 def test_edge_parity(case):
     b, h, N, dt, L_, K, Le, bwd, extra = case
     _log(f"[parity] edge {case}")
@@ -153,6 +157,26 @@ def test_transpose_parity(nb, rows, k, cols):
     assert np.array_equal(ptr.cpu().numpy(), ptr_o)
     assert np.array_equal(col.cpu().numpy(), col_o)
     check_csr_valid(idx, ptr.cpu().numpy(), col.cpu().numpy())
+
+
+def test_patch_order_pools_image_patches():
+    # in 2D patch order a level-1 token is the mean of a 4x4 pixel patch and a
+    # level-2 token of a 16x16 patch, read from the raster-stored image
+    _log("[parity] patch-order pooling")
+    from parity_util import patch_order
+    N, S = 4096, 64
+    c = Case(1, 2, N, torch.float32, 2, 2, 1, backward=False, token_order=1)
+    B = L.Buffers(c.p, backward=False)
+    L.llsa_pool(c.p, c.q.cuda(), c.k.cuda(), c.v.cuda(), B.pyr_q, B.pyr_k, B.pyr_v)
+    torch.cuda.synchronize()
+    img = c.k.double().numpy().reshape(2, S, S, 64)
+    for l, side in ((1, 4), (2, 16)):
+        n = N // 16 ** l
+        pos = patch_order(n)            # position -> raster index in the (S/side)^2 grid
+        grid = img.reshape(2, S // side, side, S // side, side, 64).mean(axis=(2, 4))
+        want = grid.reshape(2, n, 64)[:, pos]
+        got = to_np(B.pyramid_level(B.pyr_k, l)).reshape(2, n, 64)
+        assert np.abs(got - want).max() <= 1e-5, l
 
 
 def test_dense_comparator_matches_oracle_dense():

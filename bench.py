@@ -178,6 +178,49 @@ def sweep_workloads():
     return out
 
 
+def transpose_scaling(L, dev, reps):
+    """Level-1 key-major lists from real selections at growing N: the sparse
+    transpose (count / scan / fill) against the dense bit-mask baseline."""
+    import torch
+    from hierarchical_top_sparse_mean_amd.inputs import Workload, workload_inputs
+    for N, heads, levels in ((4096, 16, 2), (16384, 16, 2), (65536, 16, 2), (262144, 4, 3),
+                             (1048576, 1, 3)):
+        w = Workload(f"n{N}", 1, heads, N, 64, torch.bfloat16, 16, levels, 8, levels - 1, False, True)
+        q, k, v, _ = workload_inputs(w)
+        q, k, v = q.to(dev), k.to(dev), v.to(dev)
+        p = L.problem(1, heads, N, levels=levels, topk=8, enrich=levels - 1)
+        B = L.Buffers(p, backward=True)
+        L.llsa_pool(p, q, k, v, B.pyr_q, B.pyr_k, B.pyr_v)
+        L.llsa_select(p, B.pyr_q, B.pyr_k, B.idx)
+        n1, k1 = B.s.level_tokens[1], B.s.level_k[1]
+        ptr, col = B.csr_level(1)
+        mws = L.llsa_index_transpose_mask_workspace(heads, n1, n1)
+        mw = torch.empty(mws, dtype=torch.uint8, device=dev)
+        runs = {
+            "csr": lambda: L.llsa_index_transpose(heads, n1, k1, n1, B.index_level(1), ptr, col,
+                                                  B.tws, B.tws_bytes),
+            "mask": lambda: L.llsa_index_transpose_mask(heads, n1, k1, n1, B.index_level(1), ptr, col,
+                                                        mw, mws),
+        }
+        out = {"transpose_scaling_tokens": N, "heads": heads, "key_blocks": n1, "picks": heads * n1 * k1,
+               "mask_bytes": mws}
+        for name, f in runs.items():
+            f()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            out[name + "_us"] = round(us, 2)
+            out[name + "_ns_per_pick"] = round(us * 1e3 / (heads * n1 * k1), 4)
+        print(json.dumps(out), flush=True)
+        del q, k, v, B, mw
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +232,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--sweep", action="store_true",
                     help="time every workload and variation (one JSON line each) instead of the bench line")
+    ap.add_argument("--transpose-scaling", action="store_true",
+                    help="time the level-1 index transpose against the dense-mask baseline for "
+                         "4096 .. 1048576 tokens (one JSON line each)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -222,6 +268,9 @@ def main():
                              for c, v in pc.items()}}
             print(json.dumps(rec), flush=True)
             torch.cuda.empty_cache()
+        return
+    if args.transpose_scaling:
+        transpose_scaling(L, dev, args.steps)
         return
     if args.copy_probe:
         n = args.copy_probe * (1 << 20) // 4

@@ -167,12 +167,30 @@ int llsa_index_transpose(int32_t n_batch, int32_t n_rows, int32_t k, int32_t n_c
                          size_t workspace_bytes, void *stream) {
     if (n_batch <= 0 || n_rows <= 0 || k <= 0 || n_cols <= 0) return LLSA_ERR_INVALID;
     if ((int64_t)n_rows * k >= ((int64_t)1 << 31) / n_batch) return LLSA_ERR_UNSUPPORTED;
-    if (n_cols > 32768) return LLSA_ERR_UNSUPPORTED;
+    if (n_cols > (1 << 24) || n_batch > 65535) return LLSA_ERR_UNSUPPORTED;
     if (!aligned16(idx) || !aligned16(csr_ptr) || !aligned16(csr_col)) return LLSA_ERR_INVALID;
     const size_t need = llsa::transpose_workspace_bytes(n_batch, n_rows, k, n_cols);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LLSA_ERR_WORKSPACE;
     return status_of(llsa::launch_transpose(n_batch, n_rows, k, n_cols, idx, csr_ptr, csr_col,
                                             workspace, (hipStream_t)stream));
+}
+
+size_t llsa_index_transpose_mask_workspace(int32_t n_batch, int32_t n_rows, int32_t n_cols) {
+    if (n_batch <= 0 || n_rows <= 0 || n_cols <= 0) return 0;
+    return llsa::transpose_mask_workspace_bytes(n_batch, n_rows, n_cols);
+}
+
+int llsa_index_transpose_mask(int32_t n_batch, int32_t n_rows, int32_t k, int32_t n_cols,
+                              const int32_t *idx, int32_t *csr_ptr, int32_t *csr_col,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+    if (n_batch <= 0 || n_rows <= 0 || k <= 0 || n_cols <= 0) return LLSA_ERR_INVALID;
+    if ((int64_t)n_rows * k >= ((int64_t)1 << 31) / n_batch) return LLSA_ERR_UNSUPPORTED;
+    if ((int64_t)n_batch * n_cols >= ((int64_t)1 << 31) || n_cols > (1 << 24)) return LLSA_ERR_UNSUPPORTED;
+    if (!aligned16(idx) || !aligned16(csr_ptr) || !aligned16(csr_col)) return LLSA_ERR_INVALID;
+    const size_t need = llsa::transpose_mask_workspace_bytes(n_batch, n_rows, n_cols);
+    if (workspace == nullptr || workspace_bytes < need) return LLSA_ERR_WORKSPACE;
+    return status_of(llsa::launch_transpose_mask(n_batch, n_rows, k, n_cols, idx, csr_ptr, csr_col,
+                                                 workspace, (hipStream_t)stream));
 }
 
 int llsa_attn_bwd(const llsa_problem *p, const void *q, const void *k, const void *v,

@@ -38,6 +38,9 @@ hipError_t launch_attn_fwd(const Geometry &g, const void *q, const void *k, cons
 size_t transpose_workspace_bytes(int nb, int rows, int k, int cols);
 hipError_t launch_transpose(int nb, int rows, int k, int cols, const int32_t *idx,
                             int32_t *ptr, int32_t *col, void *ws, hipStream_t s);
+size_t transpose_mask_workspace_bytes(int nb, int rows, int cols);
+hipError_t launch_transpose_mask(int nb, int rows, int k, int cols, const int32_t *idx,
+                                 int32_t *ptr, int32_t *col, void *ws, hipStream_t s);
 size_t bwd_workspace_bytes(const Geometry &g);
 hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, const void *v,
                            const float *pk, const float *pv, const int32_t *idx,

@@ -57,6 +57,10 @@ def _load():
     L.llsa_index_transpose_workspace.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32]
     L.llsa_index_transpose_workspace.restype = _c_sz
     L.llsa_index_transpose.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _c_sz, _vp]
+    L.llsa_index_transpose_mask_workspace.argtypes = [_c_i32, _c_i32, _c_i32]
+    L.llsa_index_transpose_mask_workspace.restype = _c_sz
+    L.llsa_index_transpose_mask.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _c_sz,
+                                            _vp]
     L.llsa_attn_bwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, _c_sz, _vp]
     L.llsa_dense_attn_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -68,7 +72,7 @@ def _load():
     L.llsa_strerror.restype = ctypes.c_char_p
     for name in ("llsa_sizes_query", "llsa_pool", "llsa_select", "llsa_attn_fwd",
                  "llsa_index_transpose", "llsa_attn_bwd", "llsa_dense_attn_fwd",
-                 "llsa_dense_attn_bwd"):
+                 "llsa_dense_attn_bwd", "llsa_index_transpose_mask"):
         getattr(L, name).restype = ctypes.c_int
     return L
 
@@ -136,6 +140,18 @@ def llsa_index_transpose(n_batch, n_rows, k, n_cols, idx, csr_ptr, csr_col, work
            lib.llsa_index_transpose(n_batch, n_rows, k, n_cols, _ptr(idx), _ptr(csr_ptr),
                                     _ptr(csr_col), _ptr(workspace), workspace_bytes,
                                     _stream(stream)))
+
+
+def llsa_index_transpose_mask_workspace(n_batch, n_rows, n_cols) -> int:
+    return int(lib.llsa_index_transpose_mask_workspace(n_batch, n_rows, n_cols))
+
+
+def llsa_index_transpose_mask(n_batch, n_rows, k, n_cols, idx, csr_ptr, csr_col, workspace,
+                              workspace_bytes, stream=None):
+    _check("llsa_index_transpose_mask",
+           lib.llsa_index_transpose_mask(n_batch, n_rows, k, n_cols, _ptr(idx), _ptr(csr_ptr),
+                                         _ptr(csr_col), _ptr(workspace), workspace_bytes,
+                                         _stream(stream)))
 
 
 def llsa_attn_bwd(p, q, k, v, pyr_k, pyr_v, idx, csr_ptr, csr_col, o, lse, dout, dq, dk, dv,

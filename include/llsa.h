@@ -146,7 +146,8 @@ int llsa_attn_fwd(const llsa_problem *p, const void *q, const void *k, const voi
  *      so ptr[n_cols] = n_rows * k; csr_col [n_batch, n_rows * k]: the rows
  *      that picked key c, ascending, at csr_col[ptr[c] .. ptr[c+1]).
  * workspace: at least llsa_index_transpose_workspace(...) bytes of device
- *      memory (per-range key histograms and a staging copy of csr_col).
+ *      memory (per-range key histograms and key totals).
+ * Limits: n_cols <= 2^24 and n_batch <= 65535 (LLSA_ERR_UNSUPPORTED).
  * An index outside [0, n_cols) is skipped: it is not listed, and ptr[n_cols]
  * then counts only the listed picks.  The output is deterministic.
  */
@@ -155,6 +156,20 @@ size_t llsa_index_transpose_workspace(int32_t n_batch, int32_t n_rows, int32_t k
 int llsa_index_transpose(int32_t n_batch, int32_t n_rows, int32_t k, int32_t n_cols,
                          const int32_t *idx, int32_t *csr_ptr, int32_t *csr_col,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Baseline for comparison with llsa_index_transpose: the same output built
+ * from a dense bit mask of n_rows x n_cols per matrix (set every pick's bit,
+ * then read every key's column), the mask-based route whose cost grows
+ * with n_rows * n_cols (explainer "Step 4": mask-based methods bring back
+ * quadratic overhead).  Same arguments and output; rows ascend within a key.
+ * workspace: at least llsa_index_transpose_mask_workspace(n_batch, n_rows,
+ *      n_cols) bytes (the mask and per-key counts).
+ */
+size_t llsa_index_transpose_mask_workspace(int32_t n_batch, int32_t n_rows, int32_t n_cols);
+int llsa_index_transpose_mask(int32_t n_batch, int32_t n_rows, int32_t k, int32_t n_cols,
+                              const int32_t *idx, int32_t *csr_ptr, int32_t *csr_col,
+                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Backward pass of llsa_attn_fwd for the loss <O, dO> with the picks held

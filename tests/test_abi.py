@@ -102,7 +102,7 @@ def test_entry_points_validate_before_launch():
     assert lib.llsa_select(gp, fake, None, fake, None) == L.LLSA_ERR_INVALID
     assert lib.llsa_attn_fwd(bp, *([fake] * 8), None) == L.LLSA_ERR_UNSUPPORTED
     assert lib.llsa_attn_fwd(gp, *([fake] * 7), mis, None) == L.LLSA_ERR_INVALID
-    assert lib.llsa_index_transpose(1, 10, 2, 40000, fake, fake, fake, None, 0, None) == L.LLSA_ERR_UNSUPPORTED
+    assert lib.llsa_index_transpose(1, 10, 2, 1 << 25, fake, fake, fake, None, 0, None) == L.LLSA_ERR_UNSUPPORTED
     assert lib.llsa_index_transpose(0, 10, 2, 10, fake, fake, fake, None, 0, None) == L.LLSA_ERR_INVALID
     assert lib.llsa_index_transpose(1, 10, 2, 10, None, fake, fake, None, 0, None) == L.LLSA_ERR_INVALID
     s = L.llsa_sizes_query(good)

@@ -135,7 +135,8 @@ def test_deterministic_bitwise():
 
 # ------------------------------------------------------------- transpose --
 @pytest.mark.parametrize("nb,rows,k,cols", [(3, 100, 8, 100), (2, 4096, 8, 4096), (1, 37, 5, 23),
-                                            (4, 64, 1, 64), (1, 16384, 8, 32768), (2, 50, 16, 1000)])
+                                            (4, 64, 1, 64), (1, 16384, 8, 32768), (2, 50, 16, 1000),
+                                            (1, 4096, 8, 70000)])
 def test_transpose_parity(nb, rows, k, cols):
     _log(f"[parity] transpose {nb} {rows} {k} {cols}")
     rng = np.random.default_rng(rows * 31 + k)
@@ -157,6 +158,26 @@ def test_transpose_parity(nb, rows, k, cols):
     assert np.array_equal(ptr.cpu().numpy(), ptr_o)
     assert np.array_equal(col.cpu().numpy(), col_o)
     check_csr_valid(idx, ptr.cpu().numpy(), col.cpu().numpy())
+
+
+@pytest.mark.parametrize("nb,rows,k,cols", [(3, 100, 8, 100), (2, 4096, 8, 4096), (1, 37, 5, 23),
+                                            (1, 4096, 8, 32768)])
+def test_mask_transpose_baseline_matches_oracle(nb, rows, k, cols):
+    # the dense-mask baseline must build exactly the same key-major lists
+    _log(f"[parity] mask transpose {nb} {rows} {k} {cols}")
+    rng = np.random.default_rng(rows * 7 + k)
+    idx = np.stack([np.stack([np.sort(rng.choice(cols, k, replace=False)) for _ in range(rows)])
+                    for _ in range(nb)]).astype(np.int32)
+    ptr_o, col_o = O.transpose(idx, cols)
+    d_idx = torch.from_numpy(idx).cuda()
+    ptr = torch.empty((nb, cols + 1), dtype=torch.int32, device="cuda")
+    col = torch.empty((nb, rows * k), dtype=torch.int32, device="cuda")
+    ws_bytes = L.llsa_index_transpose_mask_workspace(nb, rows, cols)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    L.llsa_index_transpose_mask(nb, rows, k, cols, d_idx, ptr, col, ws, ws_bytes)
+    torch.cuda.synchronize()
+    assert np.array_equal(ptr.cpu().numpy(), ptr_o)
+    assert np.array_equal(col.cpu().numpy(), col_o)
 
 
 def test_patch_order_pools_image_patches():

@@ -432,6 +432,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
 constexpr int kFastK1 = 8;
 constexpr int kFastTiles = 4 * kFastK1;   // fine tiles per wave
 constexpr int kPtS = 20;                  // float row stride of the P / dS exchange
+constexpr int kOutS = 68;                 // float row stride of a staged 16 x 64 output tile
 
 template <int ORD>
 __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
@@ -444,6 +445,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
     __shared__ __attribute__((aligned(16))) char smem[kTileBytes > kRedBytes ? kTileBytes : kRedBytes];
     __shared__ float cbias[kBlock];
     __shared__ __attribute__((aligned(16))) float lds_pt[4][2][kBlock * kPtS];  // coarse P, dS entry-major
+    __shared__ __attribute__((aligned(16))) float lds_out[4][kBlock * kOutS];   // dQ rows
     typedef __bf16 Tile[kTE];
     Tile *lds_k = reinterpret_cast<Tile *>(smem);
     Tile *lds_v = lds_k + 4;
@@ -646,10 +648,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
             dkc[dt] = mfma_bf16_32(d2cat, cat8(qT, qT), dkc[dt]);
             dvc[dt] = mfma_bf16_32(p2cat, cat8(dT, dT), dvc[dt]);
         }
+        // dQ (lane: query c16, dims 16 dt + 4 g ..) passes through LDS so
+        // that every store writes whole rows (lane l: row l / 16 + 4 it)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
-            store_grad4(dq, head_off + trow(ib0 + w * 4 + jb, c16) + 16 * dt + 4 * g,
-                        (accA[dt] - Dq * accB[dt]) * a.scale, a.grad_bf16);
+            *reinterpret_cast<f32x4 *>(&lds_out[w][c16 * kOutS + 16 * dt + 4 * g]) =
+                (accA[dt] - Dq * accB[dt]) * a.scale;
+        wave_lds_sync();
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int r = g + 4 * it;
+            store_grad4(dq, head_off + trow(ib0 + w * 4 + jb, r) + 4 * c16,
+                        *reinterpret_cast<const f32x4 *>(&lds_out[w][r * kOutS + 4 * c16]), a.grad_bf16);
+        }
     }
     // ---- reduce the coarse partials over the 4 waves
     __syncthreads();
@@ -760,6 +771,7 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
     __shared__ __attribute__((aligned(16))) __bf16 lds_q[kTE];
     __shared__ __attribute__((aligned(16))) __bf16 lds_do[kTE];
     __shared__ __attribute__((aligned(16))) float lds_ld[2 * kBlock];   // lse, D of the block's queries
+    __shared__ __attribute__((aligned(16))) float lds_out[kBlock * kOutS];
     const int lane = lane_id();
     const int g = lane >> 4, c16 = lane & 15;
     const int64_t kb = xcd_remap(blockIdx.x, gridDim.x);
@@ -769,20 +781,23 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
     // element offset (within the head) of row r of sequence block b
     auto trow = [&](int b, int r) { return (int64_t)tok_row_o<ORD>(a.tm, b * kBlock + r) * kHeadDim; };
-    const __bf16 *krow = k + head_off + trow(f, c16);
-    const __bf16 *vrow = v + head_off + trow(f, c16);
-    const bf16x8 kb0 = load_bf16x8(krow + 8 * g), kb1 = load_bf16x8(krow + 32 + 8 * g);
-    const bf16x8 vb0 = load_bf16x8(vrow + 8 * g), vb1 = load_bf16x8(vrow + 32 + 8 * g);
+    const int32_t *P = csr_ptr + (int64_t)h * (a.n1 + 1);
+    const int32_t *C = csr_col + (int64_t)h * a.n1 * a.K1;
+    const int e0 = __builtin_amdgcn_readfirstlane(P[f]), e1 = __builtin_amdgcn_readfirstlane(P[f + 1]);
     f32x4 dka[4], dva[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
         dka[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         dva[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // about half of the key blocks are picked by no query block: they only
+    // receive the pooled-level gradients below and never read K or V
+    if (e1 > e0) {
+    const __bf16 *krow = k + head_off + trow(f, c16);
+    const __bf16 *vrow = v + head_off + trow(f, c16);
+    const bf16x8 kb0 = load_bf16x8(krow + 8 * g), kb1 = load_bf16x8(krow + 32 + 8 * g);
+    const bf16x8 vb0 = load_bf16x8(vrow + 8 * g), vb1 = load_bf16x8(vrow + 32 + 8 * g);
     const int rofs = (4 * g + (c16 >> 2)) * kTS + 4 * (c16 & 3);
-    const int32_t *P = csr_ptr + (int64_t)h * (a.n1 + 1);
-    const int32_t *C = csr_col + (int64_t)h * a.n1 * a.K1;
-    const int e0 = __builtin_amdgcn_readfirstlane(P[f]), e1 = __builtin_amdgcn_readfirstlane(P[f + 1]);
     // Per query block: its Q / dO tiles loaded as whole 128-byte rows per
     // instruction (lane l: rows l / 8 and l / 8 + 8, 16-byte chunk l % 8),
     // which pass through LDS before the MFMA operand rows are read back; and
@@ -860,26 +875,43 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
         for (int r = 0; r < kDkvDepth - 1; ++r)
             if (j + r < cnt) compute(R[r]);
     }
-    // C layout: lane (dim 16dt + c16, keys 4g+i); add pooled-level gradients / B^l
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-        const int dim = 16 * dt + c16;
-        float ck = 0.f, cv = 0.f;
-        float inv = 1.f;
+    }
+    // Pooled-level gradients, spread back with weight 1/B^l: every key row of
+    // the block gets the same 64 values.  Lane l covers dims 4 (l % 16) .. +3.
+    const int oc = 4 * c16;
+    f32x4 ck = f32x4{0.f, 0.f, 0.f, 0.f}, cv = ck;
+    {
+        float inv = 1.f / kBlock;
         for (int j = 0; j < a.ncl; ++j) {
             inv *= (1.0f / kBlock);
-            const int c = f / a.cl_span[j];
-            const int64_t off = a.cl_grad_off[j] + ((int64_t)h * a.cl_n[j] + c) * kHeadDim + dim;
-            ck += ws.dpk[off] * (inv * (1.0f / kBlock));
-            cv += ws.dpv[off] * (inv * (1.0f / kBlock));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t off = head_off + trow(f, 4 * g + i) + dim;
-            store_grad1(dk, off, dka[dt][i] * a.scale + ck, a.grad_bf16);
-            store_grad1(dv, off, dva[dt][i] + cv, a.grad_bf16);
+            const int64_t off = a.cl_grad_off[j] + ((int64_t)h * a.cl_n[j] + f / a.cl_span[j]) * kHeadDim + oc;
+            ck += *reinterpret_cast<const f32x4 *>(ws.dpk + off) * inv;
+            cv += *reinterpret_cast<const f32x4 *>(ws.dpv + off) * inv;
         }
     }
+    // The accumulators hold lane (dim 16dt + c16, keys 4g + i); they pass
+    // through LDS so that every store writes whole rows (lane l: row
+    // l / 16 + 4 it, dims 4 (l % 16) .. +3).
+    auto store_tile = [&](const f32x4 *acc, float mul, f32x4 add, void *dst) {
+        wave_lds_sync();
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lds_out[(4 * g + i) * kOutS + 16 * dt + c16] = acc[dt][i];
+        wave_lds_sync();
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int r = g + 4 * it;
+            const f32x4 x = *reinterpret_cast<const f32x4 *>(&lds_out[r * kOutS + oc]) * mul + add;
+            const int64_t off = head_off + trow(f, r) + oc;
+            if (a.grad_bf16)
+                *reinterpret_cast<u32x2 *>((__bf16 *)dst + off) = __builtin_bit_cast(u32x2, to_bf16x4(x));
+            else
+                *reinterpret_cast<f32x4 *>((float *)dst + off) = x;
+        }
+    };
+    store_tile(dka, a.scale, ck, dk);
+    store_tile(dva, 1.0f, cv, dv);
 }
 
 // ================================================================ f32 path

@@ -427,16 +427,20 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
         for (int dt = 0; dt < 4; ++dt)
             oacc[dt] = mfma_bf16_16(lds_read_tr4(cv + rofs + 16 * dt), pcb, oacc[dt]);
     }
-    // ---- normalise and store
+    // ---- normalise and store: O (lane: query c16, dims 16 dt + 4 g ..)
+    // passes through the free V slot so that the stores write whole rows
     lsum = sum4_groups(lsum);
     const float inv = 1.0f / lsum;
-    __bf16 *orow = o + head_off + trow(ib, c16) + 4 * g;
+    wave_lds_sync();
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
         const f32x4 r = oacc[dt] * inv;
         const bf16x4 rb = to_bf16x4(f32x4{r[0], r[1], r[2], r[3]});
-        *reinterpret_cast<u32x2 *>(orow + 16 * dt) = __builtin_bit_cast(u32x2, rb);
+        *reinterpret_cast<u32x2 *>(vw + c16 * kVStride + 16 * dt + 4 * g) = __builtin_bit_cast(u32x2, rb);
     }
+    wave_lds_sync();
+    store_bf16x8(o + head_off + trow(ib, lr) + lc, load_bf16x8(vw + lr * kVStride + lc));
+    store_bf16x8(o + head_off + trow(ib, lr + 8) + lc, load_bf16x8(vw + (lr + 8) * kVStride + lc));
     if (g == 0) lse[(int64_t)h * a.N + tok_row_o<ORD>(a.tm, ib * kBlock + c16)] = (mx + log2f(lsum)) * kLn2;
 }
 

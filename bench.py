@@ -39,14 +39,15 @@ def algorithmic(w, s):
     idx = sum(bh * n[l] * kl[l] * 4 for l in range(1, L + 1))
     tok = bh * N * d * e
     coarse_pyr = sum(bh * n[l] * d * 4 for l in range(2, Le + 2))
-    nkv = kl[1] * 16 + sum(kl[l] for l in range(2, Le + 2))
+    B = w.block
+    nkv = kl[1] * B + sum(kl[l] for l in range(2, Le + 2))
     out = {}
     out["pool"] = dict(bytes=3 * tok + 3 * pyr, flops=0)
     sel_bytes = 2 * bh * n[L] * d * 4 + bh * n[L] * kl[L] * 4
     sel_flops = 2 * d * bh * n[L] * n[L]
     for l in range(L - 1, 0, -1):
         sel_bytes += 2 * bh * n[l] * d * 4 + bh * n[l + 1] * kl[l + 1] * 4 + bh * n[l] * kl[l] * 4
-        sel_flops += 2 * d * bh * n[l] * kl[l + 1] * 16
+        sel_flops += 2 * d * bh * n[l] * kl[l + 1] * B
     out["select"] = dict(bytes=sel_bytes, flops=sel_flops)
     out["attn_fwd"] = dict(bytes=4 * tok + bh * N * 4 + 2 * coarse_pyr + idx,
                            flops=4 * bh * N * d * nkv)
@@ -160,7 +161,8 @@ def sweep_workloads():
     """The workload table plus the variations the scaling study asks for, all
     at the 65536-token shape unless named otherwise: more pooling steps,
     no enrichment, wider selection, single-level selection (quadratic in the
-    number of blocks) and bfloat16 gradients."""
+    number of blocks), blocks of 64 tokens, bfloat16 gradients and the 2D
+    patch order."""
     from dataclasses import replace
     from hierarchical_top_sparse_mean_amd.inputs import WORKLOADS
     base = WORKLOADS["n65536_bf16"]
@@ -172,6 +174,9 @@ def sweep_workloads():
         (replace(base, name="n65536_L1_K8", levels=1, enrich=0), ""),
         (replace(base, name="n65536_L1_K20", levels=1, topk=20, enrich=0), ""),
         (replace(base, name="n65536_L1_K32", levels=1, topk=32, enrich=0), ""),
+        # blocks of 64 tokens: single level (the large-block single-level setting) and two levels
+        (replace(base, name="n65536_B64_L1_K8", block=64, levels=1, enrich=0), ""),
+        (replace(base, name="n65536_B64_L2_K8", block=64, levels=2, enrich=1), ""),
         (base, "grad_bf16"),
         (base, "patch_order"),   # the image tokens read as nested 2D patches
     ]

@@ -13,9 +13,9 @@ namespace {
 
 bool aligned16(const void *p) { return p != nullptr && (((uintptr_t)p) & 15u) == 0; }
 
-int64_t ipow16(int e) {
+int64_t ipow(int64_t b, int e) {
     int64_t r = 1;
-    while (e-- > 0) r *= 16;
+    while (e-- > 0) r *= b;
     return r;
 }
 
@@ -46,7 +46,7 @@ int make_geometry(const llsa_problem *p, Geometry *g, llsa_sizes *sz) {
     const int L = p->levels;
     const int Le = p->enrich < 0 ? L - 1 : p->enrich;
     if (p->enrich < -1 || Le > L - 1) return LLSA_ERR_INVALID;
-    if (p->head_dim != 64 || p->block != 16) return LLSA_ERR_UNSUPPORTED;
+    if (p->head_dim != 64 || (p->block != 16 && p->block != 64)) return LLSA_ERR_UNSUPPORTED;
     if (p->topk > 32) return LLSA_ERR_UNSUPPORTED;
     const int64_t bh = (int64_t)p->batch * p->heads;
     if (bh * p->seq_len * p->head_dim >= ((int64_t)1 << 40) || bh * p->seq_len >= ((int64_t)1 << 31) ||
@@ -56,14 +56,17 @@ int make_geometry(const llsa_problem *p, Geometry *g, llsa_sizes *sz) {
     memset(g, 0, sizeof(*g));
     g->bh = (int)bh;
     g->N = p->seq_len;
+    g->B = p->block;
+    g->sub = p->block / 16;
+    g->lgB = p->block == 16 ? 4 : 6;
     g->L = L;
     g->K = p->topk;
     g->Le = Le;
     g->n[0] = p->seq_len;
-    for (int l = 1; l <= L; ++l) g->n[l] = (int)(p->seq_len / ipow16(l));
+    for (int l = 1; l <= L; ++l) g->n[l] = (int)(p->seq_len / ipow(p->block, l));
     g->kl[L] = p->topk < g->n[L] ? p->topk : g->n[L];
     for (int l = L - 1; l >= 1; --l) {
-        const int cand = g->kl[l + 1] * 16;
+        const int cand = g->kl[l + 1] * p->block;
         g->kl[l] = p->topk < cand ? p->topk : cand;
     }
     // every level's segment starts on a 64-byte boundary (16 floats / int32s)

@@ -4,18 +4,20 @@
 // Transpose": the key-major index lists drive the key-side gradients, no
 // dense mask is ever formed).
 //
-// Three passes:
-//  A  query-major (one wave per query block, a workgroup per level-2 node):
+// Work is organised by 16-token tiles; a block of B = 64 tokens is 4 tiles
+// that share its picks.  Three passes:
+//  A  query-major (one wave per query tile, a workgroup per 16 tiles, which
+//     lie under one level-2 node):
 //     D = rowsum(dO * O) -- formed in float32 as sum_j P_j dP_j over the
 //     attended set, which is the same value without the rounding of the
 //     stored bf16 O (float32 inputs read O) --, dQ over fine and coarse keys,
 //     and the coarse-token
-//     gradient partials summed over the workgroup's query blocks (every block
+//     gradient partials summed over the workgroup's query tiles (every tile
 //     under one level-2 node shares its coarse picks).
 //  B  coarse reduce: for every pooled token c of level l, sum the partials of
 //     the level-l rows that picked c, read from the CSR of I^(l).
-//  C  key-major (one wave per key block): dK, dV of the block's 16 tokens
-//     from the query blocks in its CSR(I^(1)) segment, plus the pooled-token
+//  C  key-major (one wave per key tile): dK, dV of the tile's 16 tokens
+//     from the query blocks in its block's CSR(I^(1)) segment, plus the pooled-token
 //     gradients of every coarse level spread back through the mean (each of
 //     the B^l tokens under a pooled token receives 1/B^l of its gradient).
 // Accumulation order is fixed everywhere (no float atomics), so results are
@@ -30,9 +32,15 @@ constexpr int kTS = 72;              // bf16 LDS row stride (144 B)
 constexpr int kTE = kBlock * kTS;    // elements of one staged 16 x 64 tile
 
 struct BwdArgs {
-    int bh, N, n1, n2, K1;
+    int bh, N, n1, K1;
+    int sub;      // 16-token tiles per block (B / 16)
+    int nt1;      // tiles per head, n1 * sub
+    int npg;      // partial groups (16 consecutive query tiles) per head
+    float lgB;    // log2(B)
+    float invB;   // 1 / B
     int ncl, ncoarse;
     int cl_n[kMaxCoarseLv], cl_k[kMaxCoarseLv], cl_span[kMaxCoarseLv], cl_entry0[kMaxCoarseLv];
+    int cl_groups[kMaxCoarseLv];          // partial groups under one token of the level
     int64_t cl_idx_off[kMaxCoarseLv], cl_pyr_off[kMaxCoarseLv];
     int64_t cl_ptr_off[kMaxCoarseLv], cl_col_off[kMaxCoarseLv];
     int64_t cl_grad_off[kMaxCoarseLv];   // float offset of level in dpk / dpv
@@ -44,7 +52,7 @@ struct BwdArgs {
 
 struct BwdWs {
     float *D;        // [bh, N]
-    float *partial;  // [bh * n2, ncoarse, 2, 64]
+    float *partial;  // [bh * npg, ncoarse, 2, 64]
     float *dpk;      // coarse-level gradients, per level [bh, n_l, 64]
     float *dpv;
 };
@@ -54,17 +62,22 @@ static BwdArgs make_bwd_args(const Geometry &g) {
     a.bh = g.bh;
     a.N = g.N;
     a.n1 = g.n[1];
-    a.n2 = g.L >= 2 ? g.n[2] : 0;
     a.K1 = g.kl[1];
+    a.sub = g.sub;
+    a.nt1 = g.n[1] * g.sub;
+    a.npg = g.L >= 2 ? a.nt1 / kBlock : 0;   // B^2 / 16 is a multiple of 16
+    a.lgB = (float)g.lgB;
+    a.invB = 1.0f / (float)g.B;
     a.ncl = g.Le < g.L - 1 ? g.Le : g.L - 1;
     a.ncoarse = 0;
     int64_t span = 1, goff = 0;
     for (int j = 0; j < a.ncl; ++j) {
         const int l = j + 2;
-        span *= kBlock;
+        span *= g.B;
         a.cl_n[j] = g.n[l];
         a.cl_k[j] = g.kl[l];
         a.cl_span[j] = (int)span;
+        a.cl_groups[j] = (int)(span * g.sub / kBlock);
         a.cl_entry0[j] = a.ncoarse;
         a.cl_idx_off[j] = g.idx_off[l];
         a.cl_pyr_off[j] = g.pyr_off[l];
@@ -91,7 +104,7 @@ static BwdWs carve_ws(const Geometry &g, const BwdArgs &a, void *ws) {
         return (float *)r;
     };
     w.D = take(sizeof(float) * (size_t)g.bh * g.N);
-    w.partial = take(sizeof(float) * (size_t)g.bh * (size_t)a.n2 * a.ncoarse * 2 * kHeadDim);
+    w.partial = take(sizeof(float) * (size_t)g.bh * (size_t)a.npg * a.ncoarse * 2 * kHeadDim);
     size_t coarse = 0;
     for (int j = 0; j < a.ncl; ++j) coarse += (size_t)g.bh * a.cl_n[j] * kHeadDim;
     w.dpk = take(sizeof(float) * coarse);
@@ -104,7 +117,7 @@ size_t bwd_workspace_bytes(const Geometry &g) {
     size_t total = 0;
     auto add = [&](size_t bytes) { total += (bytes + 255) / 256 * 256; };
     add(sizeof(float) * (size_t)g.bh * g.N);
-    add(sizeof(float) * (size_t)g.bh * (size_t)a.n2 * a.ncoarse * 2 * kHeadDim);
+    add(sizeof(float) * (size_t)g.bh * (size_t)a.npg * a.ncoarse * 2 * kHeadDim);
     size_t coarse = 0;
     for (int j = 0; j < a.ncl; ++j) coarse += (size_t)g.bh * a.cl_n[j] * kHeadDim;
     add(sizeof(float) * coarse);
@@ -126,7 +139,7 @@ __device__ __forceinline__ bool bwd_coarse_entry(const BwdArgs &a, const int32_t
     }
     const int span = a.cl_span[j];
     c = idx[a.cl_idx_off[j] + ((int64_t)h * a.cl_n[j] + ib / span) * a.cl_k[j] + pick];
-    bias = 4.0f * (float)(j + 2);
+    bias = a.lgB * (float)(j + 2);
     if (a.drop && a.K1 >= span) {
         int cov = 0;
         for (int f = 0; f < a.K1; ++f) cov += (fine[f] / span == c) ? 1 : 0;
@@ -218,9 +231,10 @@ __device__ __forceinline__ void load_coarse_tile(const BwdArgs &a, const float *
     }
 }
 
-// One workgroup (4 waves) per level-2 node, every wave 4 of its 16 query
-// blocks in turn; the fine tiles of a block stream through two register sets
-// (the next tile's K / V are in flight while the current one is computed).
+// One workgroup (4 waves) per 16 consecutive query tiles (a level-2 node for
+// B = 16), every wave 4 of them in turn; the fine key tiles of a query tile
+// stream through two register sets (the next tile's K / V are in flight while
+// the current one is computed).
 template <int NCT>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
@@ -243,12 +257,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const int w = wave_id();
     const int lane = lane_id();
     const int g = lane >> 4, c16 = lane & 15;
-    const int groups_per_head = (a.n1 + kBlock - 1) / kBlock;
+    const int groups_per_head = (a.nt1 + kBlock - 1) / kBlock;
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
     const int h = bid / groups_per_head;
     const int G = bid % groups_per_head;
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    const int nft = a.K1 * a.sub;   // fine key tiles: sub-tile t % sub of pick t / sub
 
     f32x4 dkc[NT][4], dvc[NT][4];
 #pragma unroll
@@ -264,15 +279,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
         bf16x8 ka0, ka1, va0, va1;
     };
     for (int jb = 0; jb < 4; ++jb) {
-        const int ib = G * kBlock + w * 4 + jb;
-        if (ib >= a.n1) break;
-        const int64_t row = (int64_t)ib * kBlock + c16;          // sequence position
-        const int64_t srow = tok_row(a.tm, ib * kBlock + c16);   // its storage row
+        const int qt = G * kBlock + w * 4 + jb;   // query tile
+        if (qt >= a.nt1) break;
+        const int ib = qt / a.sub;                // its query block
+        const int64_t row = (int64_t)qt * kBlock + c16;          // sequence position
+        const int64_t srow = tok_row(a.tm, qt * kBlock + c16);   // its storage row
         const __bf16 *qrow = q + head_off + srow * kHeadDim;
         const __bf16 *drow = dout + head_off + srow * kHeadDim;
         const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
         auto load_tile = [&](int t, TileRegs &R) {
-            const int f = __builtin_amdgcn_readfirstlane(fine[min(t, a.K1 - 1)]);
+            const int tt = min(t, nft - 1);
+            const int f = __builtin_amdgcn_readfirstlane(fine[tt / a.sub]) * a.sub + tt % a.sub;
             const int64_t kr = (int64_t)tok_row(a.tm, f * kBlock + c16) * kHeadDim;
             const __bf16 *kt = k + head_off + kr;
             const __bf16 *vt = v + head_off + kr;
@@ -331,10 +348,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
                 accB[dt] = mfma_bf16_32(kk, pcat, accB[dt]);
             }
         };
-        for (int t = 0; t < a.K1; t += 2) {
+        for (int t = 0; t < nft; t += 2) {
             fine_tile(RA);
             load_tile(t + 2, RA);
-            if (t + 1 < a.K1) fine_tile(RB);
+            if (t + 1 < nft) fine_tile(RB);
             load_tile(t + 3, RB);
         }
         // ---- coarse tiles: scores in both orientations, then D is complete
@@ -398,7 +415,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
         wave_lds_sync();
     }
     // ---- reduce the coarse partials over the 4 waves, one coarse tile at a time
-    float *part = ws.partial + ((int64_t)h * a.n2 + G) * a.ncoarse * 2 * kHeadDim;
+    float *part = ws.partial + ((int64_t)h * a.npg + G) * a.ncoarse * 2 * kHeadDim;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
         __syncthreads();
@@ -673,7 +690,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
             lds_red[w][1][ent * kHeadDim + dim] = dvc[dt][i];
         }
     __syncthreads();
-    float *part = ws.partial + ((int64_t)h * a.n2 + G) * a.ncoarse * 2 * kHeadDim;
+    float *part = ws.partial + ((int64_t)h * a.npg + G) * a.ncoarse * 2 * kHeadDim;
     for (int x = threadIdx.x; x < a.ncoarse * 2 * kHeadDim; x += 256) {
         const int er = x / (2 * kHeadDim), kv = (x / kHeadDim) & 1, dim = x % kHeadDim;
         const int oo = er * kHeadDim + dim;
@@ -684,7 +701,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
 // ================================================================ pass B
 // One wave per pooled token c of level l (lanes = columns): the level-l rows
 // that picked c come from the CSR of I^(l); each lane looks up one row's slot
-// of c, then the wave sums the partials of every level-2 node under each row.
+// of c, then the wave sums the partials of every group of 16 query tiles under
+// each row.
 __global__ __launch_bounds__(256) void bwd_coarse_reduce_kernel(const int32_t *__restrict__ idx,
                                                                 const int32_t *__restrict__ csr_ptr,
                                                                 const int32_t *__restrict__ csr_col,
@@ -698,7 +716,7 @@ __global__ __launch_bounds__(256) void bwd_coarse_reduce_kernel(const int32_t *_
     const int32_t *P = csr_ptr + a.cl_ptr_off[j] + (int64_t)h * (nl + 1);
     const int32_t *C = csr_col + a.cl_col_off[j] + (int64_t)h * nl * kl;
     const int32_t *I = idx + a.cl_idx_off[j] + (int64_t)h * nl * kl;
-    const int nodes = a.cl_span[j] / kBlock;   // level-2 nodes under one level-l token
+    const int nodes = a.cl_groups[j];   // partial groups under one level-l token
     const int e0 = P[c], e1 = P[c + 1];
     float sk = 0.f, sv = 0.f;
     for (int base = e0; base < e1; base += kWave) {
@@ -737,7 +755,7 @@ __global__ __launch_bounds__(256) void bwd_coarse_reduce_kernel(const int32_t *_
                 for (int u = 0; u < 8; ++u) {
                     const int jj = min(j0 + u, cnt - 1);
                     const int e = __builtin_amdgcn_readlane(ent, jj);
-                    const int64_t G0 = (int64_t)h * a.n2 + __builtin_amdgcn_readlane(g0, jj);
+                    const int64_t G0 = (int64_t)h * a.npg + __builtin_amdgcn_readlane(g0, jj);
                     const float *pp = ws.partial + ((G0 + s) * a.ncoarse + max(e, 0)) * 2 * kHeadDim;
                     const bool use = j0 + u < cnt && e >= 0;
                     pk8[u] = use ? pp[lane] : 0.f;
@@ -756,13 +774,14 @@ __global__ __launch_bounds__(256) void bwd_coarse_reduce_kernel(const int32_t *_
 }
 
 // ================================================================ pass C
-// One wave per key block, in a workgroup of its own: key blocks differ widely
+// One wave per key tile, in a workgroup of its own: key blocks differ widely
 // in how many query blocks picked them, and no wave waits for a slower
-// sibling before its slot is reused.  The query blocks of the key's CSR
-// segment stream through a ring of kDkvDepth register sets, so that several
-// blocks' Q / dO are in flight while one is computed.
+// sibling before its slot is reused.  The query tiles of the blocks in the
+// key block's CSR segment (SUB = B / 16 per block) stream through a ring of
+// kDkvDepth register sets, so that several tiles' Q / dO are in flight while
+// one is computed.
 constexpr int kDkvDepth = 4;
-template <int ORD>
+template <int ORD, int SUB>
 __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ lse, const __bf16 *__restrict__ dout, const int32_t *__restrict__ csr_ptr,
@@ -775,23 +794,24 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
     const int lane = lane_id();
     const int g = lane >> 4, c16 = lane & 15;
     const int64_t kb = xcd_remap(blockIdx.x, gridDim.x);
-    if (kb >= (int64_t)a.bh * a.n1) return;
-    const int h = (int)(kb / a.n1);
-    const int f = (int)(kb % a.n1);
+    if (kb >= (int64_t)a.bh * a.nt1) return;
+    const int h = (int)(kb / a.nt1);
+    const int f = (int)(kb % a.nt1);   // key tile
+    const int fb = f / SUB;            // its key block
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
-    // element offset (within the head) of row r of sequence block b
+    // element offset (within the head) of row r of 16-token tile b
     auto trow = [&](int b, int r) { return (int64_t)tok_row_o<ORD>(a.tm, b * kBlock + r) * kHeadDim; };
     const int32_t *P = csr_ptr + (int64_t)h * (a.n1 + 1);
     const int32_t *C = csr_col + (int64_t)h * a.n1 * a.K1;
-    const int e0 = __builtin_amdgcn_readfirstlane(P[f]), e1 = __builtin_amdgcn_readfirstlane(P[f + 1]);
+    const int e0 = __builtin_amdgcn_readfirstlane(P[fb]), e1 = __builtin_amdgcn_readfirstlane(P[fb + 1]);
     f32x4 dka[4], dva[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
         dka[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         dva[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // about half of the key blocks are picked by no query block: they only
-    // receive the pooled-level gradients below and never read K or V
+    // about half of the key blocks are picked by no query block: their tiles
+    // only receive the pooled-level gradients below and never read K or V
     if (e1 > e0) {
     const __bf16 *krow = k + head_off + trow(f, c16);
     const __bf16 *vrow = v + head_off + trow(f, c16);
@@ -854,26 +874,31 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
         }
     };
     // The segment's query blocks are read 64 at a time into one register
-    // (lane j holds entry j).  Ring: set r holds entry j + r; after computing
-    // it, set r is refilled with entry j + r + kDkvDepth, so at the loop head
-    // the set needed next is always the oldest one in flight.
+    // (lane j holds entry j); tile j of a batch is sub-tile j % SUB of entry
+    // j / SUB.  Ring: set r holds tile j + r; after computing it, set r is
+    // refilled with tile j + r + kDkvDepth, so at the loop head the set needed
+    // next is always the oldest one in flight.
     for (int base = e0; base < e1; base += kWave) {
         const int cnt = min(kWave, e1 - base);
         const int colv = lane < cnt ? C[base + lane] : 0;
+        const int ntl = cnt * SUB;
+        auto qtile = [&](int jt) {
+            const int jc = min(jt, ntl - 1);
+            return __builtin_amdgcn_readlane(colv, jc / SUB) * SUB + jc % SUB;
+        };
         Pair R[kDkvDepth];
 #pragma unroll
-        for (int r = 0; r < kDkvDepth; ++r)
-            load_pair(__builtin_amdgcn_readlane(colv, min(r, cnt - 1)), R[r]);
+        for (int r = 0; r < kDkvDepth; ++r) load_pair(qtile(r), R[r]);
         int j = 0;
-        for (; j + kDkvDepth <= cnt; j += kDkvDepth)
+        for (; j + kDkvDepth <= ntl; j += kDkvDepth)
 #pragma unroll
             for (int r = 0; r < kDkvDepth; ++r) {
                 compute(R[r]);
-                load_pair(__builtin_amdgcn_readlane(colv, min(j + kDkvDepth + r, cnt - 1)), R[r]);
+                load_pair(qtile(j + kDkvDepth + r), R[r]);
             }
 #pragma unroll
         for (int r = 0; r < kDkvDepth - 1; ++r)
-            if (j + r < cnt) compute(R[r]);
+            if (j + r < ntl) compute(R[r]);
     }
     }
     // Pooled-level gradients, spread back with weight 1/B^l: every key row of
@@ -881,10 +906,10 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
     const int oc = 4 * c16;
     f32x4 ck = f32x4{0.f, 0.f, 0.f, 0.f}, cv = ck;
     {
-        float inv = 1.f / kBlock;
+        float inv = a.invB;
         for (int j = 0; j < a.ncl; ++j) {
-            inv *= (1.0f / kBlock);
-            const int64_t off = a.cl_grad_off[j] + ((int64_t)h * a.cl_n[j] + f / a.cl_span[j]) * kHeadDim + oc;
+            inv *= a.invB;
+            const int64_t off = a.cl_grad_off[j] + ((int64_t)h * a.cl_n[j] + fb / a.cl_span[j]) * kHeadDim + oc;
             ck += *reinterpret_cast<const f32x4 *>(ws.dpk + off) * inv;
             cv += *reinterpret_cast<const f32x4 *>(ws.dpv + off) * inv;
         }
@@ -935,7 +960,7 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(
     const int lane = lane_id();
     const int h = (int)(tq / a.N);
     const int tok = (int)(tq % a.N);
-    const int ib = tok / kBlock;
+    const int ib = tok / (kBlock * a.sub);   // query block
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
     const int64_t srow = tok_row(a.tm, tok);
     const int64_t row = head_off + srow * kHeadDim + lane;
@@ -951,8 +976,8 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(
         acc = fmaf(p * (dp - D), kx, acc);
     };
     const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
-    for (int j = 0; j < a.K1; ++j) {
-        const int u0 = __builtin_amdgcn_readfirstlane(fine[j]) * kBlock;
+    for (int jt = 0; jt < a.K1 * a.sub; ++jt) {   // key tiles: sub-tile jt % sub of pick jt / sub
+        const int u0 = (__builtin_amdgcn_readfirstlane(fine[jt / a.sub]) * a.sub + jt % a.sub) * kBlock;
         float kx[kBlock], vx[kBlock];
 #pragma unroll
         for (int t = 0; t < kBlock; ++t) {
@@ -976,7 +1001,7 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(
 
 // Pooled-token gradients (f32): one wave per (level, pooled token).  The wave
 // walks the CSR of I^(l) and every query block under each row that picked the
-// token, a block's 16 query rows at a time.
+// token, 16 query rows at a time.
 
 __global__ __launch_bounds__(256) void bwd_coarse_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ pk, const float *__restrict__ pv,
@@ -992,7 +1017,7 @@ __global__ __launch_bounds__(256) void bwd_coarse_f32_kernel(
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
     const int64_t roff = a.cl_pyr_off[j] + ((int64_t)h * nl + c) * kHeadDim;
     const float kx = pk[roff + lane], vx = pv[roff + lane];
-    const float bias = 4.0f * (float)(j + 2);
+    const float bias = a.lgB * (float)(j + 2);
     float gk = 0.f, gv = 0.f;
     const int32_t *P = csr_ptr + a.cl_ptr_off[j] + (int64_t)h * (nl + 1);
     const int32_t *C = csr_col + a.cl_col_off[j] + (int64_t)h * nl * kl;
@@ -1006,23 +1031,25 @@ __global__ __launch_bounds__(256) void bwd_coarse_f32_kernel(
                 for (int ff = 0; ff < a.K1; ++ff) cov += (fine[ff] / span == c) ? 1 : 0;
                 if (cov == span) continue;
             }
-            float qx[kBlock], gx[kBlock];
-            int64_t srow[kBlock];
+            for (int qt = ib * a.sub; qt < (ib + 1) * a.sub; ++qt) {
+                float qx[kBlock], gx[kBlock];
+                int64_t srow[kBlock];
 #pragma unroll
-            for (int tt = 0; tt < kBlock; ++tt) {
-                srow[tt] = tok_row(a.tm, ib * kBlock + tt);
-                qx[tt] = q[head_off + srow[tt] * kHeadDim + lane];
-                gx[tt] = dout[head_off + srow[tt] * kHeadDim + lane];
-            }
+                for (int tt = 0; tt < kBlock; ++tt) {
+                    srow[tt] = tok_row(a.tm, qt * kBlock + tt);
+                    qx[tt] = q[head_off + srow[tt] * kHeadDim + lane];
+                    gx[tt] = dout[head_off + srow[tt] * kHeadDim + lane];
+                }
 #pragma unroll
-            for (int tt = 0; tt < kBlock; ++tt) {
-                const int64_t tok = (int64_t)h * a.N + (int64_t)ib * kBlock + tt;
-                const float s = wave_sum(qx[tt] * kx);
-                const float dp = wave_sum(gx[tt] * vx);
-                const float p = exp2f(s * a.sl2 + bias - lse[(int64_t)h * a.N + srow[tt]] * kLog2e);
-                const float ds = p * (dp - ws.D[tok]);
-                gk = fmaf(ds, qx[tt], gk);
-                gv = fmaf(p, gx[tt], gv);
+                for (int tt = 0; tt < kBlock; ++tt) {
+                    const int64_t tok = (int64_t)h * a.N + (int64_t)qt * kBlock + tt;
+                    const float s = wave_sum(qx[tt] * kx);
+                    const float dp = wave_sum(gx[tt] * vx);
+                    const float p = exp2f(s * a.sl2 + bias - lse[(int64_t)h * a.N + srow[tt]] * kLog2e);
+                    const float ds = p * (dp - ws.D[tok]);
+                    gk = fmaf(ds, qx[tt], gk);
+                    gv = fmaf(p, gx[tt], gv);
+                }
             }
         }
     }
@@ -1041,7 +1068,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_f32_kernel(
     const int lane = lane_id();
     const int h = (int)(tu / a.N);
     const int u = (int)(tu % a.N);
-    const int f = u / kBlock;
+    const int f = u / (kBlock * a.sub);   // key block
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
     const int64_t row = head_off + (int64_t)tok_row(a.tm, u) * kHeadDim + lane;
     const float kx = k[row], vx = v[row];
@@ -1049,19 +1076,19 @@ __global__ __launch_bounds__(256) void bwd_dkv_f32_kernel(
     const int32_t *P = csr_ptr + (int64_t)h * (a.n1 + 1);
     const int32_t *C = csr_col + (int64_t)h * a.n1 * a.K1;
     const int e0 = __builtin_amdgcn_readfirstlane(P[f]), e1 = __builtin_amdgcn_readfirstlane(P[f + 1]);
-    for (int e = e0; e < e1; ++e) {
-        const int ib = __builtin_amdgcn_readfirstlane(C[e]);
+    for (int et = e0 * a.sub; et < e1 * a.sub; ++et) {   // query tiles of the segment's blocks
+        const int qt = __builtin_amdgcn_readfirstlane(C[et / a.sub]) * a.sub + et % a.sub;
         float qx[kBlock], gx[kBlock];
         int64_t srow[kBlock];
 #pragma unroll
         for (int tt = 0; tt < kBlock; ++tt) {
-            srow[tt] = tok_row(a.tm, ib * kBlock + tt);
+            srow[tt] = tok_row(a.tm, qt * kBlock + tt);
             qx[tt] = q[head_off + srow[tt] * kHeadDim + lane];
             gx[tt] = dout[head_off + srow[tt] * kHeadDim + lane];
         }
 #pragma unroll
         for (int tt = 0; tt < kBlock; ++tt) {
-            const int64_t tok = (int64_t)h * a.N + (int64_t)ib * kBlock + tt;
+            const int64_t tok = (int64_t)h * a.N + (int64_t)qt * kBlock + tt;
             const float s = wave_sum(qx[tt] * kx);
             const float dp = wave_sum(gx[tt] * vx);
             const float p = exp2f(s * a.sl2 - lse[(int64_t)h * a.N + srow[tt]] * kLog2e);
@@ -1072,11 +1099,11 @@ __global__ __launch_bounds__(256) void bwd_dkv_f32_kernel(
     gk *= a.scale;
     float inv = 1.f;
     for (int j = 0; j < a.ncl; ++j) {
-        inv *= (1.0f / kBlock);
+        inv *= a.invB;
         const int c = f / a.cl_span[j];
         const int64_t off = a.cl_grad_off[j] + ((int64_t)h * a.cl_n[j] + c) * kHeadDim + lane;
-        gk += ws.dpk[off] * (inv * (1.0f / kBlock));
-        gv += ws.dpv[off] * (inv * (1.0f / kBlock));
+        gk += ws.dpk[off] * (inv * a.invB);
+        gv += ws.dpv[off] * (inv * a.invB);
     }
     store_grad1(dk, row, gk, a.grad_bf16);
     store_grad1(dv, row, gv, a.grad_bf16);
@@ -1090,11 +1117,11 @@ hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, cons
     const BwdArgs a = make_bwd_args(g);
     const BwdWs ws = carve_ws(g, a, wsp);
     if (g.bf16) {
-        const int gph = (a.n1 + kBlock - 1) / kBlock;
+        const int gph = (a.nt1 + kBlock - 1) / kBlock;
         const int nct = (a.ncoarse + kBlock - 1) / kBlock;
         const dim3 grid((unsigned)(g.bh * gph));
-        const bool fast = g.L >= 2 && a.K1 == kFastK1 && nct == 1 && a.n1 % kBlock == 0 &&
-                          !(a.drop && a.K1 >= kBlock);
+        const bool fast = g.B == kBlock && g.L >= 2 && a.K1 == kFastK1 && nct == 1 &&
+                          a.n1 % kBlock == 0 && !(a.drop && a.K1 >= kBlock);
         if (fast && g.order == 0)
             hipLaunchKernelGGL(bwd_dq_fast_kernel<0>, grid, dim3(256), 0, s, (const __bf16 *)q,
                                (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx, lse,
@@ -1120,17 +1147,12 @@ hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, cons
             hipLaunchKernelGGL(bwd_coarse_reduce_kernel, dim3((unsigned)((toks + 3) / 4)),
                                dim3(256), 0, s, idx, csr_ptr, csr_col, ws, a, j);
         }
-        const int64_t kbs = (int64_t)g.bh * a.n1;
-        if (g.order == 0)
-            hipLaunchKernelGGL(bwd_dkv_bf16_kernel<0>, dim3((unsigned)kbs), dim3(kWave), 0, s,
-                               (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, lse,
-                               (const __bf16 *)dout, csr_ptr + g.ptr_off[1], csr_col + g.col_off[1],
-                               dk, dv, ws, a);
-        else
-            hipLaunchKernelGGL(bwd_dkv_bf16_kernel<1>, dim3((unsigned)kbs), dim3(kWave), 0, s,
-                               (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, lse,
-                               (const __bf16 *)dout, csr_ptr + g.ptr_off[1], csr_col + g.col_off[1],
-                               dk, dv, ws, a);
+        const int64_t kts = (int64_t)g.bh * a.nt1;   // key tiles
+        auto dkv = g.order == 0 ? (g.sub == 1 ? bwd_dkv_bf16_kernel<0, 1> : bwd_dkv_bf16_kernel<0, 4>)
+                                : (g.sub == 1 ? bwd_dkv_bf16_kernel<1, 1> : bwd_dkv_bf16_kernel<1, 4>);
+        hipLaunchKernelGGL(dkv, dim3((unsigned)kts), dim3(kWave), 0, s, (const __bf16 *)q,
+                           (const __bf16 *)k, (const __bf16 *)v, lse, (const __bf16 *)dout,
+                           csr_ptr + g.ptr_off[1], csr_col + g.col_off[1], dk, dv, ws, a);
     } else {
         const int64_t total = (int64_t)g.bh * g.N;
         hipLaunchKernelGGL(bwd_dq_f32_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s,

@@ -3,7 +3,9 @@
 // Transformers", explainer "Step 3: Hierarchical KV Enrichment + KV
 // Reweighting"), driven only by the index lists.
 //
-// bf16 path: one wave per query block of 16 queries.  Scores are computed
+// bf16 path: one wave per tile of 16 queries (a query block of B = 16 or one
+// quarter of a block of B = 64; the tiles of a block share its picks, and a
+// picked key block is B / 16 key tiles).  Scores are computed
 // transposed, S^T = K Q^T, on v_mfma_f32_16x16x32_bf16 so that lane l owns
 // query l%16 and keys 4(l/16)..+3 of every 16-key tile; that register layout
 // is exactly the B operand of O^T += V^T P^T, so probabilities never leave
@@ -26,6 +28,9 @@ constexpr int kMaxCoarseLevels = kMaxLevels - 1;
 
 struct FwdArgs {
     int bh, N, n1, K1;
+    int sub;                                   // 16-token tiles per block (B / 16)
+    int nt1;                                   // query tiles per head, n1 * sub
+    float lgB;                                 // log2(B): the bias of level l is l * lgB
     int ncl;                                   // coarse levels used (2..ncl+1)
     int ncoarse;                               // coarse entries per query block
     int cl_n[kMaxCoarseLevels];                // tokens at that level
@@ -44,12 +49,15 @@ static FwdArgs make_fwd_args(const Geometry &g) {
     a.N = g.N;
     a.n1 = g.n[1];
     a.K1 = g.kl[1];
+    a.sub = g.sub;
+    a.nt1 = g.n[1] * g.sub;
+    a.lgB = (float)g.lgB;
     a.ncl = g.Le < g.L - 1 ? g.Le : g.L - 1;
     a.ncoarse = 0;
     int64_t span = 1;
     for (int j = 0; j < a.ncl; ++j) {
         const int l = j + 2;
-        span *= kBlock;
+        span *= g.B;
         a.cl_n[j] = g.n[l];
         a.cl_k[j] = g.kl[l];
         a.cl_span[j] = (int)span;
@@ -85,7 +93,7 @@ __device__ __forceinline__ bool coarse_entry(const FwdArgs &a, const int32_t *__
         if (cov == span) return false;
     }
     row_off = a.cl_pyr_off[j] + ((int64_t)h * a.cl_n[j] + c) * kHeadDim;
-    bias = 4.0f * (float)(j + 2);  // log2(16^l)
+    bias = a.lgB * (float)(j + 2);  // log2(B^l)
     return true;
 }
 
@@ -101,9 +109,9 @@ __device__ __forceinline__ bool coarse_locate(const FwdArgs &a, int e, int &j, i
 }
 
 // A coarse pick can only be fully covered by the fine picks when K_1 reaches
-// the B^(l-1) level-1 blocks under it.
-__device__ __forceinline__ bool drop_possible(const FwdArgs &a) {
-    return a.drop && a.K1 >= kBlock;
+// the B^(l-1) level-1 blocks under it (B for level 2, the smallest).
+__host__ __device__ __forceinline__ bool drop_possible(const FwdArgs &a) {
+    return a.drop && a.ncl > 0 && a.K1 >= a.cl_span[0];
 }
 
 // Coarse tile ct of query block ib, prefetched as raw float32 rows: the lane's
@@ -159,7 +167,7 @@ __device__ __forceinline__ void prefetch_coarse(const FwdArgs &a, const int32_t 
     for (int i = 0; i < 4; ++i) {
         int j2, p2;
         const bool ok2 = coarse_locate(a, ct * kBlock + 4 * g + i, j2, p2);
-        R.bias[i] = ok2 ? 4.0f * (float)(j2 + 2) : -INFINITY;
+        R.bias[i] = ok2 ? a.lgB * (float)(j2 + 2) : -INFINITY;
     }
     if (drop_possible(a)) {
 #pragma unroll
@@ -179,21 +187,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     const int w = wave_id();
     const int lane = lane_id();
     const int g = lane >> 4, c16 = lane & 15;
-    const int64_t blk = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + w;
-    if (blk >= (int64_t)a.bh * a.n1) return;
-    const int h = (int)(blk / a.n1);
-    const int ib = (int)(blk % a.n1);
+    const int64_t blk = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + w;   // query tile
+    if (blk >= (int64_t)a.bh * a.nt1) return;
+    const int h = (int)(blk / a.nt1);
+    const int qt = (int)(blk % a.nt1);
+    const int ib = qt / a.sub;   // its query block
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
     const __bf16 *kh = k + head_off;
     const __bf16 *vh = v + head_off;
     __bf16 *vw = vs_all[w];
 
-    // element offset (within the head) of row r of sequence block b
+    // element offset (within the head) of row r of 16-token tile b
     auto trow = [&](int b, int r) { return (int64_t)tok_row(a.tm, b * kBlock + r) * kHeadDim; };
-    const __bf16 *qrow = q + head_off + trow(ib, c16);
+    const __bf16 *qrow = q + head_off + trow(qt, c16);
     const bf16x8 qa0 = load_bf16x8(qrow + 8 * g);
     const bf16x8 qa1 = load_bf16x8(qrow + 32 + 8 * g);
-    const int32_t *fine = idx + blk * a.K1;
+    const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
+    const int nft = a.K1 * a.sub;   // fine key tiles: sub-tile t % sub of pick t / sub
     const int nct = (a.ncoarse + kBlock - 1) / kBlock;
 
     float m = -INFINITY, lsum = 0.f;
@@ -209,12 +219,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     // any is consumed (tiles past the chunk's end re-read its last tile); the
     // first coarse tile is fetched right after the first chunk's loads so its
     // two dependent reads (pick index, then pooled rows) overlap them.
-    for (int t0 = 0; t0 < a.K1; t0 += kFwdTiles) {
-        const int nt = min(kFwdTiles, a.K1 - t0);
+    for (int t0 = 0; t0 < nft; t0 += kFwdTiles) {
+        const int nt = min(kFwdTiles, nft - t0);
         bf16x8 kr[kFwdTiles][2], vr[kFwdTiles][2];
 #pragma unroll
         for (int t = 0; t < kFwdTiles; ++t) {
-            const int f = __builtin_amdgcn_readfirstlane(fine[t0 + min(t, nt - 1)]);
+            const int tt = t0 + min(t, nt - 1);
+            const int f = __builtin_amdgcn_readfirstlane(fine[tt / a.sub]) * a.sub + tt % a.sub;
             const __bf16 *kt = kh + trow(f, c16);
             kr[t][0] = load_bf16x8(kt + 8 * g);
             kr[t][1] = load_bf16x8(kt + 32 + 8 * g);
@@ -252,14 +263,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     // ---- normalise and store
     lsum = sum4_groups(lsum);
     const float inv = 1.0f / lsum;
-    __bf16 *orow = o + head_off + trow(ib, c16) + 4 * g;
+    __bf16 *orow = o + head_off + trow(qt, c16) + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
         const f32x4 r = oacc[dt] * inv;
         const bf16x4 rb = to_bf16x4(f32x4{r[0], r[1], r[2], r[3]});
         *reinterpret_cast<u32x2 *>(orow + 16 * dt) = __builtin_bit_cast(u32x2, rb);
     }
-    if (g == 0) lse[(int64_t)h * a.N + tok_row(a.tm, ib * kBlock + c16)] = (m + log2f(lsum)) * kLn2;
+    if (g == 0) lse[(int64_t)h * a.N + tok_row(a.tm, qt * kBlock + c16)] = (m + log2f(lsum)) * kLn2;
 }
 
 // ------------------------------------------------------------ fast path
@@ -453,7 +464,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
     if (tq >= (int64_t)a.bh * a.N) return;
     const int h = (int)(tq / a.N);
     const int tok = (int)(tq % a.N);
-    const int ib = tok / kBlock;
+    const int bsz = a.sub * kBlock;   // B
+    const int ib = tok / bsz;
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
     float qv[kHeadDim], acc[kHeadDim];
 #pragma unroll
@@ -478,8 +490,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
     const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
     for (int j = 0; j < a.K1; ++j) {
         const int f = fine[j];
-        for (int t = 0; t < kBlock; ++t) {
-            const int64_t u = tok_row(a.tm, f * kBlock + t);
+        for (int t = 0; t < bsz; ++t) {
+            const int64_t u = tok_row(a.tm, f * bsz + t);
             attend(k + head_off + u * kHeadDim, v + head_off + u * kHeadDim, 0.f);
         }
     }
@@ -501,8 +513,9 @@ hipError_t launch_attn_fwd(const Geometry &g, const void *q, const void *k, cons
     const FwdArgs a = make_fwd_args(g);
     if (g.bf16) {
         const int64_t blocks = (int64_t)g.bh * g.n[1];
-        const bool fast = g.L >= 2 && a.K1 == 8 && a.ncoarse > 0 && a.ncoarse <= kBlock &&
-                          !(a.drop && a.K1 >= kBlock) && a.n1 % 4 == 0;
+        const int64_t tiles = (int64_t)g.bh * a.nt1;
+        const bool fast = g.B == kBlock && g.L >= 2 && a.K1 == 8 && a.ncoarse > 0 &&
+                          a.ncoarse <= kBlock && !drop_possible(a) && a.n1 % 4 == 0;
         if (fast && g.order == 0)
             hipLaunchKernelGGL((attn_fwd_fast_kernel<8, 0>), dim3((unsigned)(blocks / 4)), dim3(256), 0,
                                s, (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx,
@@ -512,7 +525,7 @@ hipError_t launch_attn_fwd(const Geometry &g, const void *q, const void *k, cons
                                s, (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx,
                                (__bf16 *)o, lse, a);
         else
-            hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3((unsigned)((blocks + 3) / 4)), dim3(256), 0,
+            hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0,
                                s, (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx,
                                (__bf16 *)o, lse, a);
     } else {

@@ -11,6 +11,9 @@ constexpr int kMaxLevels = 6;
 struct Geometry {
     int bh;                          // batch * heads
     int N;                           // tokens
+    int B;                           // block size (16 or 64)
+    int sub;                         // 16-token tiles per block, B / 16
+    int lgB;                         // log2(B)
     int L;                           // pooling steps
     int K;                           // requested picks
     int Le;                          // enrichment depth (coarse levels 2..Le+1)

@@ -8,7 +8,8 @@
 // instruction of a wave reads whole 128-byte row segments and the block sum
 // needs no cross-lane reduction.  Level 2 is formed from the level-1 means in
 // LDS; deeper levels (rare, small) are pooled from the level below by a
-// second kernel.
+// second kernel.  Blocks of 64 tokens take a kernel of their own (one wave per
+// block) and every level above 1 comes from the level below.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -104,25 +105,90 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ q, cons
     }
 }
 
-// Level l >= 3 from level l-1 (float32), one thread per output element.
+// Level 1 for blocks of 64 tokens: one wave per block of one tensor.  Lane
+// (r, c) reads rows r, r + RPI, r + 2 RPI, ... at 16-byte chunk c, so every
+// load instruction reads whole rows; the partial sums of one chunk meet
+// through butterfly shuffles.
+template <typename T, int ORD>
+__global__ __launch_bounds__(256) void pool64_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                                                     const T *__restrict__ v, float *__restrict__ pq,
+                                                     float *__restrict__ pk, float *__restrict__ pv,
+                                                     int64_t total_blocks, int wg_per_tensor, int n1,
+                                                     TokMap tm) {
+    constexpr int kB = 64;
+    constexpr int EPC = ElemTraits<T>::kPerChunk;  // elements per 16-byte chunk
+    constexpr int CPR = kHeadDim / EPC;            // chunks per row
+    constexpr int RPI = kWave / CPR;               // rows per load instruction
+    constexpr int NLD = kB / RPI;                  // loads per lane
+    const int tensor = blockIdx.x / wg_per_tensor;
+    const int wg = blockIdx.x % wg_per_tensor;
+    const T *x = tensor == 0 ? q : (tensor == 1 ? k : v);
+    float *out = tensor == 0 ? pq : (tensor == 1 ? pk : pv);
+    const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int r = lane / CPR, c = lane % CPR;
+    const int64_t blk = (int64_t)wg * 4 + w;
+    if (blk >= total_blocks) return;
+    const int64_t h = blk / n1;
+    const int lb = (int)(blk % n1);
+    const T *src = x + h * (int64_t)n1 * kB * kHeadDim + c * EPC;
+    u32x4 rr[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i)
+        rr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+            src + (int64_t)tok_row_o<ORD>(tm, lb * kB + r + RPI * i) * kHeadDim));
+    float acc[EPC];
+#pragma unroll
+    for (int j = 0; j < EPC; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+        float f[EPC];
+        chunk_to_f32(rr[i], f, (T *)nullptr);
+#pragma unroll
+        for (int j = 0; j < EPC; ++j) acc[j] += f[j];
+    }
+#pragma unroll
+    for (int m = CPR; m < kWave; m <<= 1)
+#pragma unroll
+        for (int j = 0; j < EPC; ++j) acc[j] += shfl_xor_f(acc[j], m);
+    if (r == 0) {
+        float *dst = out + blk * kHeadDim + c * EPC;
+#pragma unroll
+        for (int j = 0; j < EPC; j += 4)
+            *reinterpret_cast<f32x4 *>(dst + j) =
+                f32x4{acc[j], acc[j + 1], acc[j + 2], acc[j + 3]} * (1.0f / kB);
+    }
+}
+
+// Level l from level l-1 (float32), one thread per output element.
 __global__ __launch_bounds__(256) void pool_up_kernel(float *__restrict__ pq, float *__restrict__ pk,
                                                       float *__restrict__ pv, int64_t src_off,
-                                                      int64_t dst_off, int64_t total_out) {
+                                                      int64_t dst_off, int64_t total_out, int B) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int tensor = blockIdx.y;
     if (t >= total_out) return;
     float *p = tensor == 0 ? pq : (tensor == 1 ? pk : pv);
     const int64_t tok = t / kHeadDim, e = t % kHeadDim;
-    const float *src = p + src_off + tok * kBlock * kHeadDim + e;
+    const float *src = p + src_off + tok * B * kHeadDim + e;
     float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < kBlock; ++j) s += src[j * kHeadDim];
-    p[dst_off + t] = s * (1.0f / kBlock);
+    for (int j = 0; j < B; ++j) s += src[j * kHeadDim];
+    p[dst_off + t] = s * (1.0f / (float)B);
 }
 
 template <typename T>
 static void launch_pool_t(const Geometry &g, const T *q, const T *k, const T *v, float *pq,
                           float *pk, float *pv, hipStream_t s) {
+    if (g.B == 64) {
+        const int64_t total_blocks = (int64_t)g.bh * g.n[1];
+        const int wg_per_tensor = (int)((total_blocks + 3) / 4);
+        const TokMap tm{g.order, g.log2S};
+        if (g.order == 0)
+            hipLaunchKernelGGL((pool64_kernel<T, 0>), dim3(3 * wg_per_tensor), dim3(256), 0, s, q, k, v,
+                               pq, pk, pv, total_blocks, wg_per_tensor, g.n[1], tm);
+        else
+            hipLaunchKernelGGL((pool64_kernel<T, 1>), dim3(3 * wg_per_tensor), dim3(256), 0, s, q, k, v,
+                               pq, pk, pv, total_blocks, wg_per_tensor, g.n[1], tm);
+        return;
+    }
     constexpr int BPG = 4 * (kWave / (kHeadDim / ElemTraits<T>::kPerChunk));
     const int64_t total_blocks = (int64_t)g.bh * g.n[1];
     const int wg_per_tensor = (int)((total_blocks + BPG - 1) / BPG);
@@ -144,10 +210,11 @@ hipError_t launch_pool(const Geometry &g, const void *q, const void *k, const vo
     else
         launch_pool_t<float>(g, (const float *)q, (const float *)k, (const float *)v, pq, pk, pv,
                              s);
-    for (int l = 3; l <= g.L; ++l) {
+    // levels the first kernel did not form (above 2 for B = 16, above 1 for B = 64)
+    for (int l = g.B == 16 ? 3 : 2; l <= g.L; ++l) {
         const int64_t total = (int64_t)g.bh * g.n[l] * kHeadDim;
         hipLaunchKernelGGL(pool_up_kernel, dim3((unsigned)((total + 255) / 256), 3), dim3(256), 0,
-                           s, pq, pk, pv, g.pyr_off[l - 1], g.pyr_off[l], total);
+                           s, pq, pk, pv, g.pyr_off[l - 1], g.pyr_off[l], total, g.B);
     }
     return hipGetLastError();
 }

@@ -4,12 +4,12 @@
 // only the B children of the parent's picks are scored.
 //
 // One wave serves 16 query rows that share their candidates: at a finer level
-// these are the 16 children of one parent, whose candidate list is the
-// children of the parent's K picks (K tiles of 16 contiguous pooled keys); at
-// the coarsest level a 16-row slice against all keys.  Scores are float32 on
-// the matrix cores (v_mfma_f32_16x16x4_f32), computed transposed so that lane
-// l owns query l%16 and 4 candidates of each 16-candidate tile.  Top-K runs in
-// registers on 64-bit keys (order-preserving score bits, inverted index), so
+// these are 16 of the B children of one parent, whose candidate list is the
+// children of the parent's K picks (B / 16 tiles of 16 contiguous pooled keys
+// per pick); at the coarsest level a 16-row slice against all keys.
+// Scores are float32 on the matrix cores (v_mfma_f32_16x16x4_f32), computed
+// transposed so that lane l owns query l%16 and 4 candidates of each
+// 16-candidate tile.  Top-K runs in registers on 64-bit keys (order-preserving score bits, inverted index), so
 // one unsigned compare orders by score and breaks ties toward the lower index:
 // every lane sorts its candidates in groups of KM with bitonic networks and
 // merges them into a running top-KM list, then the 4 lanes of a query merge
@@ -88,8 +88,9 @@ __device__ __forceinline__ void sort_asc_u32(uint32_t (&a)[N]) {
 constexpr int kSelTilesPerChunk = 8;
 
 // parent == nullptr: coarsest level, candidates 0..n-1, row groups are
-// 16-row slices.  Otherwise: row group p = the 16 children of parent p,
-// candidates = children of parent[p][0..kp).
+// 16-row slices.  Otherwise: row group gi = 16 of the B children of parent
+// gi / sub (sub = B / 16), candidates = children of that parent's picks
+// [0..kp), tile t = sub-tile t % sub of pick t / sub.
 // SPLIT = 4: the four waves of a workgroup share one row group and take a
 // quarter of its candidate tiles each (the coarsest level has few groups);
 // their lists are merged through LDS at the end.
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ q
                                                      const int32_t *__restrict__ parent,
                                                      int32_t *__restrict__ out, int n, int kout,
                                                      int kp, int groups_per_head,
-                                                     int64_t groups_total) {
+                                                     int64_t groups_total, int sub) {
     static_assert(SPLIT == 1 || SPLIT == 4, "a row group takes one wave or the whole workgroup");
     __shared__ uint64_t part_best[SPLIT == 1 ? 1 : SPLIT][kBlock][KM];
     const int part = SPLIT == 1 ? 0 : wave_id();
@@ -130,8 +131,8 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ q
     }
 
     const bool dense = parent == nullptr;
-    const int ntiles = dense ? (n + kBlock - 1) / kBlock : kp;
-    const int32_t *prow = dense ? nullptr : parent + ((int64_t)h * groups_per_head + gi) * kp;
+    const int ntiles = dense ? (n + kBlock - 1) / kBlock : kp * sub;
+    const int32_t *prow = dense ? nullptr : parent + ((int64_t)h * (groups_per_head / sub) + gi / sub) * kp;
 
     uint64_t best[KM];
 #pragma unroll
@@ -151,7 +152,8 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ q
 #pragma unroll
             for (int t = 0; t < LB; ++t) {
                 const int tile = min(t0 + hb + t, te - 1);
-                base[t] = dense ? tile * kBlock : __builtin_amdgcn_readfirstlane(prow[tile]) * kBlock;
+                base[t] = dense ? tile * kBlock
+                                : (__builtin_amdgcn_readfirstlane(prow[tile / sub]) * sub + tile % sub) * kBlock;
                 const int cand = base[t] + col;
                 const int64_t crow = cand < n ? cand : 0;
                 const f32x4 *src = reinterpret_cast<const f32x4 *>(kh + crow * kHeadDim + 16 * g);
@@ -234,17 +236,17 @@ static void launch_level(const Geometry &g, int l, const float *pq, const float 
     const int64_t total = (int64_t)g.bh * gph;
     const int32_t *parent = dense ? nullptr : idx + g.idx_off[l + 1];
     const int kp = dense ? 0 : g.kl[l + 1];
-    const int ntiles = dense ? gph : kp;
+    const int ntiles = dense ? gph : kp * g.sub;
     // split a row group over the workgroup when groups are too few to fill
     // the chip and each has tiles enough for four waves
     if (total < 1024 && ntiles >= 4 * 2)
         hipLaunchKernelGGL((select_kernel<KM, 4>), dim3((unsigned)total), dim3(256), 0, s,
                            pq + g.pyr_off[l], pk + g.pyr_off[l], parent, idx + g.idx_off[l], n,
-                           g.kl[l], kp, gph, total);
+                           g.kl[l], kp, gph, total, g.sub);
     else
         hipLaunchKernelGGL((select_kernel<KM, 1>), dim3((unsigned)((total + 3) / 4)), dim3(256), 0,
                            s, pq + g.pyr_off[l], pk + g.pyr_off[l], parent, idx + g.idx_off[l], n,
-                           g.kl[l], kp, gph, total);
+                           g.kl[l], kp, gph, total, g.sub);
 }
 
 hipError_t launch_select(const Geometry &g, const float *pq, const float *pk, int32_t *idx,

@@ -56,9 +56,10 @@ class Case:
 
     def __init__(self, batch, heads, N, dtype, L_, K, Le=-1, q=None, k=None, v=None, dout=None,
                  backward=True, drop_covered=True, grad_dtype=torch.float32, seed=0, sinus=False,
-                 token_order=0):
+                 token_order=0, block=16):
         from hierarchical_top_sparse_mean_amd.inputs import make_inputs
         self.batch, self.heads, self.N, self.dtype, self.L, self.K = batch, heads, N, dtype, L_, K
+        self.B = block
         self.Le = L_ - 1 if Le < 0 else Le
         self.backward, self.drop = backward, drop_covered
         self.grad_dtype = grad_dtype
@@ -69,7 +70,7 @@ class Case:
         self.dout = (gd if dout is None else dout.to(dtype)) if backward else None
         self.scale = 1.0 / 8.0
         self.token_order = token_order
-        self.p = L.problem(batch, heads, N, 64, 16, L_, K, Le, dtype, grad_dtype, 0.0, drop_covered,
+        self.p = L.problem(batch, heads, N, 64, block, L_, K, Le, dtype, grad_dtype, 0.0, drop_covered,
                            token_order)
 
     @property
@@ -99,7 +100,7 @@ def run_gpu(c: Case):
     L.llsa_pool(B.p, qd, kd, vd, B.pyr_q, B.pyr_k, B.pyr_v)
     L.llsa_select(B.p, B.pyr_q, B.pyr_k, B.idx)
     torch.cuda.synchronize()
-    check_index_lists([B.index_level(l).cpu().numpy() for l in range(1, c.L + 1)])
+    check_index_lists([B.index_level(l).cpu().numpy() for l in range(1, c.L + 1)], c.B)
     L.llsa_attn_fwd(B.p, qd, kd, vd, B.pyr_k, B.pyr_v, B.idx, B.o, B.lse)
     res = {}
     if c.backward:
@@ -136,16 +137,16 @@ def run_oracle(c: Case):
     q = c.q.double().numpy().reshape(bh, N, 64)[:, perm]
     k = c.k.double().numpy().reshape(bh, N, 64)[:, perm]
     v = c.v.double().numpy().reshape(bh, N, 64)[:, perm]
-    r = O.forward_all(q, k, v, 16, c.L, c.K, c.Le, c.scale, c.drop)
+    r = O.forward_all(q, k, v, c.B, c.L, c.K, c.Le, c.scale, c.drop)
     if c.backward:
         d = c.dout.double().numpy().reshape(bh, N, 64)[:, perm]
-        r["dq"], r["dk"], r["dv"] = O.attn_bwd(q, k, v, r["pyr_k"], r["pyr_v"], r["idx"], d, 16,
+        r["dq"], r["dk"], r["dv"] = O.attn_bwd(q, k, v, r["pyr_k"], r["pyr_v"], r["idx"], d, c.B,
                                                c.K, c.Le, c.scale, c.drop)
-        r["csr"] = [O.transpose(r["idx"][l - 1], N // 16 ** l) for l in range(1, c.Le + 2)]
+        r["csr"] = [O.transpose(r["idx"][l - 1], N // c.B ** l) for l in range(1, c.Le + 2)]
     return r
 
 
-def compare_indices(gi, oi, og):
+def compare_indices(gi, oi, og, B_=16):
     """Level-by-level status of every row: 0 agree, 1 exempt near-tie,
     2 cascade (parent differs), 3 failure.  Returns (status per level, counts)."""
     Lv = len(gi)
@@ -157,7 +158,7 @@ def compare_indices(gi, oi, og):
         st = np.where(same, 0, np.where((gap > 0) & (gap < GAP_BAND), 1, 3))
         if parent_ok is not None:
             bh, n = same.shape
-            inherit = np.repeat(parent_ok, 16, axis=1)[:, :n]
+            inherit = np.repeat(parent_ok, B_, axis=1)[:, :n]
             st = np.where(inherit, st, 2)
         status[l - 1] = st
         parent_ok = st == 0
@@ -166,17 +167,17 @@ def compare_indices(gi, oi, og):
     return status, counts
 
 
-def clean_blocks(status, Le):
+def clean_blocks(status, Le, B_=16):
     """Query blocks whose fine row and every enriching ancestor row agree."""
     ok = status[0] == 0
     n1 = ok.shape[1]
     for l in range(2, Le + 2):
         anc = status[l - 1] == 0
-        ok = ok & np.repeat(anc, 16 ** (l - 1), axis=1)[:, :n1]
+        ok = ok & np.repeat(anc, B_ ** (l - 1), axis=1)[:, :n1]
     return ok
 
 
-def clean_keys(gi, oi, blocks_ok, Le, N):
+def clean_keys(gi, oi, blocks_ok, Le, N, B_=16):
     """Tokens whose gradient only comes from clean query blocks (under either
     side's picks)."""
     bh, n1 = blocks_ok.shape
@@ -184,10 +185,10 @@ def clean_keys(gi, oi, blocks_ok, Le, N):
     for h, i in zip(*np.nonzero(~blocks_ok)):
         for side in (gi, oi):
             for f in side[0][h, i]:
-                bad[h, f * 16:(f + 1) * 16] = True
+                bad[h, f * B_:(f + 1) * B_] = True
             for l in range(2, Le + 2):
-                span = 16 ** l
-                for c in side[l - 1][h, i // 16 ** (l - 1)]:
+                span = B_ ** l
+                for c in side[l - 1][h, i // B_ ** (l - 1)]:
                     bad[h, c * span:(c + 1) * span] = True
     return ~bad
 
@@ -202,12 +203,12 @@ def check_case(c: Case, report=None):
         err = max(float(np.abs(a - b).max()) for a, b in zip(g[name], o[name]))
         summ[name] = err
         assert err <= PYR_TOL, (name, err)
-    status, counts = compare_indices(g["idx"], o["idx"], o["gap"])
+    status, counts = compare_indices(g["idx"], o["idx"], o["gap"], c.B)
     summ.update(counts)
     assert counts["fail"] == 0, counts
-    ok_blocks = clean_blocks(status, c.Le)
+    ok_blocks = clean_blocks(status, c.Le, c.B)
     summ["clean_blocks"] = int(ok_blocks.sum())
-    rows = np.repeat(ok_blocks, 16, axis=1)
+    rows = np.repeat(ok_blocks, c.B, axis=1)
     for name in ("o", "lse"):
         err = float(np.abs(g[name] - o[name])[rows].max())
         summ[name] = err
@@ -216,7 +217,7 @@ def check_case(c: Case, report=None):
         err = float(np.abs(g["dq"] - o["dq"])[rows].max())
         summ["dq"] = err
         assert err <= tol, ("dq", err, tol)
-        keys = clean_keys(g["idx"], o["idx"], ok_blocks, c.Le, c.N)
+        keys = clean_keys(g["idx"], o["idx"], ok_blocks, c.Le, c.N, c.B)
         for name in ("dk", "dv"):
             err = float(np.abs(g[name] - o[name])[keys].max())
             summ[name] = err

@@ -52,6 +52,17 @@ def test_sizes_of_the_measured_workload():
         assert all(arr[l] % 16 == 0 for l in range(1, 4))
 
 
+def test_sizes_block_64():
+    p = L.problem(1, 2, 65536, block=64, levels=2, topk=8)
+    s = L.llsa_sizes_query(p)
+    assert list(s.level_tokens)[:3] == [65536, 1024, 16]
+    assert list(s.level_k)[1:3] == [8, 8]
+    assert s.pyramid_elems == 2 * (1024 + 16) * 64
+    assert s.csr_col_elems == 2 * (1024 + 16) * 8
+    p = L.problem(1, 1, 4096, block=64, levels=2, topk=8)   # 1 coarsest token -> 64 candidates
+    assert list(L.llsa_sizes_query(p).level_k)[1:3] == [8, 1]
+
+
 def test_picks_clamped_to_candidates():
     p = L.problem(1, 1, 1024, levels=2, topk=16)  # 4 coarsest tokens
     s = L.llsa_sizes_query(p)
@@ -70,6 +81,7 @@ def test_picks_clamped_to_candidates():
     (dict(scale=-1.0), L.LLSA_ERR_INVALID),
     (dict(head_dim=128), L.LLSA_ERR_UNSUPPORTED),
     (dict(block=32, seq_len=32 * 32 * 4), L.LLSA_ERR_UNSUPPORTED),
+    (dict(block=64, seq_len=4096 + 1024), L.LLSA_ERR_INVALID),   # not divisible by 64^2
     (dict(topk=33), L.LLSA_ERR_UNSUPPORTED),
     (dict(token_order=2), L.LLSA_ERR_INVALID),
     (dict(token_order=1, seq_len=2048), L.LLSA_ERR_INVALID),    # not a square image

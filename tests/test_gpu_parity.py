@@ -64,6 +64,14 @@ EDGE = [
     (1, 2, 4096, torch.bfloat16, 3, 2, 2, True, {"token_order": 1}),
     (1, 1, 256, torch.bfloat16, 2, 16, 1, True, {}),       # K = all blocks (dense reduction)
     (1, 1, 256, torch.float32, 2, 16, 1, True, {}),
+    # blocks of 64 tokens (4 MFMA tiles per block)
+    (1, 2, 8192, torch.bfloat16, 1, 8, 0, True, {"block": 64}),     # single level, 128 blocks
+    (1, 2, 64 * 37, torch.bfloat16, 1, 5, 0, True, {"block": 64}),  # 37 blocks: ragged tile groups
+    (1, 2, 16384, torch.bfloat16, 2, 8, 1, True, {"block": 64}),    # 16384 -> 256 -> 4
+    (1, 2, 8192, torch.float32, 2, 2, 1, True, {"block": 64}),
+    (1, 1, 2048, torch.bfloat16, 1, 32, 0, True, {"block": 64}),    # K = all 32 blocks
+    (2, 1, 8192, torch.bfloat16, 1, 8, 0, True, {"block": 64, "grad_dtype": torch.bfloat16}),
+    (1, 2, 16384, torch.bfloat16, 1, 4, 0, True, {"block": 64, "token_order": 1}),
 ]
 
 

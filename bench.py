@@ -185,14 +185,15 @@ def sweep_workloads():
 
 def transpose_scaling(L, dev, reps):
     """Level-1 key-major lists from real selections at growing N: the sparse
-    transpose (count / scan / fill) against the dense bit-mask baseline."""
+    transpose (count / scan / fill) against the dense bit-mask baseline; then
+    the whole backward (key-major lists of every level used + attention
+    backward) built either way."""
     import torch
     from hierarchical_top_sparse_mean_amd.inputs import Workload, workload_inputs
-    for N, heads, levels in ((4096, 16, 2), (16384, 16, 2), (65536, 16, 2), (262144, 4, 3),
-                             (1048576, 1, 3)):
-        w = Workload(f"n{N}", 1, heads, N, 64, torch.bfloat16, 16, levels, 8, levels - 1, False, True)
-        q, k, v, _ = workload_inputs(w)
-        q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    heads = 16
+    for N, levels in ((4096, 2), (16384, 2), (65536, 2), (262144, 3), (1048576, 3)):
+        w = Workload(f"n{N}", 1, heads, N, 64, torch.bfloat16, 16, levels, 8, levels - 1, True, True)
+        q, k, v, dout = (x.to(dev) for x in workload_inputs(w))
         p = L.problem(1, heads, N, levels=levels, topk=8, enrich=levels - 1)
         B = L.Buffers(p, backward=True)
         L.llsa_pool(p, q, k, v, B.pyr_q, B.pyr_k, B.pyr_v)
@@ -207,6 +208,24 @@ def transpose_scaling(L, dev, reps):
             "mask": lambda: L.llsa_index_transpose_mask(heads, n1, k1, n1, B.index_level(1), ptr, col,
                                                         mw, mws),
         }
+        L.llsa_attn_fwd(p, q, k, v, B.pyr_k, B.pyr_v, B.idx, B.o, B.lse)
+
+        def lists(kind):
+            for l in range(1, B.s.enrich + 2):
+                nl, kl = B.s.level_tokens[l], B.s.level_k[l]
+                pl, cl = B.csr_level(l)
+                if kind == "csr":
+                    L.llsa_index_transpose(heads, nl, kl, nl, B.index_level(l), pl, cl, B.tws, B.tws_bytes)
+                else:
+                    L.llsa_index_transpose_mask(heads, nl, kl, nl, B.index_level(l), pl, cl, mw, mws)
+
+        def backward(kind):
+            lists(kind)
+            L.llsa_attn_bwd(p, q, k, v, B.pyr_k, B.pyr_v, B.idx, B.csr_ptr, B.csr_col, B.o, B.lse,
+                            dout, B.dq, B.dk, B.dv, B.ws, B.ws.numel())
+
+        runs["csr_backward"] = lambda: backward("csr")
+        runs["mask_backward"] = lambda: backward("mask")
         out = {"transpose_scaling_tokens": N, "heads": heads, "key_blocks": n1, "picks": heads * n1 * k1,
                "mask_bytes": mws}
         for name, f in runs.items():
@@ -220,9 +239,12 @@ def transpose_scaling(L, dev, reps):
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / reps
             out[name + "_us"] = round(us, 2)
-            out[name + "_ns_per_pick"] = round(us * 1e3 / (heads * n1 * k1), 4)
+            if name.endswith("backward"):
+                out[name + "_ns_per_token"] = round(us * 1e3 / (heads * N), 4)
+            else:
+                out[name + "_ns_per_pick"] = round(us * 1e3 / (heads * n1 * k1), 4)
         print(json.dumps(out), flush=True)
-        del q, k, v, B, mw
+        del q, k, v, dout, B, mw
         torch.cuda.empty_cache()
 
 

@@ -3,21 +3,26 @@
 // Index Transpose"): query-major pick lists become key-major lists by a count
 // per key, an exclusive prefix sum and a fill.
 //
-// Four short kernels spread every matrix over many workgroups; none uses a
-// global atomic and none needs memory cleared beforehand:
-//  1 count  each workgroup counts the picks of a contiguous range of rows in
-//           an LDS histogram and writes the whole histogram out;
-//  2 prefix key by key (one thread per key), the histograms of the row ranges
-//           become each range's offset inside the key's run, and the key's
-//           total is kept;
-//  3 scan   per matrix, the exclusive prefix of the key totals: csr_ptr;
-//  4 fill   one wave per row range walks its picks in order, 64 at a time:
-//           every pick sets its lane's bit in an LDS mask of its key, so its
-//           rank among the chunk's picks of that key is a popcount, and the
-//           rows land in ascending order at csr_ptr plus the range's offset.
-// Keys are handled in windows of kTrWindow, each window by its own
-// workgroups (the LDS holds one window's counters), so any number of keys
-// takes the same path.
+// The transpose is a stable counting sort of the picks by key (stable: the
+// picks of one key keep their row order).  One pass sorts by up to 4096
+// buckets; it has four short kernels that spread every matrix over many
+// workgroups, use no global atomic and need no memory cleared beforehand:
+//  1 count  each workgroup counts the picks of a contiguous range of elements
+//           in an LDS histogram of the buckets and writes it out;
+//  2 prefix bucket by bucket (one thread each), the histograms of the ranges
+//           become each range's offset inside the bucket's run, and the
+//           bucket's total is kept;
+//  3 scan   per matrix, the exclusive prefix of the bucket totals;
+//  4 fill   one wave per range walks its picks in order, 64 at a time: every
+//           pick sets its lane's bit in an LDS mask of its bucket, so its rank
+//           among the chunk's picks of that bucket is a popcount, and picks
+//           land in element order at the scan plus the range's offset.
+// Up to 4096 keys, the bucket is the key and one pass writes csr_ptr and
+// csr_col.  Above, two passes (least significant digit first): the low 12
+// bits of the key, into a staging list of (key, row) pairs, then the high
+// bits, into csr_col; csr_ptr then comes from a binary search of every key in
+// the sorted keys.  Every pick is read once per pass whatever the number of
+// keys, and the histograms stay at 4096 buckets per range.
 #include <algorithm>
 
 #include "common.hpp"
@@ -26,57 +31,125 @@
 namespace llsa {
 
 constexpr int kTrThreads = 256;
-constexpr int kTrWindow = 4096;    // keys per LDS window of the count and fill
-constexpr int kTrChunk = 1024;     // picks per row range (workgroup) of the count and fill
+constexpr int kTrBits = 12;
+constexpr int kTrBuckets = 1 << kTrBits;   // buckets per pass (LDS counters and masks)
+constexpr int kTrChunk = 1024;             // target picks per range (workgroup) of count and fill
 constexpr int kTrMaxRanges = 64;
+
+// MODE 0: one pass, bucket = key, idx -> csr_col.
+// MODE 1: first of two passes, bucket = low digit, idx -> (key, row) pairs.
+// MODE 2: second pass, bucket = high digit, pairs -> csr_col and sorted keys.
 struct TrPlan {
-    int ranges;          // row ranges per matrix
-    int rows_per;        // rows per range
-    int windows;         // key windows per matrix
-    size_t hist_ints;    // nb * ranges * cols
-    size_t tot_ints;     // nb * cols
+    int ranges;          // element ranges per matrix
+    int per;             // elements per range
+    int buckets;         // buckets of the pass (second pass: of the high digit)
+    bool two_pass;
 };
 
-static TrPlan plan(int nb, int rows, int k, int cols) {
+static TrPlan plan(int rows, int k, int cols) {
     TrPlan p;
     const int64_t picks = (int64_t)rows * k;
     const int64_t want = (picks + kTrChunk - 1) / kTrChunk;
     p.ranges = (int)(want < 1 ? 1 : (want > kTrMaxRanges ? kTrMaxRanges : want));
-    p.rows_per = (rows + p.ranges - 1) / p.ranges;
-    p.windows = (cols + kTrWindow - 1) / kTrWindow;
-    p.hist_ints = (size_t)nb * p.ranges * cols;
-    p.tot_ints = (size_t)nb * cols;
+    p.per = (int)((picks + p.ranges - 1) / p.ranges);
+    p.two_pass = cols > kTrBuckets;
+    p.buckets = p.two_pass ? kTrBuckets : cols;
     return p;
 }
 
 static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
-size_t transpose_workspace_bytes(int nb, int rows, int k, int cols) {
-    const TrPlan p = plan(nb, rows, k, cols);
-    return align256(sizeof(int32_t) * p.hist_ints) + align256(sizeof(int32_t) * p.tot_ints);
+// Workspace: histograms [nb, ranges, buckets], bucket totals [nb, buckets],
+// and for two passes the first pass's scan [nb, buckets + 1], the second's
+// [nb, buckets + 1], the staged pairs (keys, rows) and the sorted keys
+// [nb, rows * k] each.
+struct TrWs {
+    int32_t *hist, *tot, *ptrA, *ptrB, *pkey, *prow, *skey;
+};
+
+static TrWs carve(void *ws, int nb, int rows, int k, const TrPlan &p, size_t *bytes) {
+    TrWs w{};
+    char *c = (char *)ws;
+    size_t off = 0;
+    auto take = [&](size_t n) {   // c == nullptr: sizes only
+        int32_t *r = c ? (int32_t *)(c + off) : nullptr;
+        off += align256(sizeof(int32_t) * n);
+        return r;
+    };
+    const size_t E = (size_t)rows * k;
+    w.hist = take((size_t)nb * p.ranges * p.buckets);
+    w.tot = take((size_t)nb * p.buckets);
+    if (p.two_pass) {
+        w.ptrA = take((size_t)nb * (kTrBuckets + 1));
+        w.ptrB = take((size_t)nb * (kTrBuckets + 1));
+        w.pkey = take((size_t)nb * E);
+        w.prow = take((size_t)nb * E);
+        w.skey = take((size_t)nb * E);
+    }
+    if (bytes) *bytes = off;
+    return w;
 }
 
-// 1: histogram of the picks of rows [r0, r1) of matrix b, keys of window
-// blockIdx.z.
-__global__ __launch_bounds__(kTrThreads) void tr_count_kernel(const int32_t *__restrict__ idx,
-                                                             int32_t *__restrict__ hist, int rows,
-                                                             int k, int cols, int ranges,
-                                                             int rows_per) {
-    __shared__ int32_t h[kTrWindow];
+size_t transpose_workspace_bytes(int nb, int rows, int k, int cols) {
+    size_t bytes = 0;
+    carve(nullptr, nb, rows, k, plan(rows, k, cols), &bytes);
+    return bytes;
+}
+
+// The picks a pass reads: element e of matrix b has a key and a row, or is
+// absent (key outside [0, cols), or past the staged count in the second pass).
+struct TrSrc {
+    const int32_t *idx;    // MODE 0 / 1: [nb, E]
+    const int32_t *pkey;   // MODE 2: [nb, E]
+    const int32_t *prow;
+    const int32_t *ptrA;   // MODE 2: staged count of matrix b at ptrA[b][kTrBuckets]
+    int64_t E;             // elements per matrix, rows * k
+    int k, cols;
+};
+
+template <int MODE>
+__device__ __forceinline__ int tr_count_of(const TrSrc &S, int b) {
+    if constexpr (MODE == 2)
+        return S.ptrA[(int64_t)b * (kTrBuckets + 1) + kTrBuckets];
+    else
+        return (int)S.E;
+}
+
+// bucket of element e (-1: absent); the pick's row goes to *row
+template <int MODE>
+__device__ __forceinline__ int tr_bucket(const TrSrc &S, int b, int64_t e, int n, int &key, int &row) {
+    if (e >= n) return -1;
+    const int64_t x = (int64_t)b * S.E + e;
+    if constexpr (MODE == 2) {
+        key = S.pkey[x];
+        row = S.prow[x];
+        return key >> kTrBits;
+    } else {
+        key = S.idx[x];
+        row = (int)(e / S.k);
+        if (key < 0 || key >= S.cols) return -1;
+        return MODE == 0 ? key : (key & (kTrBuckets - 1));
+    }
+}
+
+// 1: histogram of the buckets of elements [m * per, (m + 1) * per) of matrix b
+template <int MODE>
+__global__ __launch_bounds__(kTrThreads) void tr_count_kernel(TrSrc S, int32_t *__restrict__ hist,
+                                                             int buckets, int ranges, int per) {
+    __shared__ int32_t h[kTrBuckets];
     const int m = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int c0 = blockIdx.z * kTrWindow, wn = min(kTrWindow, cols - c0);
-    const int r0 = min(rows, m * rows_per), r1 = min(rows, r0 + rows_per);
-    const int32_t *I = idx + (int64_t)b * rows * k;
-    for (int c = tid; c < wn; c += kTrThreads) h[c] = 0;
+    for (int c = tid; c < buckets; c += kTrThreads) h[c] = 0;
     __syncthreads();
-    const int64_t e1 = (int64_t)r1 * k;
-    for (int64_t e = (int64_t)r0 * k + tid; e < e1; e += kTrThreads) {
-        const int c = I[e] - c0;
-        if (c >= 0 && c < wn) atomicAdd(&h[c], 1);
+    const int n = tr_count_of<MODE>(S, b);
+    const int64_t e0 = (int64_t)m * per, e1 = min((int64_t)n, e0 + per);
+    for (int64_t e = e0 + tid; e < e1; e += kTrThreads) {
+        int key, row;
+        const int c = tr_bucket<MODE>(S, b, e, n, key, row);
+        if (c >= 0) atomicAdd(&h[c], 1);
     }
     __syncthreads();
-    int32_t *H = hist + ((int64_t)b * ranges + m) * cols + c0;
-    for (int c = tid; c < wn; c += kTrThreads) H[c] = h[c];
+    int32_t *H = hist + ((int64_t)b * ranges + m) * buckets;
+    for (int c = tid; c < buckets; c += kTrThreads) H[c] = h[c];
 }
 
 // inclusive prefix sum across a wave
@@ -90,8 +163,8 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
     return v;
 }
 
-// 2: one thread per key c of matrix b: hist[b][m][c] becomes the number of
-// picks of c in ranges before m, tot[b][c] the key's total.
+// 2: one thread per bucket c of matrix b: hist[b][m][c] becomes the number of
+// picks of c in ranges before m, tot[b][c] the bucket's total.
 __global__ __launch_bounds__(kTrThreads) void tr_prefix_kernel(int32_t *__restrict__ hist,
                                                               int32_t *__restrict__ tot, int cols,
                                                               int ranges) {
@@ -109,7 +182,7 @@ __global__ __launch_bounds__(kTrThreads) void tr_prefix_kernel(int32_t *__restri
     tot[(int64_t)b * cols + c] = run;
 }
 
-// 3: per matrix b, ptr[b][c] = number of picks of keys < c.
+// 3: per matrix b, ptr[b][c] = number of picks of buckets < c.
 constexpr int kTrScanThreads = 1024;
 __global__ __launch_bounds__(kTrScanThreads) void tr_scan_kernel(const int32_t *__restrict__ tot,
                                                                 int32_t *__restrict__ ptr,
@@ -117,7 +190,7 @@ __global__ __launch_bounds__(kTrScanThreads) void tr_scan_kernel(const int32_t *
     __shared__ int32_t wsum[kTrScanThreads / kWave];
     const int b = blockIdx.x, tid = threadIdx.x;
     const int32_t *T = tot + (int64_t)b * cols;
-    // each thread owns a contiguous run of keys
+    // each thread owns a contiguous run of buckets
     const int per = (cols + kTrScanThreads - 1) / kTrScanThreads;
     const int c0 = min(cols, tid * per), c1 = min(cols, c0 + per);
     int local = 0;
@@ -132,57 +205,56 @@ __global__ __launch_bounds__(kTrScanThreads) void tr_scan_kernel(const int32_t *
         P[c] = run;
         run += T[c];
     }
-    if (tid == kTrScanThreads - 1) P[cols] = run;   // the last thread owns the last keys
+    if (tid == kTrScanThreads - 1) P[cols] = run;   // the last thread owns the last buckets
 }
 
-// 4: one wave per (row range, key window), picks in order, 64 at a time.
-// The pick of lane l with key c sets bit l of mask[c]; its rank among the
-// chunk's picks of c is the number of lower bits set, and the highest lane of
-// each key advances the key's count seen so far (seen[c]) by the popcount.
-// A pick lands at csr_ptr[c] + the range's offset for c + seen[c] + rank; the
-// two global terms are read per pick, one chunk ahead.
-__global__ __launch_bounds__(kWave) void tr_fill_ordered_kernel(const int32_t *__restrict__ idx,
-                                                               const int32_t *__restrict__ hist,
-                                                               const int32_t *__restrict__ ptr,
-                                                               int32_t *__restrict__ col, int rows,
-                                                               int k, int cols, int ranges,
-                                                               int rows_per) {
-    __shared__ int32_t seen[kTrWindow];
-    __shared__ uint64_t mask[kTrWindow];
+// 4: one wave per element range, picks in order, 64 at a time.  The pick of
+// lane l in bucket c sets bit l of mask[c]; its rank among the chunk's picks
+// of c is the number of lower bits set, and the highest lane of each bucket
+// advances the bucket's count seen so far (seen[c]) by the popcount.  A pick
+// lands at ptr[c] + the range's offset for c + seen[c] + rank; the two global
+// terms are read per pick, one chunk ahead.
+template <int MODE>
+__global__ __launch_bounds__(kWave) void tr_fill_kernel(TrSrc S, const int32_t *__restrict__ hist,
+                                                       const int32_t *__restrict__ ptr,
+                                                       int32_t *__restrict__ out_row,
+                                                       int32_t *__restrict__ out_key, int buckets,
+                                                       int ranges, int per) {
+    __shared__ int32_t seen[kTrBuckets];
+    __shared__ uint64_t mask[kTrBuckets];
     const int m = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-    const int c0 = blockIdx.z * kTrWindow, wn = min(kTrWindow, cols - c0);
-    const int32_t *H = hist + ((int64_t)b * ranges + m) * cols;
-    const int32_t *P = ptr + (int64_t)b * (cols + 1);
-    for (int c = lane; c < wn; c += kWave) {
+    const int32_t *H = hist + ((int64_t)b * ranges + m) * buckets;
+    const int32_t *P = ptr + (int64_t)b * (buckets + 1);
+    for (int c = lane; c < buckets; c += kWave) {
         seen[c] = 0;
         mask[c] = 0;
     }
-    const int r0 = min(rows, m * rows_per), r1 = min(rows, r0 + rows_per);
-    const int32_t *I = idx + (int64_t)b * rows * k;
-    int32_t *C = col + (int64_t)b * rows * k;
-    const int64_t e1 = (int64_t)r1 * k;
-    int64_t e = (int64_t)r0 * k + lane;
-    // key of pick x, or -1 outside the window (or out of range)
-    auto key_at = [&](int64_t x) {
-        const int c = x < e1 ? I[x] : -1;
-        return (c >= c0 && c < c0 + wn) ? c : -1;
-    };
-    int cn = key_at(e);
+    const int n = tr_count_of<MODE>(S, b);
+    const int64_t e0 = (int64_t)m * per, e1 = min((int64_t)n, e0 + per);
+    int32_t *OR = out_row + (int64_t)b * S.E;
+    int32_t *OK = MODE == 0 ? nullptr : out_key + (int64_t)b * S.E;
+    int64_t e = e0 + lane;
+    int kn = 0, rn = 0;
+    int cn = tr_bucket<MODE>(S, b, e < e1 ? e : n, n, kn, rn);
     int bn = cn >= 0 ? P[cn] + H[cn] : 0;
     __syncthreads();
     for (; e - lane < e1; e += kWave) {
-        const int c = cn, base = bn;
-        cn = key_at(e + kWave);
+        const int c = cn, base = bn, key = kn, row = rn;
+        cn = tr_bucket<MODE>(S, b, e + kWave < e1 ? e + kWave : n, n, kn, rn);
         bn = cn >= 0 ? P[cn] + H[cn] : 0;
         const bool ok = c >= 0;
-        const int cl = ok ? c - c0 : 0;
+        const int cl = ok ? c : 0;
         if (ok) atomicOr((unsigned long long *)&mask[cl], 1ull << lane);
         __syncthreads();
         const uint64_t mk = ok ? mask[cl] : 0ull;
         const int rank = __popcll(mk & ((1ull << lane) - 1ull));
-        if (ok) C[base + seen[cl] + rank] = (int32_t)(e / k);
+        if (ok) {
+            const int pos = base + seen[cl] + rank;
+            OR[pos] = row;
+            if constexpr (MODE != 0) OK[pos] = key;
+        }
         __syncthreads();
-        if (ok && (mk >> lane) == 1ull) {   // highest lane of its key in the chunk
+        if (ok && (mk >> lane) == 1ull) {   // highest lane of its bucket in the chunk
             seen[cl] += __popcll(mk);
             mask[cl] = 0ull;
         }
@@ -190,20 +262,65 @@ __global__ __launch_bounds__(kWave) void tr_fill_ordered_kernel(const int32_t *_
     }
 }
 
+// Two passes: ptr[b][c] = number of sorted keys below c (binary search).
+__global__ __launch_bounds__(kTrThreads) void tr_bounds_kernel(const int32_t *__restrict__ skey,
+                                                              const int32_t *__restrict__ ptrA,
+                                                              int32_t *__restrict__ ptr, int64_t E,
+                                                              int cols) {
+    const int b = blockIdx.y;
+    const int c = blockIdx.x * kTrThreads + threadIdx.x;
+    if (c > cols) return;
+    const int n = ptrA[(int64_t)b * (kTrBuckets + 1) + kTrBuckets];
+    const int32_t *K = skey + (int64_t)b * E;
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (K[mid] < c)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    ptr[(int64_t)b * (cols + 1) + c] = lo;
+}
+
+template <int MODE>
+static void tr_pass(const TrSrc &S, const TrPlan &p, int nb, int buckets, const TrWs &w,
+                    int32_t *scan_out, int32_t *out_row, int32_t *out_key, hipStream_t s) {
+    const dim3 grid((unsigned)p.ranges, (unsigned)nb);
+    hipLaunchKernelGGL(tr_count_kernel<MODE>, grid, dim3(kTrThreads), 0, s, S, w.hist, buckets,
+                       p.ranges, p.per);
+    const dim3 pgrid((unsigned)((buckets + kTrThreads - 1) / kTrThreads), (unsigned)nb);
+    hipLaunchKernelGGL(tr_prefix_kernel, pgrid, dim3(kTrThreads), 0, s, w.hist, w.tot, buckets, p.ranges);
+    hipLaunchKernelGGL(tr_scan_kernel, dim3((unsigned)nb), dim3(kTrScanThreads), 0, s, w.tot,
+                       scan_out, buckets);
+    hipLaunchKernelGGL(tr_fill_kernel<MODE>, grid, dim3(kWave), 0, s, S, w.hist, scan_out, out_row,
+                       out_key, buckets, p.ranges, p.per);
+}
+
 hipError_t launch_transpose(int nb, int rows, int k, int cols, const int32_t *idx, int32_t *ptr,
                             int32_t *col, void *ws, hipStream_t s) {
-    const TrPlan p = plan(nb, rows, k, cols);
-    int32_t *hist = (int32_t *)ws;
-    int32_t *tot = (int32_t *)((char *)hist + align256(sizeof(int32_t) * p.hist_ints));
-    const dim3 grid((unsigned)p.ranges, (unsigned)nb, (unsigned)p.windows);
-    hipLaunchKernelGGL(tr_count_kernel, grid, dim3(kTrThreads), 0, s, idx, hist, rows, k, cols,
-                       p.ranges, p.rows_per);
-    const dim3 pgrid((unsigned)((cols + kTrThreads - 1) / kTrThreads), (unsigned)nb);
-    hipLaunchKernelGGL(tr_prefix_kernel, pgrid, dim3(kTrThreads), 0, s, hist, tot, cols, p.ranges);
-    hipLaunchKernelGGL(tr_scan_kernel, dim3((unsigned)nb), dim3(kTrScanThreads), 0, s, tot, ptr,
-                       cols);
-    hipLaunchKernelGGL(tr_fill_ordered_kernel, grid, dim3(kWave), 0, s, idx, hist, ptr, col, rows, k,
-                       cols, p.ranges, p.rows_per);
+    const TrPlan p = plan(rows, k, cols);
+    const TrWs w = carve(ws, nb, rows, k, p, nullptr);
+    TrSrc S{};
+    S.idx = idx;
+    S.E = (int64_t)rows * k;
+    S.k = k;
+    S.cols = cols;
+    if (!p.two_pass) {
+        tr_pass<0>(S, p, nb, cols, w, ptr, col, nullptr, s);
+        return hipGetLastError();
+    }
+    // low digit: idx -> staged (key, row) pairs in (low digit, row) order
+    tr_pass<1>(S, p, nb, kTrBuckets, w, w.ptrA, w.prow, w.pkey, s);
+    // high digit: pairs -> csr_col and the sorted keys, in (key, row) order
+    TrSrc S2 = S;
+    S2.pkey = w.pkey;
+    S2.prow = w.prow;
+    S2.ptrA = w.ptrA;
+    const int hi_buckets = (cols + kTrBuckets - 1) >> kTrBits;
+    tr_pass<2>(S2, p, nb, hi_buckets, w, w.ptrB, col, w.skey, s);
+    const dim3 bgrid((unsigned)((cols + 1 + kTrThreads - 1) / kTrThreads), (unsigned)nb);
+    hipLaunchKernelGGL(tr_bounds_kernel, bgrid, dim3(kTrThreads), 0, s, w.skey, w.ptrA, ptr, S.E, cols);
     return hipGetLastError();
 }
 

@@ -146,7 +146,9 @@ int llsa_attn_fwd(const llsa_problem *p, const void *q, const void *k, const voi
  *      so ptr[n_cols] = n_rows * k; csr_col [n_batch, n_rows * k]: the rows
  *      that picked key c, ascending, at csr_col[ptr[c] .. ptr[c+1]).
  * workspace: at least llsa_index_transpose_workspace(...) bytes of device
- *      memory (per-range key histograms and key totals).
+ *      memory (per-range histograms and totals of up to 4096 buckets; above
+ *      4096 keys also a staging list of (key, row) pairs and sorted keys,
+ *      12 bytes per pick).
  * Limits: n_cols <= 2^24 and n_batch <= 65535 (LLSA_ERR_UNSUPPORTED).
  * An index outside [0, n_cols) is skipped: it is not listed, and ptr[n_cols]
  * then counts only the listed picks.  The output is deterministic.

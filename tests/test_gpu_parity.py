@@ -144,7 +144,7 @@ def test_deterministic_bitwise():
 # ------------------------------------------------------------- transpose --
 @pytest.mark.parametrize("nb,rows,k,cols", [(3, 100, 8, 100), (2, 4096, 8, 4096), (1, 37, 5, 23),
                                             (4, 64, 1, 64), (1, 16384, 8, 32768), (2, 50, 16, 1000),
-                                            (1, 4096, 8, 70000)])
+                                            (1, 4096, 8, 70000), (3, 2000, 8, 9000), (2, 9000, 3, 4097)])
 def test_transpose_parity(nb, rows, k, cols):
     _log(f"[parity] transpose {nb} {rows} {k} {cols}")
     rng = np.random.default_rng(rows * 31 + k)
@@ -166,6 +166,34 @@ def test_transpose_parity(nb, rows, k, cols):
     assert np.array_equal(ptr.cpu().numpy(), ptr_o)
     assert np.array_equal(col.cpu().numpy(), col_o)
     check_csr_valid(idx, ptr.cpu().numpy(), col.cpu().numpy())
+
+
+@pytest.mark.parametrize("cols", [100, 9000])
+def test_transpose_skips_out_of_range(cols):
+    # indices outside [0, cols) are not listed (one pass and two passes)
+    nb, rows, k = 2, 300, 6
+    rng = np.random.default_rng(cols)
+    idx = np.stack([np.stack([np.sort(rng.choice(cols, k, replace=False)) for _ in range(rows)])
+                    for _ in range(nb)]).astype(np.int32)
+    bad = rng.random(idx.shape) < 0.1
+    idx[bad] = np.where(rng.random(int(bad.sum())) < 0.5, -1, cols + 7)
+    d_idx = torch.from_numpy(idx).cuda()
+    ptr = torch.empty((nb, cols + 1), dtype=torch.int32, device="cuda")
+    col = torch.full((nb, rows * k), -5, dtype=torch.int32, device="cuda")
+    ws_bytes = L.llsa_index_transpose_workspace(nb, rows, k, cols)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    L.llsa_index_transpose(nb, rows, k, cols, d_idx, ptr, col, ws, ws_bytes)
+    torch.cuda.synchronize()
+    ptr, col = ptr.cpu().numpy(), col.cpu().numpy()
+    for b in range(nb):
+        r_of = np.repeat(np.arange(rows), k)
+        key = idx[b].ravel()
+        ok = (key >= 0) & (key < cols)
+        order = np.lexsort((r_of[ok], key[ok]))   # by key, then row
+        n = int(ok.sum())
+        assert ptr[b, cols] == n and ptr[b, 0] == 0
+        assert np.array_equal(np.diff(ptr[b]), np.bincount(key[ok], minlength=cols))
+        assert np.array_equal(col[b, :n], r_of[ok][order])
 
 
 @pytest.mark.parametrize("nb,rows,k,cols", [(3, 100, 8, 100), (2, 4096, 8, 4096), (1, 37, 5, 23),

@@ -178,15 +178,21 @@ __device__ __forceinline__ float dot8(bf16x8 a, bf16x8 b) {
 // x ~= hi + lo with both parts in bf16 (relative error about 2^-17): the
 // gradient contractions run as two bf16 MFMAs so that rounding dS or P to
 // bf16 does not limit the accuracy of sums over hundreds of queries.
+// The empty asm statements pin each packed pair in its register: without
+// them the compiler re-converts element by element and re-packs with
+// v_perm_b32 wherever the value feeds a 16x16x16 MFMA operand.
 __device__ __forceinline__ void split4(const float (&x)[4], bf16x4 &hi, bf16x4 &lo) {
     const f32x4 xv = {x[0], x[1], x[2], x[3]};
-    hi = to_bf16x4(xv);
-    const u32x2 hb = __builtin_bit_cast(u32x2, hi);   // hi widened back by shifts
-    const f32x4 back = {__builtin_bit_cast(float, hb[0] << 16),
+    u32x2 hb = __builtin_bit_cast(u32x2, to_bf16x4(xv));
+    asm("" : "+v"(hb));
+    const f32x4 back = {__builtin_bit_cast(float, hb[0] << 16),   // hi widened back by shifts
                         __builtin_bit_cast(float, hb[0] & 0xffff0000u),
                         __builtin_bit_cast(float, hb[1] << 16),
                         __builtin_bit_cast(float, hb[1] & 0xffff0000u)};
-    lo = to_bf16x4(xv - back);
+    u32x2 lb = __builtin_bit_cast(u32x2, to_bf16x4(xv - back));
+    asm("" : "+v"(lb));
+    hi = __builtin_bit_cast(bf16x4, hb);
+    lo = __builtin_bit_cast(bf16x4, lb);
 }
 
 // Operand rows of coarse tile ct for query block ib: lane row = entry ct*16+c16.
@@ -828,12 +834,18 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
     };
     const float *ld_src = lane < kBlock ? lse : ws.D;
     const int lrow = lane >> 3, lcol = (lane & 7) * 8;
+    const uint32_t head_bytes = (uint32_t)a.N * kHeadDim * 2;
+    const Rsrc rq = make_rsrc(q + head_off, head_bytes), rdo = make_rsrc(dout + head_off, head_bytes);
+    // byte offset (within the head) of column lcol of row r of tile b
+    auto brow = [&](int b, int r) {
+        return ((uint32_t)tok_row_o<ORD>(a.tm, b * kBlock + r) * kHeadDim + lcol) * 2u;
+    };
     auto load_pair = [&](int ib, Pair &X) {
-        const int64_t o0 = head_off + trow(ib, lrow) + lcol, o1 = head_off + trow(ib, lrow + 8) + lcol;
-        X.qa0 = load_bf16x8(q + o0);
-        X.qa1 = load_bf16x8(q + o1);
-        X.da0 = load_bf16x8(dout + o0);
-        X.da1 = load_bf16x8(dout + o1);
+        const uint32_t o0 = brow(ib, lrow), o1 = brow(ib, lrow + 8);
+        X.qa0 = buf_load_bf16x8(rq, o0);
+        X.qa1 = buf_load_bf16x8(rq, o1);
+        X.da0 = buf_load_bf16x8(rdo, o0);
+        X.da1 = buf_load_bf16x8(rdo, o1);
         // lse is stored by token row, D by sequence position
         const int pos = ib * kBlock + c16;
         X.ld = ld_src[(int64_t)h * a.N + (lane < kBlock ? tok_row_o<ORD>(a.tm, pos) : pos)];
@@ -865,12 +877,20 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
         bf16x4 phi, plo, dhi, dlo;
         split4(pp, phi, plo);
         split4(ds, dhi, dlo);
+        // hi and lo parts as two 16x16x16 products each (the same MFMA time as
+        // one 16x16x32 over the duplicated dO / Q column, without the copies)
+        bf16x4 dT[4], qT[4];
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-            const bf16x4 dT = lds_read_tr4(&lds_do[rofs + 16 * dt]);
-            const bf16x4 qT = lds_read_tr4(&lds_q[rofs + 16 * dt]);
-            dva[dt] = mfma_bf16_32(cat8(phi, plo), cat8(dT, dT), dva[dt]);
-            dka[dt] = mfma_bf16_32(cat8(dhi, dlo), cat8(qT, qT), dka[dt]);
+            dT[dt] = lds_read_tr4(&lds_do[rofs + 16 * dt]);
+            qT[dt] = lds_read_tr4(&lds_q[rofs + 16 * dt]);
+            dva[dt] = mfma_bf16_16(phi, dT[dt], dva[dt]);
+            dka[dt] = mfma_bf16_16(dhi, qT[dt], dka[dt]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            dva[dt] = mfma_bf16_16(plo, dT[dt], dva[dt]);
+            dka[dt] = mfma_bf16_16(dlo, qT[dt], dka[dt]);
         }
     };
     // The segment's query blocks are read 64 at a time into one register

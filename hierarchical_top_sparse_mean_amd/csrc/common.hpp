@@ -67,6 +67,20 @@ __device__ __forceinline__ void store_bf16x8(__bf16 *p, bf16x8 v) {
     *reinterpret_cast<u32x4 *>(p) = __builtin_bit_cast(u32x4, v);
 }
 
+// Buffer resource over the n_bytes at p (p the same for the whole wave):
+// loads through it take a 32-bit byte offset, which saves the 64-bit address
+// arithmetic of a global load, and read zero at offsets past n_bytes.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void *p, uint32_t n_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)n_bytes, 0x00020000);
+}
+__device__ __forceinline__ bf16x8 buf_load_bf16x8(Rsrc r, uint32_t off) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load_f32(Rsrc r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 __device__ __forceinline__ bf16x8 f32_to_bf16x8(f32x4 a, f32x4 b) {
     return cat8(to_bf16x4(a), to_bf16x4(b));
 }

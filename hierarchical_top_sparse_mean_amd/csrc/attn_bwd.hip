@@ -527,7 +527,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
         store_bf16x8(dst + (lrow + 8) * kTS + lcol, r1);
     };
     // element offset (within the head) of row r of sequence block b
-    auto trow = [&](int b, int r) { return (int64_t)tok_row_o<ORD>(a.tm, b * kBlock + r) * kHeadDim; };
+    auto trow = [&](int b, int r) { return (int64_t)tok_tile_row<ORD>(a.tm, b, r) * kHeadDim; };
     auto load_tile = [&](int u, TileRegs &R) {
         const int f = __builtin_amdgcn_readlane(fidx, u);
         const int64_t o0 = head_off + trow(f, lrow) + lcol, o1 = head_off + trow(f, lrow + 8) + lcol;
@@ -547,7 +547,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
         X.qa1 = load_bf16x8(q + o1);
         X.da0 = load_bf16x8(dout + o0);
         X.da1 = load_bf16x8(dout + o1);
-        X.lse2 = lse[(int64_t)h * a.N + tok_row_o<ORD>(a.tm, b * kBlock + c16)] * kLog2e;
+        X.lse2 = lse[(int64_t)h * a.N + tok_tile_row<ORD>(a.tm, b, c16)] * kLog2e;
     };
     QRegs X;
     load_q(0, X);
@@ -806,7 +806,7 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
     const int fb = f / SUB;            // its key block
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
     // element offset (within the head) of row r of 16-token tile b
-    auto trow = [&](int b, int r) { return (int64_t)tok_row_o<ORD>(a.tm, b * kBlock + r) * kHeadDim; };
+    auto trow = [&](int b, int r) { return (int64_t)tok_tile_row<ORD>(a.tm, b, r) * kHeadDim; };
     const int32_t *P = csr_ptr + (int64_t)h * (a.n1 + 1);
     const int32_t *C = csr_col + (int64_t)h * a.n1 * a.K1;
     const int e0 = __builtin_amdgcn_readfirstlane(P[fb]), e1 = __builtin_amdgcn_readfirstlane(P[fb + 1]);
@@ -838,7 +838,7 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
     const Rsrc rq = make_rsrc(q + head_off, head_bytes), rdo = make_rsrc(dout + head_off, head_bytes);
     // byte offset (within the head) of column lcol of row r of tile b
     auto brow = [&](int b, int r) {
-        return ((uint32_t)tok_row_o<ORD>(a.tm, b * kBlock + r) * kHeadDim + lcol) * 2u;
+        return ((uint32_t)tok_tile_row<ORD>(a.tm, b, r) * kHeadDim + lcol) * 2u;
     };
     auto load_pair = [&](int ib, Pair &X) {
         const uint32_t o0 = brow(ib, lrow), o1 = brow(ib, lrow + 8);
@@ -847,8 +847,7 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
         X.da0 = buf_load_bf16x8(rdo, o0);
         X.da1 = buf_load_bf16x8(rdo, o1);
         // lse is stored by token row, D by sequence position
-        const int pos = ib * kBlock + c16;
-        X.ld = ld_src[(int64_t)h * a.N + (lane < kBlock ? tok_row_o<ORD>(a.tm, pos) : pos)];
+        X.ld = ld_src[(int64_t)h * a.N + (lane < kBlock ? tok_tile_row<ORD>(a.tm, ib, c16) : ib * kBlock + c16)];
     };
     auto compute = [&](const Pair &X) {
         wave_lds_sync();

@@ -310,7 +310,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
     // 128-byte rows per instruction (lane l: rows l / 8 and l / 8 + 8, 16-byte
     // chunk l % 8); rows reach the MFMA operand layout through LDS
     // element offset (within the head) of row r of sequence block b
-    auto trow = [&](int b, int r) { return (int64_t)tok_row_o<ORD>(a.tm, b * kBlock + r) * kHeadDim; };
+    auto trow = [&](int b, int r) { return (int64_t)tok_tile_row<ORD>(a.tm, b, r) * kHeadDim; };
     const int lr = lane >> 3, lc = (lane & 7) * 8;
     const bf16x8 qr0 = load_bf16x8(q + head_off + trow(ib, lr) + lc);
     const bf16x8 qr1 = load_bf16x8(q + head_off + trow(ib, lr + 8) + lc);
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
     wave_lds_sync();
     store_bf16x8(o + head_off + trow(ib, lr) + lc, load_bf16x8(vw + lr * kVStride + lc));
     store_bf16x8(o + head_off + trow(ib, lr + 8) + lc, load_bf16x8(vw + (lr + 8) * kVStride + lc));
-    if (g == 0) lse[(int64_t)h * a.N + tok_row_o<ORD>(a.tm, ib * kBlock + c16)] = (mx + log2f(lsum)) * kLn2;
+    if (g == 0) lse[(int64_t)h * a.N + tok_tile_row<ORD>(a.tm, ib, c16)] = (mx + log2f(lsum)) * kLn2;
 }
 
 // ---------------------------------------------------------------- f32 path

@@ -155,6 +155,20 @@ __device__ __forceinline__ int tok_row_o(const TokMap &m, int t) {
 __device__ __forceinline__ int tok_row(const TokMap &m, int t) {
     return m.order == 0 ? t : tok_row_o<1>(m, t);
 }
+// Storage row of row r (< 16) of 16-token tile b.  In order 1 a tile is a
+// 4 x 4 patch: the row is the patch corner's row (a function of b alone, so
+// scalar when b is) plus the fixed offset of r inside the patch.
+template <int ORD>
+__device__ __forceinline__ int tok_tile_row(const TokMap &m, int b, int r) {
+    if constexpr (ORD == 0) {
+        return b * 16 + r;
+    } else {
+        const uint32_t t0 = (uint32_t)b << 4;
+        const int corner = (int)((compact_even_bits(t0 >> 1) << m.log2S) | compact_even_bits(t0));
+        const int x = (r & 1) | ((r >> 1) & 2), y = ((r >> 1) & 1) | ((r >> 2) & 2);
+        return corner + (y << m.log2S) + x;
+    }
+}
 
 // Wave-scope ordering for data exchanged through LDS by lanes of one wave.
 __device__ __forceinline__ void wave_lds_sync() {

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ q, cons
 #pragma unroll
         for (int t = 0; t < kBlock; ++t)
             r[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                src + (int64_t)tok_row_o<ORD>(tm, lb * kBlock + t) * kHeadDim));
+                src + (int64_t)tok_tile_row<ORD>(tm, lb, t) * kHeadDim));
 #pragma unroll
         for (int t = 0; t < kBlock; ++t) {
             float f[EPC];
@@ -135,7 +135,8 @@ __global__ __launch_bounds__(256) void pool64_kernel(const T *__restrict__ q, co
 #pragma unroll
     for (int i = 0; i < NLD; ++i)
         rr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-            src + (int64_t)tok_row_o<ORD>(tm, lb * kB + r + RPI * i) * kHeadDim));
+            src + (int64_t)tok_tile_row<ORD>(tm, lb * (kB / kBlock) + (r + RPI * i) / kBlock,
+                                             (r + RPI * i) % kBlock) * kHeadDim));
     float acc[EPC];
 #pragma unroll
     for (int j = 0; j < EPC; ++j) acc[j] = 0.f;

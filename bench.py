@@ -387,6 +387,28 @@ def main():
             del gq, gk, gv, wsd
         del o_d, lse_d
 
+    fused = None
+    if w.backward:
+        # the fused variant: level-1 selection also counts its picks for the transpose
+        def separate():
+            L.llsa_select(p, B.pyr_q, B.pyr_k, B.idx)
+            L.transpose_levels(B)
+
+        def together():
+            L.llsa_select_transpose(p, B.pyr_q, B.pyr_k, B.idx, B.csr_ptr, B.csr_col, B.tws, B.tws_bytes)
+
+        fused = {}
+        for name, f in (("select_then_transpose_us", separate), ("select_transpose_fused_us", together)):
+            f()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(50):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            fused[name] = round(e0.elapsed_time(e1) * 1e3 / 50, 1)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_heads)
@@ -414,6 +436,7 @@ def main():
         "select_GB/s": detail["select"]["GB/s"],
         "attn_fwd_bf16_mfma_frac": detail["attn_fwd"].get("bf16_mfma_frac"),
         "dense_comparator": dense,
+        "fused_count_into_select": fused,
     }
     print(json.dumps(line))
 

@@ -119,6 +119,20 @@ int make_geometry(const llsa_problem *p, Geometry *g, llsa_sizes *sz) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? LLSA_OK : LLSA_ERR_HIP; }
 
+// Workspace of llsa_select_transpose: the level transposes run one after
+// another and share it; level 1 keeps the selection's counts when fused.
+size_t select_transpose_ws(const Geometry &g) {
+    const bool fused = llsa::select_count_fusable(g);
+    size_t need = 0;
+    for (int l = 1; l <= g.Le + 1; ++l) {
+        const size_t b = (l == 1 && fused)
+                             ? llsa::transpose_counted_workspace_bytes(g.bh, g.n[1], g.kl[1], g.n[1])
+                             : llsa::transpose_workspace_bytes(g.bh, g.n[l], g.kl[l], g.n[l]);
+        need = b > need ? b : need;
+    }
+    return need;
+}
+
 }  // namespace
 
 extern "C" {
@@ -146,7 +160,39 @@ int llsa_select(const llsa_problem *p, const float *pyr_q, const float *pyr_k, i
     const int st = make_geometry(p, &g, nullptr);
     if (st != LLSA_OK) return st;
     if (!aligned16(pyr_q) || !aligned16(pyr_k) || !aligned16(idx)) return LLSA_ERR_INVALID;
-    return status_of(llsa::launch_select(g, pyr_q, pyr_k, idx, (hipStream_t)stream));
+    return status_of(llsa::launch_select(g, pyr_q, pyr_k, idx, nullptr, (hipStream_t)stream));
+}
+
+size_t llsa_select_transpose_workspace(const llsa_problem *p) {
+    Geometry g;
+    if (make_geometry(p, &g, nullptr) != LLSA_OK) return 0;
+    return select_transpose_ws(g);
+}
+
+int llsa_select_transpose(const llsa_problem *p, const float *pyr_q, const float *pyr_k,
+                          int32_t *idx, int32_t *csr_ptr, int32_t *csr_col, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    Geometry g;
+    const int st = make_geometry(p, &g, nullptr);
+    if (st != LLSA_OK) return st;
+    if (g.bh > 65535 || g.n[1] > (1 << 24)) return LLSA_ERR_UNSUPPORTED;
+    if (!aligned16(pyr_q) || !aligned16(pyr_k) || !aligned16(idx) || !aligned16(csr_ptr) ||
+        !aligned16(csr_col))
+        return LLSA_ERR_INVALID;
+    const size_t need = select_transpose_ws(g);
+    if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return LLSA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    const bool fused = llsa::select_count_fusable(g);
+    hipError_t e = llsa::launch_select(g, pyr_q, pyr_k, idx,
+                                       fused ? llsa::transpose_counted_hist(workspace) : nullptr, s);
+    for (int l = 1; l <= g.Le + 1 && e == hipSuccess; ++l) {
+        const int32_t *il = idx + g.idx_off[l];
+        int32_t *pl = csr_ptr + g.ptr_off[l], *cl = csr_col + g.col_off[l];
+        e = (l == 1 && fused)
+                ? llsa::launch_transpose_counted(g.bh, g.n[1], g.kl[1], g.n[1], il, pl, cl, workspace, s)
+                : llsa::launch_transpose(g.bh, g.n[l], g.kl[l], g.n[l], il, pl, cl, workspace, s);
+    }
+    return status_of(e);
 }
 
 int llsa_attn_fwd(const llsa_problem *p, const void *q, const void *k, const void *v,

@@ -33,14 +33,22 @@ struct Geometry {
 
 hipError_t launch_pool(const Geometry &g, const void *q, const void *k, const void *v,
                        float *pq, float *pk, float *pv, hipStream_t s);
+// count_hist: when not null (and select_count_fusable), level 1 also counts
+// its picks per key into it, one range per 128 rows (the first transpose step).
 hipError_t launch_select(const Geometry &g, const float *pq, const float *pk, int32_t *idx,
-                         hipStream_t s);
+                         int32_t *count_hist, hipStream_t s);
+bool select_count_fusable(const Geometry &g);
+constexpr int kSelectRowsPerRange = 128;
 hipError_t launch_attn_fwd(const Geometry &g, const void *q, const void *k, const void *v,
                            const float *pk, const float *pv, const int32_t *idx, void *o,
                            float *lse, hipStream_t s);
 size_t transpose_workspace_bytes(int nb, int rows, int k, int cols);
 hipError_t launch_transpose(int nb, int rows, int k, int cols, const int32_t *idx,
                             int32_t *ptr, int32_t *col, void *ws, hipStream_t s);
+size_t transpose_counted_workspace_bytes(int nb, int rows, int k, int cols);
+int32_t *transpose_counted_hist(void *ws);
+hipError_t launch_transpose_counted(int nb, int rows, int k, int cols, const int32_t *idx,
+                                    int32_t *ptr, int32_t *col, void *ws, hipStream_t s);
 size_t transpose_mask_workspace_bytes(int nb, int rows, int cols);
 hipError_t launch_transpose_mask(int nb, int rows, int k, int cols, const int32_t *idx,
                                  int32_t *ptr, int32_t *col, void *ws, hipStream_t s);

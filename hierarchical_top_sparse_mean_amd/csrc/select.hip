@@ -86,6 +86,7 @@ __device__ __forceinline__ void sort_asc_u32(uint32_t (&a)[N]) {
 }
 
 constexpr int kSelTilesPerChunk = 8;
+constexpr int kSelCountKeys = 4096;   // keys a fused count can hold
 
 // parent == nullptr: coarsest level, candidates 0..n-1, row groups are
 // 16-row slices.  Otherwise: row group gi = 16 of the B children of parent
@@ -94,17 +95,29 @@ constexpr int kSelTilesPerChunk = 8;
 // SPLIT = 4: the four waves of a workgroup share one row group and take a
 // quarter of its candidate tiles each (the coarsest level has few groups);
 // their lists are merged through LDS at the end.
-template <int KM, int SPLIT>
-__global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ ql,
+// COUNT: the first step of the index transpose, fused.  The workgroup's 8
+// waves hold 128 consecutive rows of one head; it counts their picks per key
+// (n <= 4096 keys) in LDS and writes the histogram as range gi / 8 of
+// hist [heads, groups_per_head / 8, n].
+template <int KM, int SPLIT, bool COUNT>
+__global__ __launch_bounds__(COUNT ? 512 : 256) void select_kernel(const float *__restrict__ ql,
                                                      const float *__restrict__ kl,
                                                      const int32_t *__restrict__ parent,
                                                      int32_t *__restrict__ out, int n, int kout,
                                                      int kp, int groups_per_head,
-                                                     int64_t groups_total, int sub) {
+                                                     int64_t groups_total, int sub,
+                                                     int32_t *__restrict__ hist) {
     static_assert(SPLIT == 1 || SPLIT == 4, "a row group takes one wave or the whole workgroup");
+    static_assert(!COUNT || SPLIT == 1, "the fused count takes four row groups per workgroup");
     __shared__ uint64_t part_best[SPLIT == 1 ? 1 : SPLIT][kBlock][KM];
+    __shared__ int32_t hcount[COUNT ? kSelCountKeys : 1];
+    if constexpr (COUNT) {
+        for (int c = threadIdx.x; c < n; c += blockDim.x) hcount[c] = 0;
+        __syncthreads();
+    }
     const int part = SPLIT == 1 ? 0 : wave_id();
-    const int64_t gid = SPLIT == 1 ? (int64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + wave_id()
+    constexpr int kWpg = COUNT ? 8 : 4;   // waves per workgroup
+    const int64_t gid = SPLIT == 1 ? (int64_t)xcd_remap(blockIdx.x, gridDim.x) * kWpg + wave_id()
                                    : (int64_t)xcd_remap(blockIdx.x, gridDim.x);
     if (gid >= groups_total) return;
     const int h = (int)(gid / groups_per_head);
@@ -225,11 +238,22 @@ __global__ __launch_bounds__(256) void select_kernel(const float *__restrict__ q
         for (int i = 0; i < KM; ++i)
             if (i < kout) dst[i] = (int32_t)sel[i];
     }
+    if constexpr (COUNT) {
+        if (g == 0 && row_ok) {
+#pragma unroll
+            for (int i = 0; i < KM; ++i)
+                if (i < kout) atomicAdd(&hcount[sel[i]], 1);
+        }
+        __syncthreads();
+        const int nr = groups_per_head / kWpg;
+        int32_t *H = hist + ((int64_t)h * nr + gi / kWpg) * n;
+        for (int c = threadIdx.x; c < n; c += blockDim.x) H[c] = hcount[c];
+    }
 }
 
 template <int KM>
 static void launch_level(const Geometry &g, int l, const float *pq, const float *pk, int32_t *idx,
-                         hipStream_t s) {
+                         int32_t *hist, hipStream_t s) {
     const bool dense = (l == g.L);
     const int n = g.n[l];
     const int gph = dense ? (n + kBlock - 1) / kBlock : n / kBlock;
@@ -239,25 +263,43 @@ static void launch_level(const Geometry &g, int l, const float *pq, const float 
     const int ntiles = dense ? gph : kp * g.sub;
     // split a row group over the workgroup when groups are too few to fill
     // the chip and each has tiles enough for four waves
-    if (total < 1024 && ntiles >= 4 * 2)
-        hipLaunchKernelGGL((select_kernel<KM, 4>), dim3((unsigned)total), dim3(256), 0, s,
-                           pq + g.pyr_off[l], pk + g.pyr_off[l], parent, idx + g.idx_off[l], n,
-                           g.kl[l], kp, gph, total, g.sub);
-    else
-        hipLaunchKernelGGL((select_kernel<KM, 1>), dim3((unsigned)((total + 3) / 4)), dim3(256), 0,
+    if (hist != nullptr)   // fused count (select_count_fusable holds)
+        hipLaunchKernelGGL((select_kernel<KM, 1, true>), dim3((unsigned)(total / 8)), dim3(512), 0,
                            s, pq + g.pyr_off[l], pk + g.pyr_off[l], parent, idx + g.idx_off[l], n,
-                           g.kl[l], kp, gph, total, g.sub);
+                           g.kl[l], kp, gph, total, g.sub, hist);
+    else if (total < 1024 && ntiles >= 4 * 2)
+        hipLaunchKernelGGL((select_kernel<KM, 4, false>), dim3((unsigned)total), dim3(256), 0, s,
+                           pq + g.pyr_off[l], pk + g.pyr_off[l], parent, idx + g.idx_off[l], n,
+                           g.kl[l], kp, gph, total, g.sub, nullptr);
+    else
+        hipLaunchKernelGGL((select_kernel<KM, 1, false>), dim3((unsigned)((total + 3) / 4)), dim3(256),
+                           0, s, pq + g.pyr_off[l], pk + g.pyr_off[l], parent, idx + g.idx_off[l], n,
+                           g.kl[l], kp, gph, total, g.sub, nullptr);
+}
+
+// The level-1 selection can also count its picks for the transpose when the
+// level has at most 4096 keys, its row groups come eight to a workgroup and a
+// level-1 row group is not split over a workgroup.
+bool select_count_fusable(const Geometry &g) {
+    const int n = g.n[1];
+    const bool dense = g.L == 1;
+    const int gph = dense ? (n + kBlock - 1) / kBlock : n / kBlock;
+    const int64_t total = (int64_t)g.bh * gph;
+    const int ntiles = dense ? gph : g.kl[2] * g.sub;
+    const bool split = total < 1024 && ntiles >= 4 * 2;
+    return n <= kSelCountKeys && gph % 8 == 0 && !split;
 }
 
 hipError_t launch_select(const Geometry &g, const float *pq, const float *pk, int32_t *idx,
-                         hipStream_t s) {
+                         int32_t *count_hist, hipStream_t s) {
     for (int l = g.L; l >= 1; --l) {
+        int32_t *hist = l == 1 ? count_hist : nullptr;
         if (g.K <= 8)
-            launch_level<8>(g, l, pq, pk, idx, s);
+            launch_level<8>(g, l, pq, pk, idx, hist, s);
         else if (g.K <= 16)
-            launch_level<16>(g, l, pq, pk, idx, s);
+            launch_level<16>(g, l, pq, pk, idx, hist, s);
         else
-            launch_level<32>(g, l, pq, pk, idx, s);
+            launch_level<32>(g, l, pq, pk, idx, hist, s);
     }
     return hipGetLastError();
 }

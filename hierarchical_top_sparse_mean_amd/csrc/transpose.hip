@@ -324,6 +324,43 @@ hipError_t launch_transpose(int nb, int rows, int k, int cols, const int32_t *id
     return hipGetLastError();
 }
 
+// The same transpose when the selection already counted the picks (one range
+// per 128 rows, see select_count_fusable): prefix, scan and fill only.
+static TrPlan counted_plan(int rows, int k, int cols) {
+    TrPlan p;
+    p.ranges = rows / kSelectRowsPerRange;
+    p.per = kSelectRowsPerRange * k;
+    p.two_pass = false;
+    p.buckets = cols;
+    return p;
+}
+
+size_t transpose_counted_workspace_bytes(int nb, int rows, int k, int cols) {
+    size_t bytes = 0;
+    carve(nullptr, nb, rows, k, counted_plan(rows, k, cols), &bytes);
+    return bytes;
+}
+
+int32_t *transpose_counted_hist(void *ws) { return (int32_t *)ws; }
+
+hipError_t launch_transpose_counted(int nb, int rows, int k, int cols, const int32_t *idx,
+                                    int32_t *ptr, int32_t *col, void *ws, hipStream_t s) {
+    const TrPlan p = counted_plan(rows, k, cols);
+    const TrWs w = carve(ws, nb, rows, k, p, nullptr);
+    TrSrc S{};
+    S.idx = idx;
+    S.E = (int64_t)rows * k;
+    S.k = k;
+    S.cols = cols;
+    const dim3 grid((unsigned)p.ranges, (unsigned)nb);
+    const dim3 pgrid((unsigned)((cols + kTrThreads - 1) / kTrThreads), (unsigned)nb);
+    hipLaunchKernelGGL(tr_prefix_kernel, pgrid, dim3(kTrThreads), 0, s, w.hist, w.tot, cols, p.ranges);
+    hipLaunchKernelGGL(tr_scan_kernel, dim3((unsigned)nb), dim3(kTrScanThreads), 0, s, w.tot, ptr, cols);
+    hipLaunchKernelGGL(tr_fill_kernel<0>, grid, dim3(kWave), 0, s, S, w.hist, ptr, col, nullptr, cols,
+                       p.ranges, p.per);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------ mask baseline
 // The same key-major lists built the way the pages contrast the transpose
 // with: a dense bit mask of n_rows x n_cols per matrix, stored key-major

@@ -53,6 +53,9 @@ def _load():
     L.llsa_sizes_query.argtypes = [P, ctypes.POINTER(Sizes)]
     L.llsa_pool.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.llsa_select.argtypes = [P, _vp, _vp, _vp, _vp]
+    L.llsa_select_transpose_workspace.argtypes = [P]
+    L.llsa_select_transpose_workspace.restype = _c_sz
+    L.llsa_select_transpose.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp]
     L.llsa_attn_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.llsa_index_transpose_workspace.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32]
     L.llsa_index_transpose_workspace.restype = _c_sz
@@ -72,7 +75,7 @@ def _load():
     L.llsa_strerror.restype = ctypes.c_char_p
     for name in ("llsa_sizes_query", "llsa_pool", "llsa_select", "llsa_attn_fwd",
                  "llsa_index_transpose", "llsa_attn_bwd", "llsa_dense_attn_fwd",
-                 "llsa_dense_attn_bwd", "llsa_index_transpose_mask"):
+                 "llsa_dense_attn_bwd", "llsa_index_transpose_mask", "llsa_select_transpose"):
         getattr(L, name).restype = ctypes.c_int
     return L
 
@@ -122,6 +125,18 @@ def llsa_pool(p, q, k, v, pyr_q, pyr_k, pyr_v, stream=None):
 def llsa_select(p, pyr_q, pyr_k, idx, stream=None):
     _check("llsa_select", lib.llsa_select(ctypes.byref(p), _ptr(pyr_q), _ptr(pyr_k), _ptr(idx),
                                           _stream(stream)))
+
+
+def llsa_select_transpose_workspace(p) -> int:
+    return int(lib.llsa_select_transpose_workspace(ctypes.byref(p)))
+
+
+def llsa_select_transpose(p, pyr_q, pyr_k, idx, csr_ptr, csr_col, workspace, workspace_bytes,
+                          stream=None):
+    _check("llsa_select_transpose",
+           lib.llsa_select_transpose(ctypes.byref(p), _ptr(pyr_q), _ptr(pyr_k), _ptr(idx),
+                                     _ptr(csr_ptr), _ptr(csr_col), _ptr(workspace), workspace_bytes,
+                                     _stream(stream)))
 
 
 def llsa_attn_fwd(p, q, k, v, pyr_k, pyr_v, idx, o, lse, stream=None):
@@ -205,7 +220,8 @@ class Buffers:
             self.dk = torch.empty(shape, dtype=gdt, device=device)
             self.dv = torch.empty(shape, dtype=gdt, device=device)
             self.ws = torch.empty(max(int(s.bwd_workspace_bytes), 256), dtype=torch.uint8, device=device)
-            self.tws_bytes = int(s.transpose_workspace_bytes)
+            # one workspace serves the per-level transposes and the fused selection + transposes
+            self.tws_bytes = max(int(s.transpose_workspace_bytes), llsa_select_transpose_workspace(p))
             self.tws = torch.empty(max(self.tws_bytes, 256), dtype=torch.uint8, device=device)
 
     def pyramid_level(self, buf, l):

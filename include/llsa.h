@@ -160,6 +160,24 @@ int llsa_index_transpose(int32_t n_batch, int32_t n_rows, int32_t k, int32_t n_c
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Selection and the index transposes the backward pass reads, fused
+ * (explainer "Step 2" and "Step 4"): the same idx as llsa_select and the
+ * same csr_ptr / csr_col for levels 1..Le+1 as llsa_index_transpose(batch *
+ * heads, n_l, K_l, n_l, ...) at sizes.csr_*_offset[l].  When level 1 has at
+ * most 4096 tokens (and its rows come eight 16-row groups to a workgroup), its
+ * selection kernel also counts its picks per key, the first step of the
+ * transpose, so the picks are not read back for it.
+ * workspace: at least llsa_select_transpose_workspace(p) bytes of device
+ *      memory (16-byte aligned), shared by the level transposes in turn.
+ * Errors as llsa_select; LLSA_ERR_UNSUPPORTED also when batch * heads >
+ * 65535.
+ */
+size_t llsa_select_transpose_workspace(const llsa_problem *p);
+int llsa_select_transpose(const llsa_problem *p, const float *pyr_q, const float *pyr_k,
+                          int32_t *idx, int32_t *csr_ptr, int32_t *csr_col, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
  * Baseline for comparison with llsa_index_transpose: the same output built
  * from a dense bit mask of n_rows x n_cols per matrix (set every pick's bit,
  * then read every key's column), the mask-based route whose cost grows

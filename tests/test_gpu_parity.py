@@ -168,6 +168,40 @@ def test_transpose_parity(nb, rows, k, cols):
     check_csr_valid(idx, ptr.cpu().numpy(), col.cpu().numpy())
 
 
+@pytest.mark.parametrize("b,h,N,L_,K,Le,block", [
+    (1, 16, 65536, 2, 8, 1, 16),    # the measured workload: level-1 count fused into selection
+    (2, 4, 16384, 2, 8, 1, 16),
+    (1, 2, 768, 2, 2, 1, 16),       # 48 level-1 rows: not four 16-row groups per workgroup
+    (1, 2, 4096, 1, 8, 0, 16),      # single level, few groups: the split selection, no fusion
+    (4, 16, 4096, 1, 5, 0, 16),     # single level with 1024 row groups: fused dense level
+    (1, 4, 8192, 3, 4, 2, 16),      # three levels, two coarse transposes
+    (1, 2, 16384, 2, 8, 1, 64),
+])
+def test_select_transpose_fused_matches_separate(b, h, N, L_, K, Le, block):
+    # one fused call gives bit for bit the picks and key-major lists of
+    # llsa_select followed by one llsa_index_transpose per level
+    _log(f"[parity] fused select+transpose {b} {h} {N} L{L_} K{K} Le{Le} B{block}")
+    c = Case(b, h, N, torch.bfloat16, L_, K, Le, backward=True, sinus=round(N ** 0.5) ** 2 == N,
+             block=block)
+    B = L.Buffers(c.p, backward=True)
+    L.llsa_pool(c.p, c.q.cuda(), c.k.cuda(), c.v.cuda(), B.pyr_q, B.pyr_k, B.pyr_v)
+    L.llsa_select(c.p, B.pyr_q, B.pyr_k, B.idx)
+    L.transpose_levels(B)
+    torch.cuda.synchronize()
+    idx0 = [B.index_level(l).clone() for l in range(1, L_ + 1)]
+    csr0 = [tuple(t.clone() for t in B.csr_level(l)) for l in range(1, Le + 2)]
+    B.idx.fill_(-7)
+    B.csr_ptr.fill_(-7)
+    B.csr_col.fill_(-7)
+    L.llsa_select_transpose(c.p, B.pyr_q, B.pyr_k, B.idx, B.csr_ptr, B.csr_col, B.tws, B.tws_bytes)
+    torch.cuda.synchronize()
+    for l in range(1, L_ + 1):
+        assert torch.equal(B.index_level(l), idx0[l - 1]), l
+    for l in range(1, Le + 2):
+        ptr, col = B.csr_level(l)
+        assert torch.equal(ptr, csr0[l - 1][0]) and torch.equal(col, csr0[l - 1][1]), l
+
+
 @pytest.mark.parametrize("cols", [100, 9000])
 def test_transpose_skips_out_of_range(cols):
     # indices outside [0, cols) are not listed (one pass and two passes)

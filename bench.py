@@ -256,6 +256,8 @@ def main():
     ap.add_argument("--workload", default="n65536_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the fused count-into-select comparison (for profiled runs)")
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--sweep", action="store_true",
                     help="time every workload and variation (one JSON line each) instead of the bench line")
@@ -388,7 +390,7 @@ def main():
         del o_d, lse_d
 
     fused = None
-    if w.backward:
+    if w.backward and not args.no_fused:
         # the fused variant: level-1 selection also counts its picks for the transpose
         def separate():
             L.llsa_select(p, B.pyr_q, B.pyr_k, B.idx)

@@ -102,11 +102,13 @@ def cpu_baseline(w, max_heads):
                       f"pool+select+fwd+transpose+bwd in fp64 ({dt:.1f} s)"}
 
 
-def time_workload(L, w, steps, warmup, dev, grad_bf16=False, token_order=0):
+def time_workload(L, w, steps, warmup, dev, grad_bf16=False, token_order=0, overlap=False):
     """Runs `warmup` untimed and `steps` timed steps of the whole path on
     workload `w` (inputs resident on the GPU); returns the inputs, problem,
-    buffers, sizes, the mean per-call milliseconds (HIP events on the current
-    stream) and the wall-clock milliseconds per step."""
+    buffers, sizes, the mean per-call milliseconds (HIP events on the stream
+    each call runs on) and the wall-clock milliseconds per step.  overlap: the
+    index transposes, which only the backward reads, run on a second stream
+    (default priority) concurrently with the forward attention."""
     import torch
     from hierarchical_top_sparse_mean_amd.inputs import workload_inputs
     q, k, v, dout = workload_inputs(w)
@@ -118,33 +120,51 @@ def time_workload(L, w, steps, warmup, dev, grad_bf16=False, token_order=0):
     s = B.s
     bh = w.bh
     calls = ["pool", "select", "attn_fwd"] + (["transpose", "attn_bwd"] if w.backward else [])
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream() if overlap and w.backward else main
+
+    def transposes(stream):
+        for l in range(1, s.enrich + 2):
+            ptr, col = B.csr_level(l)
+            L.llsa_index_transpose(bh, s.level_tokens[l], s.level_k[l], s.level_tokens[l],
+                                   B.index_level(l), ptr, col, B.tws, B.tws_bytes, stream)
 
     def step(ev=None):
-        def mark(i):
+        # ev[c] = (start, end) events of call c, recorded on the call's stream
+        def mark(c, i, stream=None):
             if ev is not None:
-                ev[i].record()
-        mark(0)
+                ev[c][i].record(stream)
+        mark("pool", 0)
         L.llsa_pool(p, q, k, v, B.pyr_q, B.pyr_k, B.pyr_v)
-        mark(1)
+        mark("pool", 1)
+        mark("select", 0)
         L.llsa_select(p, B.pyr_q, B.pyr_k, B.idx)
-        mark(2)
+        mark("select", 1)
+        if w.backward and side is not main:
+            side.wait_stream(main)
+            mark("transpose", 0, side)
+            transposes(side)
+            mark("transpose", 1, side)
+        mark("attn_fwd", 0)
         L.llsa_attn_fwd(p, q, k, v, B.pyr_k, B.pyr_v, B.idx, B.o, B.lse)
-        mark(3)
+        mark("attn_fwd", 1)
         if w.backward:
-            for l in range(1, s.enrich + 2):
-                ptr, col = B.csr_level(l)
-                L.llsa_index_transpose(bh, s.level_tokens[l], s.level_k[l], s.level_tokens[l],
-                                       B.index_level(l), ptr, col, B.tws, B.tws_bytes)
-            mark(4)
+            if side is main:
+                mark("transpose", 0)
+                transposes(main)
+                mark("transpose", 1)
+            else:
+                main.wait_stream(side)
+            mark("attn_bwd", 0)
             L.llsa_attn_bwd(p, q, k, v, B.pyr_k, B.pyr_v, B.idx, B.csr_ptr, B.csr_col, B.o, B.lse,
                             dout, B.dq, B.dk, B.dv, B.ws, B.ws.numel())
-            mark(5)
+            mark("attn_bwd", 1)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    nev = len(calls) + 1
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+    events = [{c: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for c in calls}
+              for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -152,8 +172,8 @@ def time_workload(L, w, steps, warmup, dev, grad_bf16=False, token_order=0):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / steps
-    per_call = {c: sum(events[i][j].elapsed_time(events[i][j + 1]) for i in range(steps)) / steps
-                for j, c in enumerate(calls)}
+    per_call = {c: sum(events[i][c][0].elapsed_time(events[i][c][1]) for i in range(steps)) / steps
+                for c in calls}
     return q, k, v, dout, p, B, s, per_call, ms_per_step
 
 
@@ -256,6 +276,8 @@ def main():
     ap.add_argument("--workload", default="n65536_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--overlap", action="store_true",
+                    help="run the index transposes on a second stream, concurrently with the forward")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip the fused count-into-select comparison (for profiled runs)")
     ap.add_argument("--cpu-heads", type=int, default=16)
@@ -311,7 +333,8 @@ def main():
         print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
                           "launches": 3}))
         return
-    q, k, v, dout, p, B, s, per_call, ms_per_step = time_workload(L, w, args.steps, args.warmup, dev)
+    q, k, v, dout, p, B, s, per_call, ms_per_step = time_workload(L, w, args.steps, args.warmup, dev,
+                                                                  overlap=args.overlap)
     bh = w.bh
     calls = list(per_call)
     tokens = w.batch * w.seq_len

@@ -28,7 +28,7 @@
  *  - All shape, pointer and alignment checks run on the host before any HIP
  *    call; on an error status nothing is launched and no output is touched.
  *    Launch failures are reported as LLSA_ERR_HIP.
- *  - Supported set: head_dim = 64, block = 16, 1 <= levels <= 6,
+ *  - Supported set: head_dim = 64, block = 16 or 64, 1 <= levels <= 6,
  *    1 <= topk <= 32, dtype LLSA_F32 or LLSA_BF16, non-causal.  Other values
  *    give LLSA_ERR_UNSUPPORTED.
  */

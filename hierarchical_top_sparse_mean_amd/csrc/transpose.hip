@@ -283,6 +283,74 @@ __global__ __launch_bounds__(kTrThreads) void tr_bounds_kernel(const int32_t *__
     ptr[(int64_t)b * (cols + 1) + c] = lo;
 }
 
+// Small matrices (at most kTrSmallPicks picks, at most 4096 keys): the whole
+// transpose of one matrix in one workgroup -- count in LDS (keeping the picks
+// in LDS too), scan in LDS, then wave 0 places the picks in order as the fill
+// kernel does, with the bucket starts themselves as running cursors.  One
+// launch instead of four.
+constexpr int kTrSmallPicks = 8192;
+__global__ __launch_bounds__(kTrThreads) void tr_small_kernel(const int32_t *__restrict__ idx,
+                                                             int32_t *__restrict__ ptr,
+                                                             int32_t *__restrict__ col, int rows,
+                                                             int k, int cols) {
+    __shared__ int32_t base[kTrBuckets];
+    __shared__ uint64_t mask[kTrBuckets];
+    __shared__ int32_t wsum[kTrThreads / kWave];
+    __shared__ int32_t picks[kTrSmallPicks];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = lane_id();
+    const int64_t E = (int64_t)rows * k;
+    const int32_t *I = idx + (int64_t)b * E;
+    for (int c = tid; c < cols; c += kTrThreads) {
+        base[c] = 0;
+        mask[c] = 0;
+    }
+    __syncthreads();
+    for (int64_t e = tid; e < E; e += kTrThreads) {
+        const int c = I[e];
+        picks[e] = c;
+        if (c >= 0 && c < cols) atomicAdd(&base[c], 1);
+    }
+    __syncthreads();
+    // exclusive scan of the counts: each thread owns a contiguous run of keys
+    const int per = (cols + kTrThreads - 1) / kTrThreads;
+    const int c0 = min(cols, tid * per), c1 = min(cols, c0 + per);
+    int local = 0;
+    for (int c = c0; c < c1; ++c) local += base[c];
+    const int incl = wave_inclusive_scan(local);
+    if (lane == kWave - 1) wsum[wave_id()] = incl;
+    __syncthreads();
+    int run = incl - local;
+    for (int w = 0; w < wave_id(); ++w) run += wsum[w];
+    int32_t *P = ptr + (int64_t)b * (cols + 1);
+    for (int c = c0; c < c1; ++c) {
+        const int x = base[c];
+        P[c] = run;
+        base[c] = run;
+        run += x;
+    }
+    if (tid == kTrThreads - 1) P[cols] = run;
+    __syncthreads();
+    if (wave_id() != 0) return;
+    int32_t *C = col + (int64_t)b * E;
+    for (int64_t e0 = 0; e0 < E; e0 += kWave) {
+        const int64_t e = e0 + lane;
+        const int c = e < E ? picks[e] : -1;
+        const bool ok = c >= 0 && c < cols;
+        const int cl = ok ? c : 0;
+        if (ok) atomicOr((unsigned long long *)&mask[cl], 1ull << lane);
+        wave_lds_sync();
+        const uint64_t mk = ok ? mask[cl] : 0ull;
+        const int rank = __popcll(mk & ((1ull << lane) - 1ull));
+        if (ok) C[base[cl] + rank] = (int32_t)(e / k);
+        wave_lds_sync();
+        if (ok && (mk >> lane) == 1ull) {   // highest lane of its key in the chunk
+            base[cl] += __popcll(mk);
+            mask[cl] = 0ull;
+        }
+        wave_lds_sync();
+    }
+}
+
 template <int MODE>
 static void tr_pass(const TrSrc &S, const TrPlan &p, int nb, int buckets, const TrWs &w,
                     int32_t *scan_out, int32_t *out_row, int32_t *out_key, hipStream_t s) {
@@ -306,6 +374,11 @@ hipError_t launch_transpose(int nb, int rows, int k, int cols, const int32_t *id
     S.E = (int64_t)rows * k;
     S.k = k;
     S.cols = cols;
+    if (!p.two_pass && S.E <= kTrSmallPicks) {
+        hipLaunchKernelGGL(tr_small_kernel, dim3((unsigned)nb), dim3(kTrThreads), 0, s, idx, ptr, col,
+                           rows, k, cols);
+        return hipGetLastError();
+    }
     if (!p.two_pass) {
         tr_pass<0>(S, p, nb, cols, w, ptr, col, nullptr, s);
         return hipGetLastError();

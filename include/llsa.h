@@ -29,8 +29,9 @@
  *    call; on an error status nothing is launched and no output is touched.
  *    Launch failures are reported as LLSA_ERR_HIP.
  *  - Supported set: head_dim = 64, block = 16 or 64, 1 <= levels <= 6,
- *    1 <= topk <= 32, dtype LLSA_F32 or LLSA_BF16, non-causal.  Other values
- *    give LLSA_ERR_UNSUPPORTED.
+ *    1 <= topk <= 32, seq_len <= 2^25, batch * heads * seq_len < 2^31, dtype
+ *    LLSA_F32 or LLSA_BF16, non-causal.  Other values give
+ *    LLSA_ERR_UNSUPPORTED.
  */
 #ifndef LLSA_H
 #define LLSA_H

@@ -72,6 +72,8 @@ EDGE = [
     (1, 1, 2048, torch.bfloat16, 1, 32, 0, True, {"block": 64}),    # K = all 32 blocks
     (2, 1, 8192, torch.bfloat16, 1, 8, 0, True, {"block": 64, "grad_dtype": torch.bfloat16}),
     (1, 2, 16384, torch.bfloat16, 1, 4, 0, True, {"block": 64, "token_order": 1}),
+    (1, 2, 16384, torch.bfloat16, 2, 8, 0, True, {"block": 64}),                      # no enrichment
+    (1, 2, 16384, torch.bfloat16, 2, 3, 1, True, {"block": 64, "token_order": 1}),   # 128x128 image
 ]
 
 

@@ -444,20 +444,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     }
 }
 
-// Pass A for the common shape: K_1 = 8 fine picks per query block and one
-// coarse tile (at most 16 coarse entries) that no block can drop (K_1 < B).
-// The 16 query blocks under a level-2 node share their coarse picks, so the
-// workgroup stages that tile once in LDS as bf16 together with its log2
-// weights.  Every wave streams the 32 fine tiles of its 4 query blocks
-// through two register sets without a break at block boundaries (the next
-// block's first tiles and its Q / dO are in flight while a block's coarse
-// part is computed); the wave's 32 fine picks are read once, one per lane.
-constexpr int kFastK1 = 8;
-constexpr int kFastTiles = 4 * kFastK1;   // fine tiles per wave
+// Pass A for B = 16 with K_1 = K1T (even) fine picks per query block and one
+// coarse tile of at most 16 entries (CO) or none.  The 16 query blocks under
+// a level-2 node share their coarse picks, so the workgroup stages that tile
+// once in LDS as bf16 together with its log2 weights.  Every wave streams the
+// 4 K1T fine tiles of its 4 query blocks through two register sets without a
+// break at block boundaries (the next block's first tiles and its Q / dO are
+// in flight while a block's coarse part is computed); the wave's fine picks
+// are read once, one per lane.  From K1T = 16 on a level-2 pick can be fully
+// covered by a block's fine picks; it is then dropped for that block.
 constexpr int kPtS = 20;                  // float row stride of the P / dS exchange
 constexpr int kOutS = 68;                 // float row stride of a staged 16 x 64 output tile
 
-template <int ORD>
+template <int K1T, bool CO, int ORD>
 __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ pk, const float *__restrict__ pv, const int32_t *__restrict__ idx,
@@ -466,7 +465,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
     constexpr int kTileBytes = (4 * 4 + 2) * kTE * 2;          // K, V, Q, dO per wave + coarse K, V
     constexpr int kRedBytes = 4 * 2 * kBlock * kHeadDim * 4;   // coarse partials of 4 waves
     __shared__ __attribute__((aligned(16))) char smem[kTileBytes > kRedBytes ? kTileBytes : kRedBytes];
+    static_assert(K1T % 2 == 0 && K1T <= 32, "fine tiles stream in pairs, two pick registers");
+    constexpr int NT = 4 * K1T;   // fine tiles per wave
     __shared__ float cbias[kBlock];
+    __shared__ int ccol[kBlock];   // level-2 pooled token of each coarse entry (-1: other level)
     __shared__ __attribute__((aligned(16))) float lds_pt[4][2][kBlock * kPtS];  // coarse P, dS entry-major
     __shared__ __attribute__((aligned(16))) float lds_out[4][kBlock * kOutS];   // dQ rows
     typedef __bf16 Tile[kTE];
@@ -491,7 +493,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
     // ---- coarse tile, staged by the whole workgroup: thread (entry e, quarter p)
-    {
+    if constexpr (CO) {
         const int e = threadIdx.x >> 4, part = threadIdx.x & 15;
         int j = 0, pick = e;
         while (j < a.ncl - 1 && pick >= a.cl_k[j]) {
@@ -510,11 +512,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
         const bf16x4 vb = to_bf16x4(f32x4{vv[0], vv[1], vv[2], vv[3]});
         *reinterpret_cast<u32x2 *>(&ck[e * kTS + 4 * part]) = __builtin_bit_cast(u32x2, kb);
         *reinterpret_cast<u32x2 *>(&cv[e * kTS + 4 * part]) = __builtin_bit_cast(u32x2, vb);
-        if (part == 0) cbias[e] = ok ? 4.0f * (float)(js + 2) : -INFINITY;
+        if (part == 0) {
+            cbias[e] = ok ? 4.0f * (float)(js + 2) : -INFINITY;
+            ccol[e] = ok && js == 0 ? c : -1;
+        }
     }
 
-    // ---- this wave's fine picks: lane u < 32 holds pick u % 8 of block u / 8
-    const int fidx = lane < kFastTiles ? idx[((int64_t)h * a.n1 + ib0 + w * 4) * kFastK1 + lane] : 0;
+    // ---- this wave's fine picks: pick u (block u / K1T, pick u % K1T) sits in
+    // lane u of fidx0 (u < 64) or lane u - 64 of fidx1
+    const int32_t *wpicks = idx + ((int64_t)h * a.n1 + ib0 + w * 4) * K1T;
+    const int fidx0 = lane < NT ? wpicks[lane] : 0;
+    const int fidx1 = NT > kWave && lane < NT - kWave ? wpicks[kWave + lane] : 0;
+    auto pick = [&](int u) {
+        if constexpr (NT <= kWave)
+            return __builtin_amdgcn_readlane(fidx0, u);
+        else
+            return u < kWave ? __builtin_amdgcn_readlane(fidx0, u) : __builtin_amdgcn_readlane(fidx1, u - kWave);
+    };
     struct TileRegs {
         bf16x8 ka0, ka1, va0, va1;
     };
@@ -529,7 +543,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
     // element offset (within the head) of row r of sequence block b
     auto trow = [&](int b, int r) { return (int64_t)tok_tile_row<ORD>(a.tm, b, r) * kHeadDim; };
     auto load_tile = [&](int u, TileRegs &R) {
-        const int f = __builtin_amdgcn_readlane(fidx, u);
+        const int f = pick(u);
         const int64_t o0 = head_off + trow(f, lrow) + lcol, o1 = head_off + trow(f, lrow + 8) + lcol;
         R.ka0 = load_bf16x8(k + o0);
         R.ka1 = load_bf16x8(k + o1);
@@ -614,14 +628,38 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
                 accB[dt] = mfma_bf16_32(kk, pcat, accB[dt]);
             }
         };
-#pragma unroll
-        for (int t = 0; t < kFastK1; t += PD)
+        auto tile_pair = [&](int t) {
 #pragma unroll
             for (int r = 0; r < PD; ++r) {
-                const int u = jb * kFastK1 + t + r;
+                const int u = jb * K1T + t + r;
                 fine_tile(R[r]);
-                if (u + PD < kFastTiles) load_tile(u + PD, R[r]);
+                if (u + PD < NT) load_tile(u + PD, R[r]);
             }
+        };
+        if constexpr (K1T <= 8) {
+#pragma unroll
+            for (int t = 0; t < K1T; t += PD) tile_pair(t);
+        } else {   // unrolled fully, longer lists hoist too much into registers
+#pragma unroll 2
+            for (int t = 0; t < K1T; t += PD) tile_pair(t);
+        }
+        if constexpr (!CO) {
+            if (jb + 1 < 4) load_q(jb + 1, X);
+            const float Dq = sum4_groups(dsum);
+            if (g == 0) ws.D[(int64_t)h * a.N + row] = Dq;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                *reinterpret_cast<f32x4 *>(&lds_out[w][c16 * kOutS + 16 * dt + 4 * g]) =
+                    (accA[dt] - Dq * accB[dt]) * a.scale;
+            wave_lds_sync();
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int r = g + 4 * it;
+                store_grad4(dq, head_off + trow(ib0 + w * 4 + jb, r) + 4 * c16,
+                            *reinterpret_cast<const f32x4 *>(&lds_out[w][r * kOutS + 4 * c16]), a.grad_bf16);
+            }
+            continue;
+        } else {
         // ---- coarse entries: lane (query c16, entries 4g+i)
         const __bf16 *ckr = ck + c16 * kTS;
         const __bf16 *cvr = cv + c16 * kTS;
@@ -631,10 +669,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
                                        mfma_bf16_32(load_bf16x8(cvr + 8 * g), da0, zero4));
         if (jb + 1 < 4) load_q(jb + 1, X);   // next block's Q / dO in flight from here
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            cs[i] = fast_exp2(cs[i] * a.sl2 + cbias[4 * g + i] - lse2);
-            dsum += cs[i] * cdp[i];
+        for (int i = 0; i < 4; ++i) cs[i] = fast_exp2(cs[i] * a.sl2 + cbias[4 * g + i] - lse2);
+        if constexpr (K1T >= kBlock) {
+            if (a.drop) {   // entries whose 16 children are all fine picks of this block
+                int cov[4] = {0, 0, 0, 0}, cc[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) cc[i] = ccol[4 * g + i];
+                for (int t = 0; t < K1T; ++t) {
+                    const int f = pick(jb * K1T + t) >> 4;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) cov[i] += f == cc[i] ? 1 : 0;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (cov[i] == kBlock) cs[i] = 0.f;
+            }
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dsum += cs[i] * cdp[i];
         const float Dq = sum4_groups(dsum);
         if (g == 0) ws.D[(int64_t)h * a.N + row] = Dq;
         float ds[4];
@@ -684,7 +736,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
             store_grad4(dq, head_off + trow(ib0 + w * 4 + jb, r) + 4 * c16,
                         *reinterpret_cast<const f32x4 *>(&lds_out[w][r * kOutS + 4 * c16]), a.grad_bf16);
         }
+        }
     }
+    if constexpr (!CO) return;
     // ---- reduce the coarse partials over the 4 waves
     __syncthreads();
 #pragma unroll
@@ -1139,14 +1193,23 @@ hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, cons
         const int gph = (a.nt1 + kBlock - 1) / kBlock;
         const int nct = (a.ncoarse + kBlock - 1) / kBlock;
         const dim3 grid((unsigned)(g.bh * gph));
-        const bool fast = g.B == kBlock && g.L >= 2 && a.K1 == kFastK1 && nct == 1 &&
-                          a.n1 % kBlock == 0 && !(a.drop && a.K1 >= kBlock);
-        if (fast && g.order == 0)
-            hipLaunchKernelGGL(bwd_dq_fast_kernel<0>, grid, dim3(256), 0, s, (const __bf16 *)q,
-                               (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx, lse,
-                               (const __bf16 *)dout, dq, ws, a);
-        else if (fast)
-            hipLaunchKernelGGL(bwd_dq_fast_kernel<1>, grid, dim3(256), 0, s, (const __bf16 *)q,
+        // the streaming kernel for B = 16, at most one coarse tile and K_1 in {8, 16, 20, 32}
+        using Kern = void (*)(const __bf16 *, const __bf16 *, const __bf16 *, const float *,
+                              const float *, const int32_t *, const float *, const __bf16 *, void *,
+                              BwdWs, BwdArgs);
+        static const Kern table[2][2][4] = {
+            {{bwd_dq_fast_kernel<8, false, 0>, bwd_dq_fast_kernel<16, false, 0>,
+              bwd_dq_fast_kernel<20, false, 0>, bwd_dq_fast_kernel<32, false, 0>},
+             {bwd_dq_fast_kernel<8, true, 0>, bwd_dq_fast_kernel<16, true, 0>,
+              bwd_dq_fast_kernel<20, true, 0>, bwd_dq_fast_kernel<32, true, 0>}},
+            {{bwd_dq_fast_kernel<8, false, 1>, bwd_dq_fast_kernel<16, false, 1>,
+              bwd_dq_fast_kernel<20, false, 1>, bwd_dq_fast_kernel<32, false, 1>},
+             {bwd_dq_fast_kernel<8, true, 1>, bwd_dq_fast_kernel<16, true, 1>,
+              bwd_dq_fast_kernel<20, true, 1>, bwd_dq_fast_kernel<32, true, 1>}}};
+        const int kslot = a.K1 == 8 ? 0 : a.K1 == 16 ? 1 : a.K1 == 20 ? 2 : a.K1 == 32 ? 3 : -1;
+        const bool fast = g.B == kBlock && a.n1 % kBlock == 0 && nct <= 1 && kslot >= 0;
+        if (fast)
+            hipLaunchKernelGGL(table[g.order][nct][kslot], grid, dim3(256), 0, s, (const __bf16 *)q,
                                (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx, lse,
                                (const __bf16 *)dout, dq, ws, a);
         else if (nct == 0)

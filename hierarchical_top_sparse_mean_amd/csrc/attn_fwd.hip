@@ -455,6 +455,188 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
     if (g == 0) lse[(int64_t)h * a.N + tok_tile_row<ORD>(a.tm, ib, c16)] = (mx + log2f(lsum)) * kLn2;
 }
 
+// ---------------------------------------------------------- chunked path
+// The fast path's loads and layout for other shapes (B = 16): any K_1 (fine
+// tiles in chunks of 8, the last chunk masked), with a shared coarse tile of at
+// most 16 entries (CO) or none (no enrichment).  The coarse tile goes first,
+// then every chunk updates the running max and rescales (online softmax).
+// Several chunks need the registers of two waves per SIMD.
+template <int NCH, bool CO, int ORD>
+__global__ __launch_bounds__(256, NCH == 1 ? 3 : 2) void attn_fwd_chunk_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
+    const float *__restrict__ pk, const float *__restrict__ pv, const int32_t *__restrict__ idx,
+    __bf16 *__restrict__ o, float *__restrict__ lse, FwdArgs a) {
+    constexpr int KT = kFwdTiles;
+    constexpr int kHalf = KT / 2;   // V tiles staged at a time (LDS per wave)
+    __shared__ __attribute__((aligned(16))) __bf16 vs_all[4][kHalf * kTileElems];
+    __shared__ __attribute__((aligned(16))) __bf16 qs_all[4][kTileElems];
+    __shared__ __attribute__((aligned(16))) __bf16 ck[CO ? kTileElems : 8];
+    __shared__ __attribute__((aligned(16))) __bf16 cv[CO ? kTileElems : 8];
+    __shared__ float cbias[kBlock];
+    const int w = wave_id();
+    const int lane = lane_id();
+    const int g = lane >> 4, c16 = lane & 15;
+    const int64_t blk0 = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * 4;   // all 4 blocks valid
+    const int64_t blk = blk0 + w;
+    const int h = (int)(blk0 / a.n1);
+    const int ib0 = (int)(blk0 % a.n1);
+    const int ib = ib0 + w;
+    const int64_t head_off = (int64_t)h * a.N * kHeadDim;
+    const __bf16 *kh = k + head_off;
+    const __bf16 *vh = v + head_off;
+    __bf16 *vw = vs_all[w];
+    __bf16 *qw = qs_all[w];
+    auto trow = [&](int b, int r) { return (int64_t)tok_tile_row<ORD>(a.tm, b, r) * kHeadDim; };
+    const int lr = lane >> 3, lc = (lane & 7) * 8;
+    auto stage_rows = [&](__bf16 *dst, bf16x8 r0, bf16x8 r1) {
+        store_bf16x8(dst + lr * kVStride + lc, r0);
+        store_bf16x8(dst + (lr + 8) * kVStride + lc, r1);
+    };
+    stage_rows(qw, load_bf16x8(q + head_off + trow(ib, lr) + lc),
+               load_bf16x8(q + head_off + trow(ib, lr + 8) + lc));
+    const int32_t *fine = idx + blk * a.K1;
+    float m = -INFINITY, lsum = 0.f;
+    f32x4 oacc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int rofs = (4 * g + (c16 >> 2)) * kVStride + 4 * (c16 & 3);
+    wave_lds_sync();
+    const bf16x8 qa0 = load_bf16x8(qw + c16 * kVStride + 8 * g);
+    const bf16x8 qa1 = load_bf16x8(qw + c16 * kVStride + 32 + 8 * g);
+    if constexpr (CO) {
+        // coarse tile, staged by the whole workgroup: thread (entry e, quarter p)
+        const int e = threadIdx.x >> 4, part = threadIdx.x & 15;
+        int j, pick;
+        const bool ok = coarse_locate(a, e, j, pick);
+        const int js = ok ? j : 0, ps = ok ? pick : 0;
+        const int anc = ib0 >> (4 * (js + 1));   // ancestor at level js+2
+        const int c = idx[a.cl_idx_off[js] + ((int64_t)h * a.cl_n[js] + anc) * a.cl_k[js] + ps];
+        const int64_t row = a.cl_pyr_off[js] + ((int64_t)h * a.cl_n[js] + c) * kHeadDim + 4 * part;
+        f32x4 kk = *reinterpret_cast<const f32x4 *>(pk + row);
+        f32x4 vv = *reinterpret_cast<const f32x4 *>(pv + row);
+        if (!ok) kk = vv = f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<u32x2 *>(&ck[e * kVStride + 4 * part]) = __builtin_bit_cast(u32x2, to_bf16x4(kk));
+        *reinterpret_cast<u32x2 *>(&cv[e * kVStride + 4 * part]) = __builtin_bit_cast(u32x2, to_bf16x4(vv));
+        if (part == 0) cbias[e] = ok ? 4.0f * (float)(js + 2) : -INFINITY;
+        __syncthreads();
+        const __bf16 *ckr = ck + c16 * kVStride;
+        f32x4 sc = mfma_bf16_32(load_bf16x8(ckr + 32 + 8 * g), qa1,
+                                mfma_bf16_32(load_bf16x8(ckr + 8 * g), qa0, f32x4{0.f, 0.f, 0.f, 0.f})) * a.sl2;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sc[i] += cbias[4 * g + i];
+            if (drop_possible(a)) {
+                // a level-2 pick whose 16 children are all fine picks of this
+                // block is dropped for it (only level 2 can be covered: K_1 <= 32)
+                int j2, p2;
+                if (coarse_locate(a, 4 * g + i, j2, p2) && j2 == 0) {
+                    const int c = idx[a.cl_idx_off[0] + ((int64_t)h * a.cl_n[0] + (ib >> 4)) * a.cl_k[0] + p2];
+                    int cov = 0;
+                    for (int f = 0; f < a.K1; ++f) cov += (fine[f] >> 4) == c ? 1 : 0;
+                    if (cov == kBlock) sc[i] = -INFINITY;
+                }
+            }
+            mx = fmaxf(mx, sc[i]);
+        }
+        m = max4_groups(mx);
+        const float ms = m == -INFINITY ? 0.f : m;   // every entry absent or dropped
+        float pc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pc[i] = fast_exp2(sc[i] - ms);
+            lsum += pc[i];
+        }
+        const bf16x4 pcb = to_bf16x4(f32x4{pc[0], pc[1], pc[2], pc[3]});
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            oacc[dt] = mfma_bf16_16(lds_read_tr4(cv + rofs + 16 * dt), pcb, oacc[dt]);
+    }
+#pragma unroll 1
+    for (int c0 = 0; c0 < NCH * KT; c0 += KT) {
+        const int nt = min(KT, a.K1 - c0);   // live tiles of this chunk (>= 1)
+        bf16x8 kr[KT][2], vr[KT][2];
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            const int f = __builtin_amdgcn_readfirstlane(fine[c0 + min(t, nt - 1)]);
+            const int64_t o0 = trow(f, lr) + lc, o1 = trow(f, lr + 8) + lc;
+            kr[t][0] = load_bf16x8(kh + o0);
+            kr[t][1] = load_bf16x8(kh + o1);
+            vr[t][0] = load_bf16x8(vh + o0);
+            vr[t][1] = load_bf16x8(vh + o1);
+        }
+        f32x4 st[KT];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            wave_lds_sync();
+#pragma unroll
+            for (int t = 0; t < kHalf; ++t)
+                stage_rows(vw + t * kTileElems, kr[half * kHalf + t][0], kr[half * kHalf + t][1]);
+            wave_lds_sync();
+#pragma unroll
+            for (int t = 0; t < kHalf; ++t) {
+                const __bf16 *kro = vw + t * kTileElems + c16 * kVStride + 8 * g;
+                st[half * kHalf + t] =
+                    mfma_bf16_32(load_bf16x8(kro + 32), qa1,
+                                 mfma_bf16_32(load_bf16x8(kro), qa0, f32x4{0.f, 0.f, 0.f, 0.f})) * a.sl2;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            if (t >= nt) st[t] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[t][i]);
+        }
+        const float mnew = fmaxf(m, max4_groups(mx));   // finite: tile 0 of a chunk is live
+        const float alpha = fast_exp2(m - mnew);
+        m = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            wave_lds_sync();
+#pragma unroll
+            for (int t = 0; t < kHalf; ++t)
+                stage_rows(vw + t * kTileElems, vr[half * kHalf + t][0], vr[half * kHalf + t][1]);
+            wave_lds_sync();
+#pragma unroll
+            for (int tp = 0; tp < kHalf / 2; ++tp) {
+                const int t0 = half * kHalf + 2 * tp;
+                float p0[4], p1[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p0[i] = fast_exp2(st[t0][i] - m);
+                    p1[i] = fast_exp2(st[t0 + 1][i] - m);
+                    lsum += p0[i] + p1[i];
+                }
+                const bf16x8 pb = cat8(to_bf16x4(f32x4{p0[0], p0[1], p0[2], p0[3]}),
+                                       to_bf16x4(f32x4{p1[0], p1[1], p1[2], p1[3]}));
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    const bf16x4 v0 = lds_read_tr4(vw + (2 * tp) * kTileElems + rofs + 16 * dt);
+                    const bf16x4 v1 = lds_read_tr4(vw + (2 * tp + 1) * kTileElems + rofs + 16 * dt);
+                    oacc[dt] = mfma_bf16_32(cat8(v0, v1), pb, oacc[dt]);
+                }
+            }
+        }
+    }
+    // ---- normalise and store (whole rows through the free V slot)
+    lsum = sum4_groups(lsum);
+    const float inv = 1.0f / lsum;
+    wave_lds_sync();
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        const f32x4 r = oacc[dt] * inv;
+        *reinterpret_cast<u32x2 *>(vw + c16 * kVStride + 16 * dt + 4 * g) = __builtin_bit_cast(u32x2, to_bf16x4(r));
+    }
+    wave_lds_sync();
+    store_bf16x8(o + head_off + trow(ib, lr) + lc, load_bf16x8(vw + lr * kVStride + lc));
+    store_bf16x8(o + head_off + trow(ib, lr + 8) + lc, load_bf16x8(vw + (lr + 8) * kVStride + lc));
+    if (g == 0) lse[(int64_t)h * a.N + tok_tile_row<ORD>(a.tm, ib, c16)] = (m + log2f(lsum)) * kLn2;
+}
+
 // ---------------------------------------------------------------- f32 path
 __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
@@ -516,14 +698,30 @@ hipError_t launch_attn_fwd(const Geometry &g, const void *q, const void *k, cons
         const int64_t tiles = (int64_t)g.bh * a.nt1;
         const bool fast = g.B == kBlock && g.L >= 2 && a.K1 == 8 && a.ncoarse > 0 &&
                           a.ncoarse <= kBlock && !drop_possible(a) && a.n1 % 4 == 0;
-        if (fast && g.order == 0)
-            hipLaunchKernelGGL((attn_fwd_fast_kernel<8, 0>), dim3((unsigned)(blocks / 4)), dim3(256), 0,
-                               s, (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx,
-                               (__bf16 *)o, lse, a);
-        else if (fast)
-            hipLaunchKernelGGL((attn_fwd_fast_kernel<8, 1>), dim3((unsigned)(blocks / 4)), dim3(256), 0,
-                               s, (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx,
-                               (__bf16 *)o, lse, a);
+        // any K_1 and at most one coarse tile, in chunks of 8 fine tiles
+        const bool chunked = g.B == kBlock && a.n1 % 4 == 0 && a.ncoarse <= kBlock && a.K1 <= 4 * kFwdTiles;
+        const int nch = (a.K1 + kFwdTiles - 1) / kFwdTiles;
+        const bool co = a.ncoarse > 0;
+        using Kern = void (*)(const __bf16 *, const __bf16 *, const __bf16 *, const float *, const float *,
+                              const int32_t *, __bf16 *, float *, FwdArgs);
+        Kern kern = nullptr;
+        if (fast)
+            kern = g.order == 0 ? attn_fwd_fast_kernel<8, 0> : attn_fwd_fast_kernel<8, 1>;
+        else if (chunked) {
+            static const Kern table[2][2][4] = {
+                {{attn_fwd_chunk_kernel<1, false, 0>, attn_fwd_chunk_kernel<2, false, 0>,
+                  attn_fwd_chunk_kernel<3, false, 0>, attn_fwd_chunk_kernel<4, false, 0>},
+                 {attn_fwd_chunk_kernel<1, true, 0>, attn_fwd_chunk_kernel<2, true, 0>,
+                  attn_fwd_chunk_kernel<3, true, 0>, attn_fwd_chunk_kernel<4, true, 0>}},
+                {{attn_fwd_chunk_kernel<1, false, 1>, attn_fwd_chunk_kernel<2, false, 1>,
+                  attn_fwd_chunk_kernel<3, false, 1>, attn_fwd_chunk_kernel<4, false, 1>},
+                 {attn_fwd_chunk_kernel<1, true, 1>, attn_fwd_chunk_kernel<2, true, 1>,
+                  attn_fwd_chunk_kernel<3, true, 1>, attn_fwd_chunk_kernel<4, true, 1>}}};
+            kern = table[g.order][co ? 1 : 0][nch - 1];
+        }
+        if (kern != nullptr)
+            hipLaunchKernelGGL(kern, dim3((unsigned)(blocks / 4)), dim3(256), 0, s, (const __bf16 *)q,
+                               (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx, (__bf16 *)o, lse, a);
         else
             hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0,
                                s, (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx,

@@ -288,7 +288,7 @@ __global__ __launch_bounds__(kTrThreads) void tr_bounds_kernel(const int32_t *__
 // in LDS too), scan in LDS, then wave 0 places the picks in order as the fill
 // kernel does, with the bucket starts themselves as running cursors.  One
 // launch instead of four.
-constexpr int kTrSmallPicks = 8192;
+constexpr int kTrSmallPicks = 4096;
 __global__ __launch_bounds__(kTrThreads) void tr_small_kernel(const int32_t *__restrict__ idx,
                                                              int32_t *__restrict__ ptr,
                                                              int32_t *__restrict__ col, int rows,

@@ -758,6 +758,236 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
     }
 }
 
+// Pass A for blocks of 64 tokens: one workgroup per 4 consecutive query blocks
+// (16 query tiles: a group of the coarse partials), one wave per tile of the
+// block in hand.  A block's 4 tiles share its picks, so the workgroup loads
+// each picked key block (4 key tiles, K and V) once into LDS -- each wave one
+// tile, as whole rows -- and every wave uses all four: a quarter of the
+// gathers of one wave per tile.  Picked blocks alternate between two LDS
+// buffers (the next block's rows are in flight while one is used).  The
+// coarse tile (at most 16 entries, shared by the 4 blocks) and the partial
+// reduction are as in the B = 16 kernel; K_1 < B, so nothing is dropped.
+template <int ORD>
+__global__ __launch_bounds__(256, 2) void bwd_dq_b64_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
+    const float *__restrict__ pk, const float *__restrict__ pv, const int32_t *__restrict__ idx,
+    const float *__restrict__ lse, const __bf16 *__restrict__ dout, void *__restrict__ dq, BwdWs ws,
+    BwdArgs a) {
+    constexpr int kSub = 4;
+    typedef __bf16 Tile[kTE];
+    __shared__ __attribute__((aligned(16))) Tile kvbuf[2][2][kSub];   // [K, V][buffer][tile]
+    Tile(*kbuf)[kSub] = kvbuf[0];
+    Tile(*vbuf)[kSub] = kvbuf[1];
+    __shared__ __attribute__((aligned(16))) Tile lds_q[kSub];
+    __shared__ __attribute__((aligned(16))) Tile lds_do[kSub];
+    __shared__ __attribute__((aligned(16))) __bf16 ck[kTE];
+    __shared__ __attribute__((aligned(16))) __bf16 cv[kTE];
+    __shared__ float cbias[kBlock];
+    __shared__ __attribute__((aligned(16))) float lds_pt[kSub][2][kBlock * kPtS];
+    static_assert(sizeof(kvbuf) >= 4 * 2 * kBlock * kHeadDim * 4, "partials fit the buffers");
+    typedef float RedTile[2][kBlock * kHeadDim];
+    RedTile *lds_red = reinterpret_cast<RedTile *>(&kvbuf[0][0][0][0]);   // after the last block
+
+    const int w = wave_id();
+    const int lane = lane_id();
+    const int g = lane >> 4, c16 = lane & 15;
+    const int gph = a.n1 / kSub;   // workgroups per head
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = bid / gph;
+    const int G = bid % gph;       // partial group: query blocks 4G .. 4G + 3
+    const int64_t head_off = (int64_t)h * a.N * kHeadDim;
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    const bool co = a.ncoarse > 0;
+    auto trow = [&](int b, int r) { return (int64_t)tok_tile_row<ORD>(a.tm, b, r) * kHeadDim; };
+    const int lrow = lane >> 3, lcol = (lane & 7) * 8;
+    auto stage_rows = [&](__bf16 *dst, bf16x8 r0, bf16x8 r1) {
+        store_bf16x8(dst + lrow * kTS + lcol, r0);
+        store_bf16x8(dst + (lrow + 8) * kTS + lcol, r1);
+    };
+    if (co) {   // coarse tile, staged by the whole workgroup: thread (entry e, quarter p)
+        const int e = threadIdx.x >> 4, part = threadIdx.x & 15;
+        int j = 0, pick = e;
+        while (j < a.ncl - 1 && pick >= a.cl_k[j]) {
+            pick -= a.cl_k[j];
+            ++j;
+        }
+        const bool ok = e < a.ncoarse;
+        const int js = ok ? j : 0, ps = ok ? pick : 0;
+        const int c = idx[a.cl_idx_off[js] + ((int64_t)h * a.cl_n[js] + 4 * G / a.cl_span[js]) * a.cl_k[js] + ps];
+        const int64_t roff = a.cl_pyr_off[js] + ((int64_t)h * a.cl_n[js] + c) * kHeadDim + 4 * part;
+        f32x4 kk = *reinterpret_cast<const f32x4 *>(pk + roff);
+        f32x4 vv = *reinterpret_cast<const f32x4 *>(pv + roff);
+        if (!ok) kk = vv = zero4;
+        *reinterpret_cast<u32x2 *>(&ck[e * kTS + 4 * part]) = __builtin_bit_cast(u32x2, to_bf16x4(kk));
+        *reinterpret_cast<u32x2 *>(&cv[e * kTS + 4 * part]) = __builtin_bit_cast(u32x2, to_bf16x4(vv));
+        if (part == 0) cbias[e] = ok ? a.lgB * (float)(js + 2) : -INFINITY;
+    }
+    f32x4 dkc[4], dvc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        dkc[dt] = zero4;
+        dvc[dt] = zero4;
+    }
+    const int rofs = (4 * g + (c16 >> 2)) * kTS + 4 * (c16 & 3);  // transposed-read address
+    bf16x8 kr[2], vr[2];
+    for (int jb = 0; jb < kSub; ++jb) {
+        const int ib = 4 * G + jb;          // query block in hand
+        const int qt = ib * kSub + w;       // this wave's tile of it
+        const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
+        auto load_tile = [&](int j) {       // wave w's tile of picked block j
+            const int f = __builtin_amdgcn_readfirstlane(fine[j]) * kSub + w;
+            const int64_t o0 = head_off + trow(f, lrow) + lcol, o1 = head_off + trow(f, lrow + 8) + lcol;
+            kr[0] = load_bf16x8(k + o0);
+            kr[1] = load_bf16x8(k + o1);
+            vr[0] = load_bf16x8(v + o0);
+            vr[1] = load_bf16x8(v + o1);
+        };
+        load_tile(0);
+        const float lse2 = lse[(int64_t)h * a.N + tok_tile_row<ORD>(a.tm, qt, c16)] * kLog2e;
+        wave_lds_sync();
+        stage_rows(lds_q[w], load_bf16x8(q + head_off + trow(qt, lrow) + lcol),
+                   load_bf16x8(q + head_off + trow(qt, lrow + 8) + lcol));
+        stage_rows(lds_do[w], load_bf16x8(dout + head_off + trow(qt, lrow) + lcol),
+                   load_bf16x8(dout + head_off + trow(qt, lrow + 8) + lcol));
+        wave_lds_sync();
+        const bf16x8 qa0 = load_bf16x8(&lds_q[w][c16 * kTS + 8 * g]);
+        const bf16x8 qa1 = load_bf16x8(&lds_q[w][c16 * kTS + 32 + 8 * g]);
+        const bf16x8 da0 = load_bf16x8(&lds_do[w][c16 * kTS + 8 * g]);
+        const bf16x8 da1 = load_bf16x8(&lds_do[w][c16 * kTS + 32 + 8 * g]);
+        f32x4 accA[4], accB[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            accA[dt] = zero4;
+            accB[dt] = zero4;
+        }
+        float dsum = 0.f;
+        for (int j = 0; j < a.K1; ++j) {
+            const int buf = j & 1;
+            stage_rows(kbuf[buf][w], kr[0], kr[1]);
+            stage_rows(vbuf[buf][w], vr[0], vr[1]);
+            // the block's four key tiles staged; every wave is done with block j - 2
+            __syncthreads();
+            if (j + 1 < a.K1) load_tile(j + 1);
+#pragma unroll 1
+            for (int t = 0; t < kSub; ++t) {
+                const __bf16 *kt = kbuf[buf][t], *vt = vbuf[buf][t];
+                const f32x4 s = mfma_bf16_32(load_bf16x8(&kt[c16 * kTS + 32 + 8 * g]), qa1,
+                                             mfma_bf16_32(load_bf16x8(&kt[c16 * kTS + 8 * g]), qa0, zero4));
+                const f32x4 dp = mfma_bf16_32(load_bf16x8(&vt[c16 * kTS + 32 + 8 * g]), da1,
+                                              mfma_bf16_32(load_bf16x8(&vt[c16 * kTS + 8 * g]), da0, zero4));
+                float p[4], x[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[i] = fast_exp2(s[i] * a.sl2 - lse2);
+                    x[i] = p[i] * dp[i];
+                    dsum += x[i];
+                }
+                bf16x4 phi, plo, xhi, xlo;
+                split4(p, phi, plo);
+                split4(x, xhi, xlo);
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    const bf16x4 kT = lds_read_tr4(&kt[rofs + 16 * dt]);
+                    accA[dt] = mfma_bf16_16(kT, xhi, accA[dt]);
+                    accB[dt] = mfma_bf16_16(kT, phi, accB[dt]);
+                }
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    const bf16x4 kT = lds_read_tr4(&kt[rofs + 16 * dt]);
+                    accA[dt] = mfma_bf16_16(kT, xlo, accA[dt]);
+                    accB[dt] = mfma_bf16_16(kT, plo, accB[dt]);
+                }
+            }
+        }
+        float Dq;
+        if (co) {
+            // ---- coarse entries: lane (query c16, entries 4g+i)
+            const __bf16 *ckr = ck + c16 * kTS;
+            const __bf16 *cvr = cv + c16 * kTS;
+            f32x4 cs = mfma_bf16_32(load_bf16x8(ckr + 32 + 8 * g), qa1,
+                                    mfma_bf16_32(load_bf16x8(ckr + 8 * g), qa0, zero4));
+            const f32x4 cdp = mfma_bf16_32(load_bf16x8(cvr + 32 + 8 * g), da1,
+                                           mfma_bf16_32(load_bf16x8(cvr + 8 * g), da0, zero4));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                cs[i] = fast_exp2(cs[i] * a.sl2 + cbias[4 * g + i] - lse2);
+                dsum += cs[i] * cdp[i];
+            }
+            Dq = sum4_groups(dsum);
+            float ds[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ds[i] = cs[i] * (cdp[i] - Dq);
+            // P and dS entry-major through LDS: lane (entry c16, queries 4g+i)
+            wave_lds_sync();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lds_pt[w][0][(4 * g + i) * kPtS + c16] = cs[i];
+                lds_pt[w][1][(4 * g + i) * kPtS + c16] = ds[i];
+            }
+            wave_lds_sync();
+            const f32x4 p2v = *reinterpret_cast<const f32x4 *>(&lds_pt[w][0][c16 * kPtS + 4 * g]);
+            const f32x4 d2v = *reinterpret_cast<const f32x4 *>(&lds_pt[w][1][c16 * kPtS + 4 * g]);
+            float ds2[4], p2[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p2[i] = p2v[i];
+                ds2[i] = d2v[i];
+            }
+            bf16x4 dhi, dlo, d2hi, d2lo, p2hi, p2lo;
+            split4(ds, dhi, dlo);
+            split4(ds2, d2hi, d2lo);
+            split4(p2, p2hi, p2lo);
+            const bf16x8 dcat = cat8(dhi, dlo), d2cat = cat8(d2hi, d2lo), p2cat = cat8(p2hi, p2lo);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const bf16x4 kT = lds_read_tr4(&ck[rofs + 16 * dt]);
+                accA[dt] = mfma_bf16_32(cat8(kT, kT), dcat, accA[dt]);   // + Kc^T dS_c
+                const bf16x4 qT = lds_read_tr4(&lds_q[w][rofs + 16 * dt]);
+                const bf16x4 dT = lds_read_tr4(&lds_do[w][rofs + 16 * dt]);
+                dkc[dt] = mfma_bf16_32(d2cat, cat8(qT, qT), dkc[dt]);
+                dvc[dt] = mfma_bf16_32(p2cat, cat8(dT, dT), dvc[dt]);
+            }
+        } else {
+            Dq = sum4_groups(dsum);
+        }
+        if (g == 0) ws.D[(int64_t)h * a.N + (int64_t)qt * kBlock + c16] = Dq;
+        // dQ (lane: query c16, dims 16 dt + 4 g ..) through a quarter of the
+        // key buffers once every wave is done with them, then whole rows
+        // (lane l: row l / 16 + 4 it)
+        static_assert(sizeof(kvbuf) / 2 >= 4 * kBlock * kOutS * sizeof(float), "dQ staging fits");
+        float *stage = reinterpret_cast<float *>(&kvbuf[0][0][0][0]) + w * kBlock * kOutS;
+        __syncthreads();
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            *reinterpret_cast<f32x4 *>(&stage[c16 * kOutS + 16 * dt + 4 * g]) = (accA[dt] - Dq * accB[dt]) * a.scale;
+        wave_lds_sync();
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int r = g + 4 * it;
+            store_grad4(dq, head_off + trow(qt, r) + 4 * c16,
+                        *reinterpret_cast<const f32x4 *>(&stage[r * kOutS + 4 * c16]), a.grad_bf16);
+        }
+        __syncthreads();   // all waves done with this block's key buffers
+    }
+    if (!co) return;
+    // ---- reduce the coarse partials over the 4 waves (the key buffers are free)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ent = 4 * g + i, dim = 16 * dt + c16;
+            lds_red[w][0][ent * kHeadDim + dim] = dkc[dt][i] * a.scale;
+            lds_red[w][1][ent * kHeadDim + dim] = dvc[dt][i];
+        }
+    __syncthreads();
+    float *part = ws.partial + ((int64_t)h * a.npg + G) * a.ncoarse * 2 * kHeadDim;
+    for (int x = threadIdx.x; x < a.ncoarse * 2 * kHeadDim; x += 256) {
+        const int er = x / (2 * kHeadDim), kv = (x / kHeadDim) & 1, dim = x % kHeadDim;
+        const int oo = er * kHeadDim + dim;
+        part[x] = lds_red[0][kv][oo] + lds_red[1][kv][oo] + lds_red[2][kv][oo] + lds_red[3][kv][oo];
+    }
+}
+
 // ================================================================ pass B
 // One wave per pooled token c of level l (lanes = columns): the level-l rows
 // that picked c come from the CSR of I^(l); each lane looks up one row's slot
@@ -1012,6 +1242,151 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
     store_tile(dva, 1.0f, cv, dv);
 }
 
+// Pass C for blocks of 64 tokens: one workgroup per key block, one wave per
+// 16-key tile of it.  The 4 key tiles share the block's CSR segment, so the
+// workgroup loads each query block's 4 tiles (Q, dO rows and their lse, D)
+// once into LDS -- each wave one tile -- and every wave works through all
+// four: a quarter of the gathers of one wave per key tile.  Query blocks
+// alternate between two LDS buffers; the next one's rows are in flight while
+// one is used.
+template <int ORD>
+__global__ __launch_bounds__(256, 2) void bwd_dkv_b64_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
+    const float *__restrict__ lse, const __bf16 *__restrict__ dout, const int32_t *__restrict__ csr_ptr,
+    const int32_t *__restrict__ csr_col, void *__restrict__ dk, void *__restrict__ dv, BwdWs ws,
+    BwdArgs a) {
+    constexpr int kSub = 4;
+    __shared__ __attribute__((aligned(16))) __bf16 qbuf[2][kSub][kTE];
+    __shared__ __attribute__((aligned(16))) __bf16 dbuf[2][kSub][kTE];
+    __shared__ __attribute__((aligned(16))) float ldbuf[2][kSub][2 * kBlock];   // lse, D per query tile
+    const int w = wave_id();
+    const int lane = lane_id();
+    const int g = lane >> 4, c16 = lane & 15;
+    const int64_t kb = xcd_remap(blockIdx.x, gridDim.x);   // key block
+    const int h = (int)(kb / a.n1);
+    const int fb = (int)(kb % a.n1);
+    const int f = fb * kSub + w;   // this wave's key tile
+    const int64_t head_off = (int64_t)h * a.N * kHeadDim;
+    auto trow = [&](int b, int r) { return (int64_t)tok_tile_row<ORD>(a.tm, b, r) * kHeadDim; };
+    const int32_t *P = csr_ptr + (int64_t)h * (a.n1 + 1);
+    const int32_t *C = csr_col + (int64_t)h * a.n1 * a.K1;
+    const int e0 = __builtin_amdgcn_readfirstlane(P[fb]), e1 = __builtin_amdgcn_readfirstlane(P[fb + 1]);
+    f32x4 dka[4], dva[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        dka[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dva[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int lrow = lane >> 3, lcol = (lane & 7) * 8;
+    const int rofs = (4 * g + (c16 >> 2)) * kTS + 4 * (c16 & 3);
+    if (e1 > e0) {
+        const __bf16 *krow = k + head_off + trow(f, c16);
+        const __bf16 *vrow = v + head_off + trow(f, c16);
+        const bf16x8 kb0 = load_bf16x8(krow + 8 * g), kb1 = load_bf16x8(krow + 32 + 8 * g);
+        const bf16x8 vb0 = load_bf16x8(vrow + 8 * g), vb1 = load_bf16x8(vrow + 32 + 8 * g);
+        const uint32_t head_bytes = (uint32_t)a.N * kHeadDim * 2;
+        const Rsrc rq = make_rsrc(q + head_off, head_bytes), rdo = make_rsrc(dout + head_off, head_bytes);
+        auto brow = [&](int b, int r) {
+            return ((uint32_t)tok_tile_row<ORD>(a.tm, b, r) * kHeadDim + lcol) * 2u;
+        };
+        // wave w's query tile of CSR entry e, as whole rows, and one float per
+        // lane (lanes 0-15 the tile's lse, 16-31 its D)
+        bf16x8 xq0, xq1, xd0, xd1;
+        float xld;
+        const float *ld_src = lane < kBlock ? lse : ws.D;
+        auto load_entry = [&](int e) {
+            const int qt = __builtin_amdgcn_readfirstlane(C[e]) * kSub + w;
+            const uint32_t o0 = brow(qt, lrow), o1 = brow(qt, lrow + 8);
+            xq0 = buf_load_bf16x8(rq, o0);
+            xq1 = buf_load_bf16x8(rq, o1);
+            xd0 = buf_load_bf16x8(rdo, o0);
+            xd1 = buf_load_bf16x8(rdo, o1);
+            xld = ld_src[(int64_t)h * a.N +
+                         (lane < kBlock ? tok_tile_row<ORD>(a.tm, qt, c16) : qt * kBlock + c16)];
+        };
+        load_entry(e0);
+        for (int e = e0; e < e1; ++e) {
+            const int buf = (e - e0) & 1;
+            store_bf16x8(&qbuf[buf][w][lrow * kTS + lcol], xq0);
+            store_bf16x8(&qbuf[buf][w][(lrow + 8) * kTS + lcol], xq1);
+            store_bf16x8(&dbuf[buf][w][lrow * kTS + lcol], xd0);
+            store_bf16x8(&dbuf[buf][w][(lrow + 8) * kTS + lcol], xd1);
+            if (lane < 2 * kBlock) ldbuf[buf][w][lane] = xld;
+            // the entry's four tiles staged; every wave is done with entry e - 2
+            __syncthreads();
+            if (e + 1 < e1) load_entry(e + 1);
+#pragma unroll 1
+            for (int t = 0; t < kSub; ++t) {
+                const __bf16 *qs = qbuf[buf][t], *ds_ = dbuf[buf][t];
+                const f32x4 s = mfma_bf16_32(load_bf16x8(&qs[c16 * kTS + 32 + 8 * g]), kb1,
+                                             mfma_bf16_32(load_bf16x8(&qs[c16 * kTS + 8 * g]), kb0,
+                                                          f32x4{0.f, 0.f, 0.f, 0.f}));
+                const f32x4 dp = mfma_bf16_32(load_bf16x8(&ds_[c16 * kTS + 32 + 8 * g]), vb1,
+                                              mfma_bf16_32(load_bf16x8(&ds_[c16 * kTS + 8 * g]), vb0,
+                                                           f32x4{0.f, 0.f, 0.f, 0.f}));
+                const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&ldbuf[buf][t][4 * g]);
+                const f32x4 D4 = *reinterpret_cast<const f32x4 *>(&ldbuf[buf][t][kBlock + 4 * g]);
+                float pp[4], dsv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pp[i] = fast_exp2(s[i] * a.sl2 - l4[i] * kLog2e);
+                    dsv[i] = pp[i] * (dp[i] - D4[i]);
+                }
+                bf16x4 phi, plo, dhi, dlo;
+                split4(pp, phi, plo);
+                split4(dsv, dhi, dlo);
+                bf16x4 dT[4], qT[4];
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    dT[dt] = lds_read_tr4(&ds_[rofs + 16 * dt]);
+                    qT[dt] = lds_read_tr4(&qs[rofs + 16 * dt]);
+                    dva[dt] = mfma_bf16_16(phi, dT[dt], dva[dt]);
+                    dka[dt] = mfma_bf16_16(dhi, qT[dt], dka[dt]);
+                }
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    dva[dt] = mfma_bf16_16(plo, dT[dt], dva[dt]);
+                    dka[dt] = mfma_bf16_16(dlo, qT[dt], dka[dt]);
+                }
+            }
+        }
+        __syncthreads();   // the buffers become the output staging below
+    }
+    // pooled-level gradients, spread back with weight 1/B^l (lane: dims 4 (l % 16) ..)
+    const int oc = 4 * c16;
+    f32x4 ck = f32x4{0.f, 0.f, 0.f, 0.f}, cv = ck;
+    {
+        float inv = a.invB;
+        for (int j = 0; j < a.ncl; ++j) {
+            inv *= a.invB;
+            const int64_t off = a.cl_grad_off[j] + ((int64_t)h * a.cl_n[j] + fb / a.cl_span[j]) * kHeadDim + oc;
+            ck += *reinterpret_cast<const f32x4 *>(ws.dpk + off) * inv;
+            cv += *reinterpret_cast<const f32x4 *>(ws.dpv + off) * inv;
+        }
+    }
+    float *lds_out = reinterpret_cast<float *>(qbuf[0][0]) + w * kBlock * kOutS;   // 4 x 4352 B fit
+    auto store_tile = [&](const f32x4 *acc, float mul, f32x4 add, void *dst) {
+        wave_lds_sync();
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lds_out[(4 * g + i) * kOutS + 16 * dt + c16] = acc[dt][i];
+        wave_lds_sync();
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int r = g + 4 * it;
+            const f32x4 x = *reinterpret_cast<const f32x4 *>(&lds_out[r * kOutS + oc]) * mul + add;
+            const int64_t off = head_off + trow(f, r) + oc;
+            if (a.grad_bf16)
+                *reinterpret_cast<u32x2 *>((__bf16 *)dst + off) = __builtin_bit_cast(u32x2, to_bf16x4(x));
+            else
+                *reinterpret_cast<f32x4 *>((float *)dst + off) = x;
+        }
+    };
+    store_tile(dka, a.scale, ck, dk);
+    store_tile(dva, 1.0f, cv, dv);
+}
+
 // ================================================================ f32 path
 // Float32 inputs (the small exact-parity configurations): one wave per token,
 // lane = dimension; every dot product is a butterfly sum across the wave, and
@@ -1212,6 +1587,11 @@ hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, cons
             hipLaunchKernelGGL(table[g.order][nct][kslot], grid, dim3(256), 0, s, (const __bf16 *)q,
                                (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx, lse,
                                (const __bf16 *)dout, dq, ws, a);
+        else if (g.B == 4 * kBlock && nct <= 1 && a.n1 % 4 == 0)   // blocks of 64: shared key tiles
+            hipLaunchKernelGGL((g.order == 0 ? bwd_dq_b64_kernel<0> : bwd_dq_b64_kernel<1>),
+                               dim3((unsigned)(g.bh * (a.n1 / 4))), dim3(256), 0, s, (const __bf16 *)q,
+                               (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx, lse,
+                               (const __bf16 *)dout, dq, ws, a);
         else if (nct == 0)
             hipLaunchKernelGGL(bwd_dq_bf16_kernel<0>, grid, dim3(256), 0, s, (const __bf16 *)q,
                                (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx, lse,
@@ -1230,11 +1610,17 @@ hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, cons
                                dim3(256), 0, s, idx, csr_ptr, csr_col, ws, a, j);
         }
         const int64_t kts = (int64_t)g.bh * a.nt1;   // key tiles
-        auto dkv = g.order == 0 ? (g.sub == 1 ? bwd_dkv_bf16_kernel<0, 1> : bwd_dkv_bf16_kernel<0, 4>)
-                                : (g.sub == 1 ? bwd_dkv_bf16_kernel<1, 1> : bwd_dkv_bf16_kernel<1, 4>);
-        hipLaunchKernelGGL(dkv, dim3((unsigned)kts), dim3(kWave), 0, s, (const __bf16 *)q,
-                           (const __bf16 *)k, (const __bf16 *)v, lse, (const __bf16 *)dout,
-                           csr_ptr + g.ptr_off[1], csr_col + g.col_off[1], dk, dv, ws, a);
+        if (g.sub == 1) {
+            hipLaunchKernelGGL((g.order == 0 ? bwd_dkv_bf16_kernel<0, 1> : bwd_dkv_bf16_kernel<1, 1>),
+                               dim3((unsigned)kts), dim3(kWave), 0, s, (const __bf16 *)q,
+                               (const __bf16 *)k, (const __bf16 *)v, lse, (const __bf16 *)dout,
+                               csr_ptr + g.ptr_off[1], csr_col + g.col_off[1], dk, dv, ws, a);
+        } else {   // blocks of 64 tokens: a workgroup per key block
+            hipLaunchKernelGGL((g.order == 0 ? bwd_dkv_b64_kernel<0> : bwd_dkv_b64_kernel<1>),
+                               dim3((unsigned)((int64_t)g.bh * a.n1)), dim3(256), 0, s, (const __bf16 *)q,
+                               (const __bf16 *)k, (const __bf16 *)v, lse, (const __bf16 *)dout,
+                               csr_ptr + g.ptr_off[1], csr_col + g.col_off[1], dk, dv, ws, a);
+        }
     } else {
         const int64_t total = (int64_t)g.bh * g.N;
         hipLaunchKernelGGL(bwd_dq_f32_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s,

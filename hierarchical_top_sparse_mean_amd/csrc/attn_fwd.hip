@@ -637,6 +637,160 @@ __global__ __launch_bounds__(256, NCH == 1 ? 3 : 2) void attn_fwd_chunk_kernel(
     if (g == 0) lse[(int64_t)h * a.N + tok_tile_row<ORD>(a.tm, ib, c16)] = (m + log2f(lsum)) * kLn2;
 }
 
+// ------------------------------------------------------ blocks of 64 tokens
+// One workgroup per query block of B = 64, one wave per 16-query tile of it.
+// The 4 tiles share the block's picks, so the workgroup loads each picked key
+// block (4 key tiles, K and V) once into LDS -- each wave one tile, as whole
+// rows -- and all four waves attend to it: a quarter of the gathers of one
+// wave per tile.  Picked blocks alternate between two LDS buffers (the next
+// block's rows are in flight while one is used) under an online softmax; a
+// coarse tile of at most 16 entries, shared by the block, goes first.  K_1 <
+// B, so no coarse pick can be covered.
+template <int ORD>
+__global__ __launch_bounds__(256, 2) void attn_fwd_b64_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
+    const float *__restrict__ pk, const float *__restrict__ pv, const int32_t *__restrict__ idx,
+    __bf16 *__restrict__ o, float *__restrict__ lse, FwdArgs a) {
+    constexpr int kSub = 4;   // tiles per block
+    __shared__ __attribute__((aligned(16))) __bf16 kbuf[2][kSub][kTileElems];
+    __shared__ __attribute__((aligned(16))) __bf16 vbuf[2][kSub][kTileElems];
+    __shared__ __attribute__((aligned(16))) __bf16 qs_all[kSub][kTileElems];
+    __shared__ __attribute__((aligned(16))) __bf16 ck[kTileElems];
+    __shared__ __attribute__((aligned(16))) __bf16 cv[kTileElems];
+    __shared__ float cbias[kBlock];
+    const int w = wave_id();
+    const int lane = lane_id();
+    const int g = lane >> 4, c16 = lane & 15;
+    const int64_t blk = xcd_remap(blockIdx.x, gridDim.x);   // query block
+    const int h = (int)(blk / a.n1);
+    const int ib = (int)(blk % a.n1);
+    const int qt = ib * kSub + w;   // this wave's query tile
+    const int64_t head_off = (int64_t)h * a.N * kHeadDim;
+    const __bf16 *kh = k + head_off;
+    const __bf16 *vh = v + head_off;
+    auto trow = [&](int b, int r) { return (int64_t)tok_tile_row<ORD>(a.tm, b, r) * kHeadDim; };
+    const int lr = lane >> 3, lc = (lane & 7) * 8;
+    auto stage_rows = [&](__bf16 *dst, bf16x8 r0, bf16x8 r1) {
+        store_bf16x8(dst + lr * kVStride + lc, r0);
+        store_bf16x8(dst + (lr + 8) * kVStride + lc, r1);
+    };
+    __bf16 *qw = qs_all[w];
+    stage_rows(qw, load_bf16x8(q + head_off + trow(qt, lr) + lc),
+               load_bf16x8(q + head_off + trow(qt, lr + 8) + lc));
+    const int32_t *fine = idx + blk * a.K1;
+    // wave w's tile of picked block j, as whole rows
+    bf16x8 kr[2], vr[2];
+    auto load_tile = [&](int j) {
+        const int f = __builtin_amdgcn_readfirstlane(fine[j]) * kSub + w;
+        const int64_t o0 = trow(f, lr) + lc, o1 = trow(f, lr + 8) + lc;
+        kr[0] = load_bf16x8(kh + o0);
+        kr[1] = load_bf16x8(kh + o1);
+        vr[0] = load_bf16x8(vh + o0);
+        vr[1] = load_bf16x8(vh + o1);
+    };
+    load_tile(0);
+    if (a.ncoarse > 0) {   // coarse tile, staged by the whole workgroup: thread (entry e, quarter p)
+        const int e = threadIdx.x >> 4, part = threadIdx.x & 15;
+        int j, pick;
+        const bool ok = coarse_locate(a, e, j, pick);
+        const int js = ok ? j : 0, ps = ok ? pick : 0;
+        const int c = idx[a.cl_idx_off[js] + ((int64_t)h * a.cl_n[js] + ib / a.cl_span[js]) * a.cl_k[js] + ps];
+        const int64_t row = a.cl_pyr_off[js] + ((int64_t)h * a.cl_n[js] + c) * kHeadDim + 4 * part;
+        f32x4 kk = *reinterpret_cast<const f32x4 *>(pk + row);
+        f32x4 vv = *reinterpret_cast<const f32x4 *>(pv + row);
+        if (!ok) kk = vv = f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<u32x2 *>(&ck[e * kVStride + 4 * part]) = __builtin_bit_cast(u32x2, to_bf16x4(kk));
+        *reinterpret_cast<u32x2 *>(&cv[e * kVStride + 4 * part]) = __builtin_bit_cast(u32x2, to_bf16x4(vv));
+        if (part == 0) cbias[e] = ok ? a.lgB * (float)(js + 2) : -INFINITY;
+    }
+    wave_lds_sync();
+    const bf16x8 qa0 = load_bf16x8(qw + c16 * kVStride + 8 * g);
+    const bf16x8 qa1 = load_bf16x8(qw + c16 * kVStride + 32 + 8 * g);
+    const int rofs = (4 * g + (c16 >> 2)) * kVStride + 4 * (c16 & 3);
+    float m = -INFINITY, lsum = 0.f;
+    f32x4 oacc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (a.ncoarse > 0) {
+        __syncthreads();   // coarse tile staged
+        const __bf16 *ckr = ck + c16 * kVStride;
+        f32x4 sc = mfma_bf16_32(load_bf16x8(ckr + 32 + 8 * g), qa1,
+                                mfma_bf16_32(load_bf16x8(ckr + 8 * g), qa0, f32x4{0.f, 0.f, 0.f, 0.f})) * a.sl2;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sc[i] += cbias[4 * g + i];
+            mx = fmaxf(mx, sc[i]);
+        }
+        m = max4_groups(mx);   // entry 0 exists
+        float pc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pc[i] = fast_exp2(sc[i] - m);
+            lsum += pc[i];
+        }
+        const bf16x4 pcb = to_bf16x4(f32x4{pc[0], pc[1], pc[2], pc[3]});
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            oacc[dt] = mfma_bf16_16(lds_read_tr4(cv + rofs + 16 * dt), pcb, oacc[dt]);
+    }
+    for (int j = 0; j < a.K1; ++j) {
+        const int buf = j & 1;
+        stage_rows(kbuf[buf][w], kr[0], kr[1]);
+        stage_rows(vbuf[buf][w], vr[0], vr[1]);
+        // all four tiles of block j staged; every wave is done with block j - 2
+        __syncthreads();
+        if (j + 1 < a.K1) load_tile(j + 1);   // the next block in flight
+        f32x4 st[kSub];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < kSub; ++t) {
+            const __bf16 *kro = kbuf[buf][t] + c16 * kVStride + 8 * g;
+            st[t] = mfma_bf16_32(load_bf16x8(kro + 32), qa1,
+                                 mfma_bf16_32(load_bf16x8(kro), qa0, f32x4{0.f, 0.f, 0.f, 0.f})) * a.sl2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[t][i]);
+        }
+        const float mnew = fmaxf(m, max4_groups(mx));
+        const float alpha = fast_exp2(m - mnew);
+        m = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
+#pragma unroll
+        for (int tp = 0; tp < kSub / 2; ++tp) {
+            float p0[4], p1[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p0[i] = fast_exp2(st[2 * tp][i] - m);
+                p1[i] = fast_exp2(st[2 * tp + 1][i] - m);
+                lsum += p0[i] + p1[i];
+            }
+            const bf16x8 pb = cat8(to_bf16x4(f32x4{p0[0], p0[1], p0[2], p0[3]}),
+                                   to_bf16x4(f32x4{p1[0], p1[1], p1[2], p1[3]}));
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const bf16x4 v0 = lds_read_tr4(vbuf[buf][2 * tp] + rofs + 16 * dt);
+                const bf16x4 v1 = lds_read_tr4(vbuf[buf][2 * tp + 1] + rofs + 16 * dt);
+                oacc[dt] = mfma_bf16_32(cat8(v0, v1), pb, oacc[dt]);
+            }
+        }
+    }
+    // ---- normalise and store (whole rows through the wave's Q slot)
+    lsum = sum4_groups(lsum);
+    const float inv = 1.0f / lsum;
+    wave_lds_sync();
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        const f32x4 r = oacc[dt] * inv;
+        *reinterpret_cast<u32x2 *>(qw + c16 * kVStride + 16 * dt + 4 * g) = __builtin_bit_cast(u32x2, to_bf16x4(r));
+    }
+    wave_lds_sync();
+    store_bf16x8(o + head_off + trow(qt, lr) + lc, load_bf16x8(qw + lr * kVStride + lc));
+    store_bf16x8(o + head_off + trow(qt, lr + 8) + lc, load_bf16x8(qw + (lr + 8) * kVStride + lc));
+    if (g == 0) lse[(int64_t)h * a.N + tok_tile_row<ORD>(a.tm, qt, c16)] = (m + log2f(lsum)) * kLn2;
+}
+
 // ---------------------------------------------------------------- f32 path
 __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
@@ -707,7 +861,12 @@ hipError_t launch_attn_fwd(const Geometry &g, const void *q, const void *k, cons
         Kern kern = nullptr;
         if (fast)
             kern = g.order == 0 ? attn_fwd_fast_kernel<8, 0> : attn_fwd_fast_kernel<8, 1>;
-        else if (chunked) {
+        else if (g.B == 4 * kBlock && a.ncoarse <= kBlock) {   // one workgroup per query block
+            hipLaunchKernelGGL(g.order == 0 ? attn_fwd_b64_kernel<0> : attn_fwd_b64_kernel<1>,
+                               dim3((unsigned)blocks), dim3(256), 0, s, (const __bf16 *)q,
+                               (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx, (__bf16 *)o, lse, a);
+            return hipGetLastError();
+        } else if (chunked) {
             static const Kern table[2][2][4] = {
                 {{attn_fwd_chunk_kernel<1, false, 0>, attn_fwd_chunk_kernel<2, false, 0>,
                   attn_fwd_chunk_kernel<3, false, 0>, attn_fwd_chunk_kernel<4, false, 0>},

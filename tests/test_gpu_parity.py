@@ -146,17 +146,27 @@ def test_deterministic_bitwise():
 # ------------------------------------------------------------- transpose --
 @pytest.mark.parametrize("nb,rows,k,cols", [(3, 100, 8, 100), (2, 4096, 8, 4096), (1, 37, 5, 23),
                                             (4, 64, 1, 64), (1, 16384, 8, 32768), (2, 50, 16, 1000),
-                                            (1, 4096, 8, 70000), (3, 2000, 8, 9000), (2, 9000, 3, 4097)])
+                                            (1, 4096, 8, 70000), (3, 2000, 8, 9000), (2, 9000, 3, 4097),
+                                            (4, 65536, 8, 65536)])   # level 1 of 1M tokens: two passes
 def test_transpose_parity(nb, rows, k, cols):
     _log(f"[parity] transpose {nb} {rows} {k} {cols}")
     rng = np.random.default_rng(rows * 31 + k)
     # skewed picks: half of the rows favour a few hot keys -> long and empty segments
     idx = np.empty((nb, rows, k), dtype=np.int32)
     hot = rng.choice(cols, size=min(cols, 2 * k), replace=False)
-    for b in range(nb):
-        for r in range(rows):
-            pool = hot if (r % 2 == 0 and len(hot) >= k) else np.arange(cols)
-            idx[b, r] = np.sort(rng.choice(pool, size=k, replace=False))
+    if rows * cols > 10 ** 8:
+        # large shapes, drawn vectorised: pick j of a row lies in the j-th of k
+        # equal windows after a random start (so a row's picks are distinct)
+        step = cols // k
+        start = rng.integers(0, cols, size=(nb, rows, 1))
+        jit = rng.integers(0, step, size=(nb, rows, k))
+        idx[:] = np.sort((start + np.arange(k) * step + jit) % cols, axis=-1)
+        idx[:, ::2] = np.sort(hot[:k])
+    else:
+        for b in range(nb):
+            for r in range(rows):
+                pool = hot if (r % 2 == 0 and len(hot) >= k) else np.arange(cols)
+                idx[b, r] = np.sort(rng.choice(pool, size=k, replace=False))
     ptr_o, col_o = O.transpose(idx, cols)
     d_idx = torch.from_numpy(idx).cuda()
     ptr = torch.empty((nb, cols + 1), dtype=torch.int32, device="cuda")

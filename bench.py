@@ -124,10 +124,7 @@ def time_workload(L, w, steps, warmup, dev, grad_bf16=False, token_order=0, over
     side = torch.cuda.Stream() if overlap and w.backward else main
 
     def transposes(stream):
-        for l in range(1, s.enrich + 2):
-            ptr, col = B.csr_level(l)
-            L.llsa_index_transpose(bh, s.level_tokens[l], s.level_k[l], s.level_tokens[l],
-                                   B.index_level(l), ptr, col, B.tws, B.tws_bytes, stream)
+        L.transpose_levels(B, stream)
 
     def step(ev=None):
         # ev[c] = (start, end) events of call c, recorded on the call's stream

@@ -197,6 +197,44 @@ int llsa_select_transpose(const llsa_problem *p, const float *pyr_q, const float
     return status_of(e);
 }
 
+size_t llsa_index_transpose_levels_workspace(const llsa_problem *p) {
+    Geometry g;
+    if (make_geometry(p, &g, nullptr) != LLSA_OK) return 0;
+    size_t need = 0;
+    for (int l = 1; l <= g.Le + 1; ++l) {
+        const size_t b = llsa::transpose_workspace_bytes(g.bh, g.n[l], g.kl[l], g.n[l]);
+        need = b > need ? b : need;
+    }
+    return need;
+}
+
+int llsa_index_transpose_levels(const llsa_problem *p, const int32_t *idx, int32_t *csr_ptr,
+                                int32_t *csr_col, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+    Geometry g;
+    const int st = make_geometry(p, &g, nullptr);
+    if (st != LLSA_OK) return st;
+    if (g.bh > 65535 || g.n[1] > (1 << 24)) return LLSA_ERR_UNSUPPORTED;
+    if (!aligned16(idx) || !aligned16(csr_ptr) || !aligned16(csr_col)) return LLSA_ERR_INVALID;
+    const size_t need = llsa_index_transpose_levels_workspace(p);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+        return LLSA_ERR_WORKSPACE;
+    int rows[llsa::kMaxLevels + 1], ks[llsa::kMaxLevels + 1];
+    const int32_t *il[llsa::kMaxLevels + 1];
+    int32_t *pl[llsa::kMaxLevels + 1], *cl[llsa::kMaxLevels + 1];
+    const int n = g.Le + 1;
+    for (int i = 0; i < n; ++i) {
+        const int l = i + 1;
+        rows[i] = g.n[l];
+        ks[i] = g.kl[l];
+        il[i] = idx + g.idx_off[l];
+        pl[i] = csr_ptr + g.ptr_off[l];
+        cl[i] = csr_col + g.col_off[l];
+    }
+    return status_of(llsa::launch_transpose_many(g.bh, n, rows, ks, rows, il, pl, cl, workspace,
+                                                 (hipStream_t)stream));
+}
+
 int llsa_attn_fwd(const llsa_problem *p, const void *q, const void *k, const void *v,
                   const float *pyr_k, const float *pyr_v, const int32_t *idx, void *o, float *lse,
                   void *stream) {

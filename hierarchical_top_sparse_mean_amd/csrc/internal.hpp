@@ -45,6 +45,9 @@ hipError_t launch_attn_fwd(const Geometry &g, const void *q, const void *k, cons
 size_t transpose_workspace_bytes(int nb, int rows, int k, int cols);
 hipError_t launch_transpose(int nb, int rows, int k, int cols, const int32_t *idx,
                             int32_t *ptr, int32_t *col, void *ws, hipStream_t s);
+hipError_t launch_transpose_many(int nb, int n, const int *rows, const int *k, const int *cols,
+                                 const int32_t *const *idx, int32_t *const *ptr,
+                                 int32_t *const *col, void *ws, hipStream_t s);
 size_t transpose_counted_workspace_bytes(int nb, int rows, int k, int cols);
 int32_t *transpose_counted_hist(void *ws);
 hipError_t launch_transpose_counted(int nb, int rows, int k, int cols, const int32_t *idx,

@@ -35,6 +35,7 @@ constexpr int kTrBits = 12;
 constexpr int kTrBuckets = 1 << kTrBits;   // buckets per pass (LDS counters and masks)
 constexpr int kTrChunk = 1024;             // target picks per range (workgroup) of count and fill
 constexpr int kTrMaxRanges = 64;
+constexpr int kTrBatch = 8;                // global loads a thread issues before using them
 
 // MODE 0: one pass, bucket = key, idx -> csr_col.
 // MODE 1: first of two passes, bucket = low digit, idx -> (key, row) pairs.
@@ -90,7 +91,10 @@ static TrWs carve(void *ws, int nb, int rows, int k, const TrPlan &p, size_t *by
     return w;
 }
 
+static bool tr_one_fits(int rows, int k, int cols);   // the one-launch kernel takes it
+
 size_t transpose_workspace_bytes(int nb, int rows, int k, int cols) {
+    if (tr_one_fits(rows, k, cols)) return 0;
     size_t bytes = 0;
     carve(nullptr, nb, rows, k, plan(rows, k, cols), &bytes);
     return bytes;
@@ -142,10 +146,19 @@ __global__ __launch_bounds__(kTrThreads) void tr_count_kernel(TrSrc S, int32_t *
     __syncthreads();
     const int n = tr_count_of<MODE>(S, b);
     const int64_t e0 = (int64_t)m * per, e1 = min((int64_t)n, e0 + per);
-    for (int64_t e = e0 + tid; e < e1; e += kTrThreads) {
-        int key, row;
-        const int c = tr_bucket<MODE>(S, b, e, n, key, row);
-        if (c >= 0) atomicAdd(&h[c], 1);
+    // kTrBatch loads in flight before their atomics (an LDS atomic between two
+    // global loads would otherwise wait for the first)
+    for (int64_t eb = e0 + tid; eb < e1; eb += kTrBatch * kTrThreads) {
+        int c[kTrBatch];
+#pragma unroll
+        for (int j = 0; j < kTrBatch; ++j) {
+            const int64_t e = eb + (int64_t)j * kTrThreads;
+            int key, row;
+            c[j] = tr_bucket<MODE>(S, b, e < e1 ? e : n, n, key, row);
+        }
+#pragma unroll
+        for (int j = 0; j < kTrBatch; ++j)
+            if (c[j] >= 0) atomicAdd(&h[c[j]], 1);
     }
     __syncthreads();
     int32_t *H = hist + ((int64_t)b * ranges + m) * buckets;
@@ -233,32 +246,39 @@ __global__ __launch_bounds__(kWave) void tr_fill_kernel(TrSrc S, const int32_t *
     const int64_t e0 = (int64_t)m * per, e1 = min((int64_t)n, e0 + per);
     int32_t *OR = out_row + (int64_t)b * S.E;
     int32_t *OK = MODE == 0 ? nullptr : out_key + (int64_t)b * S.E;
-    int64_t e = e0 + lane;
-    int kn = 0, rn = 0;
-    int cn = tr_bucket<MODE>(S, b, e < e1 ? e : n, n, kn, rn);
-    int bn = cn >= 0 ? P[cn] + H[cn] : 0;
     __syncthreads();
-    for (; e - lane < e1; e += kWave) {
-        const int c = cn, base = bn, key = kn, row = rn;
-        cn = tr_bucket<MODE>(S, b, e + kWave < e1 ? e + kWave : n, n, kn, rn);
-        bn = cn >= 0 ? P[cn] + H[cn] : 0;
-        const bool ok = c >= 0;
-        const int cl = ok ? c : 0;
-        if (ok) atomicOr((unsigned long long *)&mask[cl], 1ull << lane);
-        __syncthreads();
-        const uint64_t mk = ok ? mask[cl] : 0ull;
-        const int rank = __popcll(mk & ((1ull << lane) - 1ull));
-        if (ok) {
-            const int pos = base + seen[cl] + rank;
-            OR[pos] = row;
-            if constexpr (MODE != 0) OK[pos] = key;
+    for (int64_t eb = e0; eb < e1; eb += kTrBatch * kWave) {
+        // kTrBatch chunks: their picks, then their buckets' global starts, all
+        // in flight together
+        int c[kTrBatch], key[kTrBatch], row[kTrBatch], base[kTrBatch];
+#pragma unroll
+        for (int j = 0; j < kTrBatch; ++j) {
+            const int64_t e = eb + (int64_t)j * kWave + lane;
+            c[j] = tr_bucket<MODE>(S, b, e < e1 ? e : n, n, key[j], row[j]);
         }
-        __syncthreads();
-        if (ok && (mk >> lane) == 1ull) {   // highest lane of its bucket in the chunk
-            seen[cl] += __popcll(mk);
-            mask[cl] = 0ull;
+#pragma unroll
+        for (int j = 0; j < kTrBatch; ++j) base[j] = c[j] >= 0 ? P[c[j]] + H[c[j]] : 0;
+#pragma unroll
+        for (int j = 0; j < kTrBatch; ++j) {
+            if (eb + (int64_t)j * kWave >= e1) break;
+            const bool ok = c[j] >= 0;
+            const int cl = ok ? c[j] : 0;
+            if (ok) atomicOr((unsigned long long *)&mask[cl], 1ull << lane);
+            __syncthreads();
+            const uint64_t mk = ok ? mask[cl] : 0ull;
+            const int rank = __popcll(mk & ((1ull << lane) - 1ull));
+            if (ok) {
+                const int pos = base[j] + seen[cl] + rank;
+                OR[pos] = row[j];
+                if constexpr (MODE != 0) OK[pos] = key[j];
+            }
+            __syncthreads();
+            if (ok && (mk >> lane) == 1ull) {   // highest lane of its bucket in the chunk
+                seen[cl] += __popcll(mk);
+                mask[cl] = 0ull;
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
 }
 
@@ -283,71 +303,173 @@ __global__ __launch_bounds__(kTrThreads) void tr_bounds_kernel(const int32_t *__
     ptr[(int64_t)b * (cols + 1) + c] = lo;
 }
 
-// Small matrices (at most kTrSmallPicks picks, at most 4096 keys): the whole
-// transpose of one matrix in one workgroup -- count in LDS (keeping the picks
-// in LDS too), scan in LDS, then wave 0 places the picks in order as the fill
-// kernel does, with the bucket starts themselves as running cursors.  One
-// launch instead of four.
-constexpr int kTrSmallPicks = 4096;
-__global__ __launch_bounds__(kTrThreads) void tr_small_kernel(const int32_t *__restrict__ idx,
-                                                             int32_t *__restrict__ ptr,
-                                                             int32_t *__restrict__ col, int rows,
-                                                             int k, int cols) {
-    __shared__ int32_t base[kTrBuckets];
-    __shared__ uint64_t mask[kTrBuckets];
-    __shared__ int32_t wsum[kTrThreads / kWave];
-    __shared__ int32_t picks[kTrSmallPicks];
-    const int b = blockIdx.x, tid = threadIdx.x, lane = lane_id();
-    const int64_t E = (int64_t)rows * k;
+// Matrices of at most kTrOneMaxPicks picks and kTrOneMaxCols keys: the whole
+// transpose in one launch.  Workgroup (part, b) owns keys [256 part, 256 part
+// + 256) of matrix b and reads every pick of the matrix (from L2: each pick
+// is read by cols / 256 workgroups):
+//  - the number of picks with a smaller key gives where its keys' lists start;
+//  - wave w owns elements [w per, (w + 1) per) and counts their picks of its
+//    keys per key, so an exclusive prefix over the waves, plus the scan over
+//    the keys, is the first slot of each (wave, key);
+//  - each wave then reads its elements again in order, keeps the picks of its
+//    keys in an LDS queue (ballot and popcount keep their order), and places
+//    them 64 at a time, ranking the picks of one key inside a chunk by a
+//    popcount of an LDS lane mask as the fill kernel does, with its own masks
+//    and cursors: the 16 waves place their picks independently and every list
+//    keeps its row order.
+// No workspace, no global atomic, nothing to clear beforehand.
+constexpr int kTrOneThreads = 1024;
+constexpr int kTrOneWaves = kTrOneThreads / kWave;
+constexpr int kTrOneKeys = 256;                                    // keys per workgroup
+constexpr int kTrOneChunks = 32;                                   // 64-pick chunks per round
+constexpr int kTrOneRound = kTrOneChunks * kWave;                  // picks a wave holds at once
+constexpr int kTrOneMaxPicks = 4 * kTrOneWaves * kTrOneRound;      // 131072 per matrix
+constexpr int kTrOneMaxCols = 4096;
+constexpr int kTrOneEBits = 17;                                    // a queued pick: key << 17 | element
+static_assert(kTrOneMaxPicks <= (1 << kTrOneEBits), "element index must fit its field");
+
+static bool tr_one_fits(int rows, int k, int cols) {
+    return (int64_t)rows * k <= kTrOneMaxPicks && cols <= kTrOneMaxCols;
+}
+
+// Several matrices (the levels of one problem, all with nb batches) in one
+// launch: x-blocks [first_i, first_i + parts_i) belong to matrix i.
+constexpr int kTrOneMaxMats = 8;
+struct TrOneMat {
+    const int32_t *idx;
+    int32_t *ptr, *col;
+    int rows, k, cols, parts;
+};
+struct TrOneArgs {
+    TrOneMat m[kTrOneMaxMats];
+    int nmat;
+};
+
+__global__ __launch_bounds__(kTrOneThreads) void tr_one_kernel(TrOneArgs A) {
+    int mi = 0, part = blockIdx.x;
+    while (mi + 1 < A.nmat && part >= A.m[mi].parts) part -= A.m[mi++].parts;
+    const int32_t *__restrict__ idx = A.m[mi].idx;
+    int32_t *__restrict__ ptr = A.m[mi].ptr;
+    int32_t *__restrict__ col = A.m[mi].col;
+    const int rows = A.m[mi].rows, k = A.m[mi].k, cols = A.m[mi].cols;
+    __shared__ int32_t cur[kTrOneWaves][kTrOneKeys];    // per-wave counts, then cursors
+    __shared__ uint64_t mask[kTrOneWaves][kTrOneKeys];
+    __shared__ uint32_t queue[kTrOneWaves][2 * kWave];
+    __shared__ int32_t below_w[kTrOneWaves];
+    __shared__ int32_t scan_w[kTrOneKeys / kWave];
+    const int b = blockIdx.y;
+    const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
+    const uint64_t lower = (1ull << lane) - 1ull;
+    const int c0 = part * kTrOneKeys, nk = min(kTrOneKeys, cols - c0);
+    const int E = rows * k;
+    const int per = (E + kTrOneWaves - 1) / kTrOneWaves;
+    const int ew0 = min(E, w * per), ew1 = min(E, ew0 + per);
     const int32_t *I = idx + (int64_t)b * E;
-    for (int c = tid; c < cols; c += kTrThreads) {
-        base[c] = 0;
-        mask[c] = 0;
+    for (int i = tid; i < kTrOneWaves * kTrOneKeys; i += kTrOneThreads) {
+        (&cur[0][0])[i] = 0;
+        (&mask[0][0])[i] = 0ull;
+    }
+    // the wave's picks, a round (32 chunks) at a time, all loads of a round in
+    // flight together; one round holds every pick of a matrix of 32768 picks
+    const int rounds = (ew1 - ew0 + kTrOneRound - 1) / kTrOneRound;
+    int kv[kTrOneChunks];
+    auto load = [&](int r) {
+#pragma unroll
+        for (int j = 0; j < kTrOneChunks; ++j) {
+            const int e = ew0 + r * kTrOneRound + j * kWave + lane;
+            kv[j] = e < ew1 ? I[e] : -1;
+        }
+    };
+    load(0);
+    __syncthreads();
+    int below = 0;
+    for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+        for (int j = 0; j < kTrOneChunks; ++j) {
+            const int c = kv[j];
+            below += (c >= 0 && c < c0) ? 1 : 0;
+            if (c >= c0 && c < c0 + nk) atomicAdd(&cur[w][c - c0], 1);
+        }
+        if (r + 1 < rounds) load(r + 1);
+    }
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) below += __shfl_xor(below, d, kWave);
+    if (lane == 0) below_w[w] = below;
+    __syncthreads();
+    // thread t < 256: key c0 + t -- prefix over the waves, then the scan over keys
+    int tot = 0;
+    if (tid < kTrOneKeys) {
+#pragma unroll
+        for (int x = 0; x < kTrOneWaves; ++x) {
+            const int v = cur[x][tid];
+            cur[x][tid] = tot;
+            tot += v;
+        }
+    }
+    const int incl = wave_inclusive_scan(tot);
+    if (tid < kTrOneKeys && lane == kWave - 1) scan_w[w] = incl;
+    __syncthreads();
+    if (tid < kTrOneKeys) {
+        int start = incl - tot;
+#pragma unroll
+        for (int x = 0; x < kTrOneWaves; ++x) start += below_w[x];
+        for (int x = 0; x < w; ++x) start += scan_w[x];
+        int32_t *P = ptr + (int64_t)b * (cols + 1);
+        if (tid < nk) P[c0 + tid] = start;
+        if (c0 + nk == cols && tid == kTrOneKeys - 1) P[cols] = start + tot;   // all valid picks
+#pragma unroll
+        for (int x = 0; x < kTrOneWaves; ++x) cur[x][tid] += start;
     }
     __syncthreads();
-    for (int64_t e = tid; e < E; e += kTrThreads) {
-        const int c = I[e];
-        picks[e] = c;
-        if (c >= 0 && c < cols) atomicAdd(&base[c], 1);
-    }
-    __syncthreads();
-    // exclusive scan of the counts: each thread owns a contiguous run of keys
-    const int per = (cols + kTrThreads - 1) / kTrThreads;
-    const int c0 = min(cols, tid * per), c1 = min(cols, c0 + per);
-    int local = 0;
-    for (int c = c0; c < c1; ++c) local += base[c];
-    const int incl = wave_inclusive_scan(local);
-    if (lane == kWave - 1) wsum[wave_id()] = incl;
-    __syncthreads();
-    int run = incl - local;
-    for (int w = 0; w < wave_id(); ++w) run += wsum[w];
-    int32_t *P = ptr + (int64_t)b * (cols + 1);
-    for (int c = c0; c < c1; ++c) {
-        const int x = base[c];
-        P[c] = run;
-        base[c] = run;
-        run += x;
-    }
-    if (tid == kTrThreads - 1) P[cols] = run;
-    __syncthreads();
-    if (wave_id() != 0) return;
     int32_t *C = col + (int64_t)b * E;
-    for (int64_t e0 = 0; e0 < E; e0 += kWave) {
-        const int64_t e = e0 + lane;
-        const int c = e < E ? picks[e] : -1;
-        const bool ok = c >= 0 && c < cols;
-        const int cl = ok ? c : 0;
-        if (ok) atomicOr((unsigned long long *)&mask[cl], 1ull << lane);
+    uint32_t *Q = queue[w];
+    int fill = 0;   // queued picks (uniform across the wave, below 64 between chunks)
+    // places the first n (<= 64) queued picks and moves the rest to the front
+    auto place = [&](int n) {
         wave_lds_sync();
-        const uint64_t mk = ok ? mask[cl] : 0ull;
-        const int rank = __popcll(mk & ((1ull << lane) - 1ull));
-        if (ok) C[base[cl] + rank] = (int32_t)(e / k);
+        const bool ok = lane < n;
+        const uint32_t v = ok ? Q[lane] : 0u;
+        const int cl = (int)(v >> kTrOneEBits);
+        if (ok) atomicOr((unsigned long long *)&mask[w][cl], 1ull << lane);
+        wave_lds_sync();
+        const uint64_t mk = ok ? mask[w][cl] : 0ull;
+        if (ok) C[cur[w][cl] + __popcll(mk & lower)] = (int)(v & ((1u << kTrOneEBits) - 1u)) / k;
         wave_lds_sync();
         if (ok && (mk >> lane) == 1ull) {   // highest lane of its key in the chunk
-            base[cl] += __popcll(mk);
-            mask[cl] = 0ull;
+            cur[w][cl] += __popcll(mk);
+            mask[w][cl] = 0ull;
         }
+        if (lane < fill - n) Q[lane] = Q[n + lane];   // reads [64, 128), writes [0, 64)
+        fill -= n;
         wave_lds_sync();
+    };
+    for (int r = 0; r < rounds; ++r) {
+        if (rounds > 1) load(r);
+        const int er = ew0 + r * kTrOneRound;
+#pragma unroll
+        for (int j = 0; j < kTrOneChunks; ++j) {
+            const int c = kv[j];
+            const bool in = c >= c0 && c < c0 + nk;
+            const uint64_t bal = __ballot(in);
+            if (in) Q[fill + __popcll(bal & lower)] = ((uint32_t)(c - c0) << kTrOneEBits) | (uint32_t)(er + j * kWave + lane);
+            fill += __popcll(bal);
+            if (fill >= kWave) place(kWave);
+        }
+    }
+    if (fill > 0) place(fill);
+}
+
+static void launch_tr_one(const TrOneMat *mats, int n, int nb, hipStream_t s) {
+    for (int i0 = 0; i0 < n; i0 += kTrOneMaxMats) {
+        TrOneArgs A{};
+        A.nmat = std::min(n - i0, kTrOneMaxMats);
+        int parts = 0;
+        for (int i = 0; i < A.nmat; ++i) {
+            A.m[i] = mats[i0 + i];
+            A.m[i].parts = (A.m[i].cols + kTrOneKeys - 1) / kTrOneKeys;
+            parts += A.m[i].parts;
+        }
+        hipLaunchKernelGGL(tr_one_kernel, dim3((unsigned)parts, (unsigned)nb), dim3(kTrOneThreads), 0, s, A);
     }
 }
 
@@ -374,9 +496,9 @@ hipError_t launch_transpose(int nb, int rows, int k, int cols, const int32_t *id
     S.E = (int64_t)rows * k;
     S.k = k;
     S.cols = cols;
-    if (!p.two_pass && S.E <= kTrSmallPicks) {
-        hipLaunchKernelGGL(tr_small_kernel, dim3((unsigned)nb), dim3(kTrThreads), 0, s, idx, ptr, col,
-                           rows, k, cols);
+    if (tr_one_fits(rows, k, cols)) {
+        const TrOneMat m{idx, ptr, col, rows, k, cols, 0};
+        launch_tr_one(&m, 1, nb, s);
         return hipGetLastError();
     }
     if (!p.two_pass) {
@@ -394,6 +516,25 @@ hipError_t launch_transpose(int nb, int rows, int k, int cols, const int32_t *id
     tr_pass<2>(S2, p, nb, hi_buckets, w, w.ptrB, col, w.skey, s);
     const dim3 bgrid((unsigned)((cols + 1 + kTrThreads - 1) / kTrThreads), (unsigned)nb);
     hipLaunchKernelGGL(tr_bounds_kernel, bgrid, dim3(kTrThreads), 0, s, w.skey, w.ptrA, ptr, S.E, cols);
+    return hipGetLastError();
+}
+
+// Several matrices with nb batches each: those the one-launch kernel takes
+// share one launch, the others run one after another (sharing the workspace).
+hipError_t launch_transpose_many(int nb, int n, const int *rows, const int *k, const int *cols,
+                                 const int32_t *const *idx, int32_t *const *ptr,
+                                 int32_t *const *col, void *ws, hipStream_t s) {
+    TrOneMat one[64];
+    int n_one = 0;
+    for (int i = 0; i < n; ++i) {
+        if (n_one < 64 && tr_one_fits(rows[i], k[i], cols[i]))
+            one[n_one++] = TrOneMat{idx[i], ptr[i], col[i], rows[i], k[i], cols[i], 0};
+        else {
+            const hipError_t e = launch_transpose(nb, rows[i], k[i], cols[i], idx[i], ptr[i], col[i], ws, s);
+            if (e != hipSuccess) return e;
+        }
+    }
+    if (n_one > 0) launch_tr_one(one, n_one, nb, s);
     return hipGetLastError();
 }
 

@@ -60,6 +60,9 @@ def _load():
     L.llsa_index_transpose_workspace.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32]
     L.llsa_index_transpose_workspace.restype = _c_sz
     L.llsa_index_transpose.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _c_sz, _vp]
+    L.llsa_index_transpose_levels_workspace.argtypes = [P]
+    L.llsa_index_transpose_levels_workspace.restype = _c_sz
+    L.llsa_index_transpose_levels.argtypes = [P, _vp, _vp, _vp, _vp, _c_sz, _vp]
     L.llsa_index_transpose_mask_workspace.argtypes = [_c_i32, _c_i32, _c_i32]
     L.llsa_index_transpose_mask_workspace.restype = _c_sz
     L.llsa_index_transpose_mask.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _c_sz,
@@ -75,7 +78,8 @@ def _load():
     L.llsa_strerror.restype = ctypes.c_char_p
     for name in ("llsa_sizes_query", "llsa_pool", "llsa_select", "llsa_attn_fwd",
                  "llsa_index_transpose", "llsa_attn_bwd", "llsa_dense_attn_fwd",
-                 "llsa_dense_attn_bwd", "llsa_index_transpose_mask", "llsa_select_transpose"):
+                 "llsa_dense_attn_bwd", "llsa_index_transpose_mask", "llsa_select_transpose",
+                 "llsa_index_transpose_levels"):
         getattr(L, name).restype = ctypes.c_int
     return L
 
@@ -157,6 +161,17 @@ def llsa_index_transpose(n_batch, n_rows, k, n_cols, idx, csr_ptr, csr_col, work
                                     _stream(stream)))
 
 
+def llsa_index_transpose_levels_workspace(p) -> int:
+    return int(lib.llsa_index_transpose_levels_workspace(ctypes.byref(p)))
+
+
+def llsa_index_transpose_levels(p, idx, csr_ptr, csr_col, workspace=None, workspace_bytes=0,
+                                stream=None):
+    _check("llsa_index_transpose_levels",
+           lib.llsa_index_transpose_levels(ctypes.byref(p), _ptr(idx), _ptr(csr_ptr), _ptr(csr_col),
+                                           _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
 def llsa_index_transpose_mask_workspace(n_batch, n_rows, n_cols) -> int:
     return int(lib.llsa_index_transpose_mask_workspace(n_batch, n_rows, n_cols))
 
@@ -220,8 +235,10 @@ class Buffers:
             self.dk = torch.empty(shape, dtype=gdt, device=device)
             self.dv = torch.empty(shape, dtype=gdt, device=device)
             self.ws = torch.empty(max(int(s.bwd_workspace_bytes), 256), dtype=torch.uint8, device=device)
-            # one workspace serves the per-level transposes and the fused selection + transposes
-            self.tws_bytes = max(int(s.transpose_workspace_bytes), llsa_select_transpose_workspace(p))
+            # one workspace serves the per-level transposes, the transposes of all levels
+            # and the fused selection + transposes
+            self.tws_bytes = max(int(s.transpose_workspace_bytes), llsa_select_transpose_workspace(p),
+                                 llsa_index_transpose_levels_workspace(p))
             self.tws = torch.empty(max(self.tws_bytes, 256), dtype=torch.uint8, device=device)
 
     def pyramid_level(self, buf, l):
@@ -253,13 +270,8 @@ def forward(B: Buffers, q, k, v, stream=None):
 
 
 def transpose_levels(B: Buffers, stream=None):
-    """CSR of I^(l) for every level the backward pass reads (levels 1..Le+1)."""
-    s, p = B.s, B.p
-    bh = p.batch * p.heads
-    for l in range(1, s.enrich + 2):
-        ptr, col = B.csr_level(l)
-        llsa_index_transpose(bh, s.level_tokens[l], s.level_k[l], s.level_tokens[l],
-                             B.index_level(l), ptr, col, B.tws, B.tws_bytes, stream)
+    """CSR of I^(l) for every level the backward pass reads (levels 1..Le+1), one call."""
+    llsa_index_transpose_levels(B.p, B.idx, B.csr_ptr, B.csr_col, B.tws, B.tws_bytes, stream)
 
 
 def backward(B: Buffers, q, k, v, dout, stream=None):

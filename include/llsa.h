@@ -147,9 +147,10 @@ int llsa_attn_fwd(const llsa_problem *p, const void *q, const void *k, const voi
  *      so ptr[n_cols] = n_rows * k; csr_col [n_batch, n_rows * k]: the rows
  *      that picked key c, ascending, at csr_col[ptr[c] .. ptr[c+1]).
  * workspace: at least llsa_index_transpose_workspace(...) bytes of device
- *      memory (per-range histograms and totals of up to 4096 buckets; above
- *      4096 keys also a staging list of (key, row) pairs and sorted keys,
- *      12 bytes per pick).
+ *      memory.  Zero (workspace may be NULL) for matrices of at most 131072
+ *      picks and 4096 keys, which one launch transposes; otherwise per-range
+ *      histograms and totals of up to 4096 buckets, and above 4096 keys also
+ *      a staging list of (key, row) pairs and sorted keys, 12 bytes per pick.
  * Limits: n_cols <= 2^24 and n_batch <= 65535 (LLSA_ERR_UNSUPPORTED).
  * An index outside [0, n_cols) is skipped: it is not listed, and ptr[n_cols]
  * then counts only the listed picks.  The output is deterministic.
@@ -159,6 +160,25 @@ size_t llsa_index_transpose_workspace(int32_t n_batch, int32_t n_rows, int32_t k
 int llsa_index_transpose(int32_t n_batch, int32_t n_rows, int32_t k, int32_t n_cols,
                          const int32_t *idx, int32_t *csr_ptr, int32_t *csr_col,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The index transposes the backward pass reads, for one problem: the CSR of
+ * I^(l) for l = 1..Le+1, exactly as llsa_index_transpose(batch * heads, n_l,
+ * K_l, n_l, idx + sizes.index_offset[l], ...) would write them at
+ * sizes.csr_ptr_offset[l] / sizes.csr_col_offset[l].  The levels that fit the
+ * one-launch transpose (at most 131072 picks and 4096 keys) share a single
+ * launch; larger ones run in turn.
+ * In : idx, every level as llsa_select writes it.
+ * workspace: at least llsa_index_transpose_levels_workspace(p) bytes of
+ *      device memory (16-byte aligned; zero bytes, NULL allowed, when every
+ *      level fits the one-launch transpose).
+ * Errors as llsa_select; LLSA_ERR_UNSUPPORTED also when batch * heads >
+ * 65535.
+ */
+size_t llsa_index_transpose_levels_workspace(const llsa_problem *p);
+int llsa_index_transpose_levels(const llsa_problem *p, const int32_t *idx, int32_t *csr_ptr,
+                                int32_t *csr_col, void *workspace, size_t workspace_bytes,
+                                void *stream);
 
 /*
  * Selection and the index transposes the backward pass reads, fused

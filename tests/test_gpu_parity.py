@@ -191,7 +191,7 @@ def test_transpose_parity(nb, rows, k, cols):
 ])
 def test_select_transpose_fused_matches_separate(b, h, N, L_, K, Le, block):
     # one fused call gives bit for bit the picks and key-major lists of
-    # llsa_select followed by one llsa_index_transpose per level
+    # llsa_select followed by the transposes of every level
     _log(f"[parity] fused select+transpose {b} {h} {N} L{L_} K{K} Le{Le} B{block}")
     c = Case(b, h, N, torch.bfloat16, L_, K, Le, backward=True, sinus=round(N ** 0.5) ** 2 == N,
              block=block)
@@ -212,6 +212,42 @@ def test_select_transpose_fused_matches_separate(b, h, N, L_, K, Le, block):
     for l in range(1, Le + 2):
         ptr, col = B.csr_level(l)
         assert torch.equal(ptr, csr0[l - 1][0]) and torch.equal(col, csr0[l - 1][1]), l
+
+
+@pytest.mark.parametrize("b,h,N,L_,K,Le,block", [
+    (1, 16, 65536, 2, 8, 1, 16),    # both levels in one launch
+    (1, 4, 8192, 3, 4, 2, 16),      # three levels in one launch
+    (1, 2, 65536, 1, 32, 0, 16),    # 131072 picks: the largest one-launch matrix
+    (1, 2, 262144, 3, 8, 2, 16),    # level 1 has 16384 keys: two passes, levels 2-3 one launch
+    (2, 2, 16384, 2, 8, 1, 64),
+])
+def test_transpose_levels_matches_per_level(b, h, N, L_, K, Le, block):
+    # llsa_index_transpose_levels writes, bit for bit, what one
+    # llsa_index_transpose per level writes, and both equal the oracle's lists
+    _log(f"[parity] transpose levels {b} {h} {N} L{L_} K{K} Le{Le} B{block}")
+    c = Case(b, h, N, torch.bfloat16, L_, K, Le, backward=True, sinus=round(N ** 0.5) ** 2 == N,
+             block=block)
+    B = L.Buffers(c.p, backward=True)
+    L.llsa_pool(c.p, c.q.cuda(), c.k.cuda(), c.v.cuda(), B.pyr_q, B.pyr_k, B.pyr_v)
+    L.llsa_select(c.p, B.pyr_q, B.pyr_k, B.idx)
+    B.csr_ptr.fill_(-7)
+    B.csr_col.fill_(-7)
+    L.llsa_index_transpose_levels(c.p, B.idx, B.csr_ptr, B.csr_col, B.tws, B.tws_bytes)
+    torch.cuda.synchronize()
+    got = [tuple(t.cpu().numpy() for t in B.csr_level(l)) for l in range(1, Le + 2)]
+    s, bh = B.s, b * h
+    for l in range(1, Le + 2):
+        ptr, col = B.csr_level(l)
+        ptr.fill_(-5)
+        col.fill_(-5)
+        L.llsa_index_transpose(bh, s.level_tokens[l], s.level_k[l], s.level_tokens[l],
+                               B.index_level(l), ptr, col, B.tws, B.tws_bytes)
+    torch.cuda.synchronize()
+    for l in range(1, Le + 2):
+        ptr, col = (t.cpu().numpy() for t in B.csr_level(l))
+        assert np.array_equal(got[l - 1][0], ptr) and np.array_equal(got[l - 1][1], col), l
+        ptr_o, col_o = O.transpose(B.index_level(l).cpu().numpy(), s.level_tokens[l])
+        assert np.array_equal(ptr, ptr_o) and np.array_equal(col, col_o), l
 
 
 @pytest.mark.parametrize("cols", [100, 9000])

@@ -462,19 +462,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
     const float *__restrict__ pk, const float *__restrict__ pv, const int32_t *__restrict__ idx,
     const float *__restrict__ lse, const __bf16 *__restrict__ dout, void *__restrict__ dq, BwdWs ws,
     BwdArgs a) {
-    constexpr int kTileBytes = (4 * 4 + 2) * kTE * 2;          // K, V, Q, dO per wave + coarse K, V
+    // per wave two K / V slot pairs (K0, V0, K1, V1: the two tiles of a pair),
+    // Q and dO; then the coarse K, V tiles
+    constexpr int kTileBytes = (4 * 6 + 2) * kTE * 2;
     constexpr int kRedBytes = 4 * 2 * kBlock * kHeadDim * 4;   // coarse partials of 4 waves
     __shared__ __attribute__((aligned(16))) char smem[kTileBytes > kRedBytes ? kTileBytes : kRedBytes];
     static_assert(K1T % 2 == 0 && K1T <= 32, "fine tiles stream in pairs, two pick registers");
+    static_assert(kBlock * kOutS * 4 <= 2 * kTE * 2, "dQ rows fit the second slot pair");
     constexpr int NT = 4 * K1T;   // fine tiles per wave
     __shared__ float cbias[kBlock];
     __shared__ int ccol[kBlock];   // level-2 pooled token of each coarse entry (-1: other level)
     __shared__ __attribute__((aligned(16))) float lds_pt[4][2][kBlock * kPtS];  // coarse P, dS entry-major
-    __shared__ __attribute__((aligned(16))) float lds_out[4][kBlock * kOutS];   // dQ rows
     typedef __bf16 Tile[kTE];
-    Tile *lds_k = reinterpret_cast<Tile *>(smem);
-    Tile *lds_v = lds_k + 4;
-    Tile *lds_q = lds_v + 4;
+    Tile *lds_kv = reinterpret_cast<Tile *>(smem);
+    Tile *lds_q = lds_kv + 16;
     Tile *lds_do = lds_q + 4;
     __bf16 *ck = reinterpret_cast<__bf16 *>(lds_do + 4);
     __bf16 *cv = ck + kTE;
@@ -491,6 +492,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
     const int ib0 = G * kBlock;
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    __bf16 *const k0s = lds_kv[4 * w], *const v0s = lds_kv[4 * w + 1];
+    __bf16 *const k1s = lds_kv[4 * w + 2], *const v1s = lds_kv[4 * w + 3];
+    float *const out_w = reinterpret_cast<float *>(k1s);   // dQ rows, over the second slot pair
 
     // ---- coarse tile, staged by the whole workgroup: thread (entry e, quarter p)
     if constexpr (CO) {
@@ -600,40 +604,50 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
             accB[dt] = zero4;
         }
         float dsum = 0.f;
-        auto fine_tile = [&](const TileRegs &R) {
-            wave_lds_sync();
-            stage_rows(lds_k[w], R.ka0, R.ka1);
-            stage_rows(lds_v[w], R.va0, R.va1);
-            wave_lds_sync();
-            const __bf16 *kr = &lds_k[w][c16 * kTS + 8 * g];
-            const __bf16 *vr = &lds_v[w][c16 * kTS + 8 * g];
+        // Two fine tiles at a time, each in a slot pair of its own: their
+        // score chains are independent, and the key-side contractions take
+        // the 16 keys of both tiles as the 32 k-slots of one MFMA (the hi and
+        // lo parts of P and P dP in two MFMAs).  The next pair's loads go out
+        // as soon as this pair's rows are staged.
+        auto score = [&](const __bf16 *ks, const __bf16 *vs, float (&p)[4], float (&x)[4]) {
+            const __bf16 *kr = ks + c16 * kTS + 8 * g;
+            const __bf16 *vr = vs + c16 * kTS + 8 * g;
             const f32x4 s = mfma_bf16_32(load_bf16x8(kr + 32), qa1, mfma_bf16_32(load_bf16x8(kr), qa0, zero4));
             const f32x4 dp = mfma_bf16_32(load_bf16x8(vr + 32), da1, mfma_bf16_32(load_bf16x8(vr), da0, zero4));
-            float p[4], x[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 p[i] = fast_exp2(s[i] * a.sl2 - lse2);
                 x[i] = p[i] * dp[i];
-                dsum += x[i];
-            }
-            bf16x4 phi, plo, xhi, xlo;
-            split4(p, phi, plo);
-            split4(x, xhi, xlo);
-            const bf16x8 pcat = cat8(phi, plo), xcat = cat8(xhi, xlo);
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                const bf16x4 kT = lds_read_tr4(&lds_k[w][rofs + 16 * dt]);
-                const bf16x8 kk = cat8(kT, kT);
-                accA[dt] = mfma_bf16_32(kk, xcat, accA[dt]);
-                accB[dt] = mfma_bf16_32(kk, pcat, accB[dt]);
             }
         };
         auto tile_pair = [&](int t) {
+            const int u = jb * K1T + t;   // first tile of the pair
+            wave_lds_sync();
+            stage_rows(k0s, R[0].ka0, R[0].ka1);
+            stage_rows(v0s, R[0].va0, R[0].va1);
+            stage_rows(k1s, R[1].ka0, R[1].ka1);
+            stage_rows(v1s, R[1].va0, R[1].va1);
 #pragma unroll
-            for (int r = 0; r < PD; ++r) {
-                const int u = jb * K1T + t + r;
-                fine_tile(R[r]);
-                if (u + PD < NT) load_tile(u + PD, R[r]);
+            for (int r = 0; r < PD; ++r)
+                if (u + PD + r < NT) load_tile(u + PD + r, R[r]);
+            wave_lds_sync();
+            float p0[4], x0[4], p1[4], x1[4];
+            score(k0s, v0s, p0, x0);
+            score(k1s, v1s, p1, x1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dsum += x0[i] + x1[i];
+            bf16x4 phi0, plo0, xhi0, xlo0, phi1, plo1, xhi1, xlo1;
+            split4(p0, phi0, plo0);
+            split4(x0, xhi0, xlo0);
+            split4(p1, phi1, plo1);
+            split4(x1, xhi1, xlo1);
+            const bf16x8 ph = cat8(phi0, phi1), pl = cat8(plo0, plo1);
+            const bf16x8 xh = cat8(xhi0, xhi1), xl = cat8(xlo0, xlo1);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const bf16x8 kk = cat8(lds_read_tr4(k0s + rofs + 16 * dt), lds_read_tr4(k1s + rofs + 16 * dt));
+                accA[dt] = mfma_bf16_32(kk, xl, mfma_bf16_32(kk, xh, accA[dt]));
+                accB[dt] = mfma_bf16_32(kk, pl, mfma_bf16_32(kk, ph, accB[dt]));
             }
         };
         if constexpr (K1T <= 8) {
@@ -647,16 +661,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
             if (jb + 1 < 4) load_q(jb + 1, X);
             const float Dq = sum4_groups(dsum);
             if (g == 0) ws.D[(int64_t)h * a.N + row] = Dq;
+            wave_lds_sync();
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
-                *reinterpret_cast<f32x4 *>(&lds_out[w][c16 * kOutS + 16 * dt + 4 * g]) =
+                *reinterpret_cast<f32x4 *>(&out_w[c16 * kOutS + 16 * dt + 4 * g]) =
                     (accA[dt] - Dq * accB[dt]) * a.scale;
             wave_lds_sync();
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
                 const int r = g + 4 * it;
                 store_grad4(dq, head_off + trow(ib0 + w * 4 + jb, r) + 4 * c16,
-                            *reinterpret_cast<const f32x4 *>(&lds_out[w][r * kOutS + 4 * c16]), a.grad_bf16);
+                            *reinterpret_cast<const f32x4 *>(&out_w[r * kOutS + 4 * c16]), a.grad_bf16);
             }
             continue;
         } else {
@@ -725,16 +740,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
         }
         // dQ (lane: query c16, dims 16 dt + 4 g ..) passes through LDS so
         // that every store writes whole rows (lane l: row l / 16 + 4 it)
+        wave_lds_sync();
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
-            *reinterpret_cast<f32x4 *>(&lds_out[w][c16 * kOutS + 16 * dt + 4 * g]) =
+            *reinterpret_cast<f32x4 *>(&out_w[c16 * kOutS + 16 * dt + 4 * g]) =
                 (accA[dt] - Dq * accB[dt]) * a.scale;
         wave_lds_sync();
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int r = g + 4 * it;
             store_grad4(dq, head_off + trow(ib0 + w * 4 + jb, r) + 4 * c16,
-                        *reinterpret_cast<const f32x4 *>(&lds_out[w][r * kOutS + 4 * c16]), a.grad_bf16);
+                        *reinterpret_cast<const f32x4 *>(&out_w[r * kOutS + 4 * c16]), a.grad_bf16);
         }
         }
     }
@@ -1067,20 +1083,22 @@ __global__ __launch_bounds__(256) void bwd_coarse_reduce_kernel(const int32_t *_
 // One wave per key tile, in a workgroup of its own: key blocks differ widely
 // in how many query blocks picked them, and no wave waits for a slower
 // sibling before its slot is reused.  The query tiles of the blocks in the
-// key block's CSR segment (SUB = B / 16 per block) stream through a ring of
-// kDkvDepth register sets, so that several tiles' Q / dO are in flight while
-// one is computed.
-constexpr int kDkvDepth = 4;
+// key block's CSR segment (SUB = B / 16 per block) go two at a time: a pair
+// is staged in LDS, the next pair's Q / dO loads go out into the freed
+// registers, and the pair is computed while they are in flight.
+constexpr int kDkvDepth = 2;
 template <int ORD, int SUB>
 __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ lse, const __bf16 *__restrict__ dout, const int32_t *__restrict__ csr_ptr,
     const int32_t *__restrict__ csr_col, void *__restrict__ dk, void *__restrict__ dv, BwdWs ws,
     BwdArgs a) {
-    __shared__ __attribute__((aligned(16))) __bf16 lds_q[kTE];
-    __shared__ __attribute__((aligned(16))) __bf16 lds_do[kTE];
-    __shared__ __attribute__((aligned(16))) float lds_ld[2 * kBlock];   // lse, D of the block's queries
-    __shared__ __attribute__((aligned(16))) float lds_out[kBlock * kOutS];
+    // two slots (Q, dO, lse / D) for the two query tiles of a pair; the
+    // output rows reuse the second slot's Q and dO
+    __shared__ __attribute__((aligned(16))) __bf16 lds_qd[2][2][kTE];
+    __shared__ __attribute__((aligned(16))) float lds_ld[2][2 * kBlock];   // lse, D of the tile's queries
+    static_assert(kBlock * kOutS * 4 <= 2 * kTE * 2, "output rows fit the second slot");
+    float *const lds_out = reinterpret_cast<float *>(&lds_qd[1][0][0]);
     const int lane = lane_id();
     const int g = lane >> 4, c16 = lane & 15;
     const int64_t kb = xcd_remap(blockIdx.x, gridDim.x);
@@ -1133,40 +1151,54 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
         // lse is stored by token row, D by sequence position
         X.ld = ld_src[(int64_t)h * a.N + (lane < kBlock ? tok_tile_row<ORD>(a.tm, ib, c16) : ib * kBlock + c16)];
     };
-    auto compute = [&](const Pair &X) {
-        wave_lds_sync();
-        store_bf16x8(&lds_q[lrow * kTS + lcol], X.qa0);
-        store_bf16x8(&lds_q[(lrow + 8) * kTS + lcol], X.qa1);
-        store_bf16x8(&lds_do[lrow * kTS + lcol], X.da0);
-        store_bf16x8(&lds_do[(lrow + 8) * kTS + lcol], X.da1);
-        if (lane < 2 * kBlock) lds_ld[lane] = X.ld;
-        wave_lds_sync();
-        const bf16x8 qa0 = load_bf16x8(&lds_q[c16 * kTS + 8 * g]);
-        const bf16x8 qa1 = load_bf16x8(&lds_q[c16 * kTS + 32 + 8 * g]);
-        const bf16x8 da0 = load_bf16x8(&lds_do[c16 * kTS + 8 * g]);
-        const bf16x8 da1 = load_bf16x8(&lds_do[c16 * kTS + 32 + 8 * g]);
+    // tile jt of the current batch of the segment (clamped to its last tile)
+    int colv = 0, ntl = 0;
+    auto qtile_of = [&](int jt) {
+        const int jc = min(jt, ntl - 1);
+        return __builtin_amdgcn_readlane(colv, jc / SUB) * SUB + jc % SUB;
+    };
+    // S, dP and the softmax gradient of the query tile in slot t; lane (key
+    // c16, queries 4g + i)
+    auto scores = [&](int t, bf16x4 &phi, bf16x4 &plo, bf16x4 &dhi, bf16x4 &dlo) {
+        const __bf16 *lq = lds_qd[t][0], *ldo = lds_qd[t][1];
+        const bf16x8 qa0 = load_bf16x8(&lq[c16 * kTS + 8 * g]);
+        const bf16x8 qa1 = load_bf16x8(&lq[c16 * kTS + 32 + 8 * g]);
+        const bf16x8 da0 = load_bf16x8(&ldo[c16 * kTS + 8 * g]);
+        const bf16x8 da1 = load_bf16x8(&ldo[c16 * kTS + 32 + 8 * g]);
         f32x4 s = mfma_bf16_32(qa0, kb0, f32x4{0.f, 0.f, 0.f, 0.f});
         s = mfma_bf16_32(qa1, kb1, s);
         f32x4 dp = mfma_bf16_32(da0, vb0, f32x4{0.f, 0.f, 0.f, 0.f});
         dp = mfma_bf16_32(da1, vb1, dp);
-        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lds_ld[4 * g]);
-        const f32x4 D4 = *reinterpret_cast<const f32x4 *>(&lds_ld[kBlock + 4 * g]);
+        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lds_ld[t][4 * g]);
+        const f32x4 D4 = *reinterpret_cast<const f32x4 *>(&lds_ld[t][kBlock + 4 * g]);
         float pp[4], ds[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             pp[i] = fast_exp2(s[i] * a.sl2 - l4[i] * kLog2e);
             ds[i] = pp[i] * (dp[i] - D4[i]);
         }
-        bf16x4 phi, plo, dhi, dlo;
         split4(pp, phi, plo);
         split4(ds, dhi, dlo);
-        // hi and lo parts as two 16x16x16 products each (the same MFMA time as
-        // one 16x16x32 over the duplicated dO / Q column, without the copies)
+    };
+    auto stage = [&](int t, const Pair &X) {
+        store_bf16x8(&lds_qd[t][0][lrow * kTS + lcol], X.qa0);
+        store_bf16x8(&lds_qd[t][0][(lrow + 8) * kTS + lcol], X.qa1);
+        store_bf16x8(&lds_qd[t][1][lrow * kTS + lcol], X.da0);
+        store_bf16x8(&lds_qd[t][1][(lrow + 8) * kTS + lcol], X.da1);
+        if (lane < 2 * kBlock) lds_ld[t][lane] = X.ld;
+    };
+    // one query tile: hi and lo parts as two 16x16x16 products each
+    auto compute_one = [&](const Pair &X) {
+        wave_lds_sync();
+        stage(0, X);
+        wave_lds_sync();
+        bf16x4 phi, plo, dhi, dlo;
+        scores(0, phi, plo, dhi, dlo);
         bf16x4 dT[4], qT[4];
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-            dT[dt] = lds_read_tr4(&lds_do[rofs + 16 * dt]);
-            qT[dt] = lds_read_tr4(&lds_q[rofs + 16 * dt]);
+            dT[dt] = lds_read_tr4(&lds_qd[0][1][rofs + 16 * dt]);
+            qT[dt] = lds_read_tr4(&lds_qd[0][0][rofs + 16 * dt]);
             dva[dt] = mfma_bf16_16(phi, dT[dt], dva[dt]);
             dka[dt] = mfma_bf16_16(dhi, qT[dt], dka[dt]);
         }
@@ -1176,32 +1208,59 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
             dka[dt] = mfma_bf16_16(dlo, qT[dt], dka[dt]);
         }
     };
+    // two query tiles: their score chains are independent, and the
+    // contractions over queries take the 16 queries of both tiles as the 32
+    // k-slots of one MFMA (hi and lo parts in two).  Once both are staged the
+    // registers are refilled (reload) while the pair is computed.
+    auto compute_pair = [&](Pair &X0, Pair &X1, int n0, bool reload) {
+        wave_lds_sync();
+        stage(0, X0);
+        stage(1, X1);
+        if (reload) {
+            load_pair(qtile_of(n0), X0);
+            load_pair(qtile_of(n0 + 1), X1);
+        }
+        wave_lds_sync();
+        bf16x4 phi0, plo0, dhi0, dlo0, phi1, plo1, dhi1, dlo1;
+        scores(0, phi0, plo0, dhi0, dlo0);
+        scores(1, phi1, plo1, dhi1, dlo1);
+        const bf16x8 ph = cat8(phi0, phi1), pl = cat8(plo0, plo1);
+        const bf16x8 dh = cat8(dhi0, dhi1), dl = cat8(dlo0, dlo1);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const bf16x8 dT = cat8(lds_read_tr4(&lds_qd[0][1][rofs + 16 * dt]),
+                                   lds_read_tr4(&lds_qd[1][1][rofs + 16 * dt]));
+            const bf16x8 qT = cat8(lds_read_tr4(&lds_qd[0][0][rofs + 16 * dt]),
+                                   lds_read_tr4(&lds_qd[1][0][rofs + 16 * dt]));
+            dva[dt] = mfma_bf16_32(pl, dT, mfma_bf16_32(ph, dT, dva[dt]));
+            dka[dt] = mfma_bf16_32(dl, qT, mfma_bf16_32(dh, qT, dka[dt]));
+        }
+    };
     // The segment's query blocks are read 64 at a time into one register
     // (lane j holds entry j); tile j of a batch is sub-tile j % SUB of entry
-    // j / SUB.  Ring: set r holds tile j + r; after computing it, set r is
-    // refilled with tile j + r + kDkvDepth, so at the loop head the set needed
-    // next is always the oldest one in flight.
+    // j / SUB.  Ring of kDkvDepth register sets taken two at a time: sets
+    // (r, r + 1) hold tiles j + r, j + r + 1 and are refilled with the tiles
+    // kDkvDepth further on.
+    static_assert(kDkvDepth % 2 == 0, "register sets go in pairs");
     for (int base = e0; base < e1; base += kWave) {
         const int cnt = min(kWave, e1 - base);
-        const int colv = lane < cnt ? C[base + lane] : 0;
-        const int ntl = cnt * SUB;
-        auto qtile = [&](int jt) {
-            const int jc = min(jt, ntl - 1);
-            return __builtin_amdgcn_readlane(colv, jc / SUB) * SUB + jc % SUB;
-        };
+        colv = lane < cnt ? C[base + lane] : 0;
+        ntl = cnt * SUB;
         Pair R[kDkvDepth];
 #pragma unroll
-        for (int r = 0; r < kDkvDepth; ++r) load_pair(qtile(r), R[r]);
+        for (int r = 0; r < kDkvDepth; ++r) load_pair(qtile_of(r), R[r]);
         int j = 0;
         for (; j + kDkvDepth <= ntl; j += kDkvDepth)
 #pragma unroll
-            for (int r = 0; r < kDkvDepth; ++r) {
-                compute(R[r]);
-                load_pair(qtile(j + kDkvDepth + r), R[r]);
-            }
+            for (int r = 0; r < kDkvDepth; r += 2) compute_pair(R[r], R[r + 1], j + kDkvDepth + r, true);
+        // the last ntl - j < kDkvDepth tiles sit in sets 0 .. ntl - j - 1
 #pragma unroll
-        for (int r = 0; r < kDkvDepth - 1; ++r)
-            if (j + r < ntl) compute(R[r]);
+        for (int r = 0; r + 1 < kDkvDepth; r += 2) {
+            if (j + r + 1 < ntl)
+                compute_pair(R[r], R[r + 1], 0, false);
+            else if (j + r < ntl)
+                compute_one(R[r]);
+        }
     }
     }
     // Pooled-level gradients, spread back with weight 1/B^l: every key row of

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(COUNT ? 512 : 256) void select_kernel(const float *
                 base[t] = dense ? tile * kBlock
                                 : (__builtin_amdgcn_readfirstlane(prow[tile / sub]) * sub + tile % sub) * kBlock;
                 const int cand = base[t] + col;
-                const int64_t crow = cand < n ? cand : 0;
+                const int64_t crow = (unsigned)cand < (unsigned)n ? cand : 0;   // out-of-range parent picks read row 0
                 const f32x4 *src = reinterpret_cast<const f32x4 *>(kh + crow * kHeadDim + 16 * g);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(COUNT ? 512 : 256) void select_kernel(const float *
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int c = base[t] + 4 * g + i;
-                    keys[4 * (hb + t) + i] = (live && c < n) ? score_key(acc[i], (uint32_t)c) : 0ull;
+                    keys[4 * (hb + t) + i] = (live && (unsigned)c < (unsigned)n) ? score_key(acc[i], (uint32_t)c) : 0ull;
                 }
             }
         }

@@ -118,6 +118,14 @@ def test_entry_points_validate_before_launch():
     assert lib.llsa_index_transpose(1, 10, 2, 1 << 25, fake, fake, fake, None, 0, None) == L.LLSA_ERR_UNSUPPORTED
     assert lib.llsa_index_transpose(0, 10, 2, 10, fake, fake, fake, None, 0, None) == L.LLSA_ERR_INVALID
     assert lib.llsa_index_transpose(1, 10, 2, 10, None, fake, fake, None, 0, None) == L.LLSA_ERR_INVALID
+    # transposes of every level: nothing fits the one-launch kernel at 262144
+    # tokens on level 1 (16384 keys), so that level needs a workspace
+    assert L.llsa_index_transpose_levels_workspace(good) == 0
+    big = L.problem(1, 2, 262144, levels=3)
+    assert L.llsa_index_transpose_levels_workspace(big) > 0
+    assert lib.llsa_index_transpose_levels(bp, fake, fake, fake, None, 0, None) == L.LLSA_ERR_UNSUPPORTED
+    assert lib.llsa_index_transpose_levels(gp, mis, fake, fake, None, 0, None) == L.LLSA_ERR_INVALID
+    assert lib.llsa_index_transpose_levels(ctypes.byref(big), fake, fake, fake, None, 0, None) == L.LLSA_ERR_WORKSPACE
     s = L.llsa_sizes_query(good)
     args = [fake] * 14
     assert lib.llsa_attn_bwd(gp, *args, None, 0, None) == L.LLSA_ERR_WORKSPACE

@@ -151,9 +151,9 @@ __device__ __forceinline__ bool bwd_coarse_entry(const BwdArgs &a, const int32_t
 __device__ __forceinline__ void store_grad4(void *base, int64_t off, f32x4 v, int bf) {
     if (bf) {
         const bf16x4 b = to_bf16x4(f32x4{v[0], v[1], v[2], v[3]});
-        *reinterpret_cast<u32x2 *>((__bf16 *)base + off) = __builtin_bit_cast(u32x2, b);
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x2, b), reinterpret_cast<u32x2 *>((__bf16 *)base + off));
     } else {
-        *reinterpret_cast<f32x4 *>((float *)base + off) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>((float *)base + off));
     }
 }
 __device__ __forceinline__ void store_grad1(void *base, int64_t off, float v, int bf) {
@@ -561,10 +561,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
     auto load_q = [&](int jb, QRegs &X) {
         const int b = ib0 + w * 4 + jb;
         const int64_t o0 = head_off + trow(b, lrow) + lcol, o1 = head_off + trow(b, lrow + 8) + lcol;
-        X.qa0 = load_bf16x8(q + o0);
-        X.qa1 = load_bf16x8(q + o1);
-        X.da0 = load_bf16x8(dout + o0);
-        X.da1 = load_bf16x8(dout + o1);
+        X.qa0 = load_bf16x8_nt(q + o0);
+        X.qa1 = load_bf16x8_nt(q + o1);
+        X.da0 = load_bf16x8_nt(dout + o0);
+        X.da1 = load_bf16x8_nt(dout + o1);
         X.lse2 = lse[(int64_t)h * a.N + tok_tile_row<ORD>(a.tm, b, c16)] * kLog2e;
     };
     QRegs X;
@@ -861,10 +861,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_b64_kernel(
         load_tile(0);
         const float lse2 = lse[(int64_t)h * a.N + tok_tile_row<ORD>(a.tm, qt, c16)] * kLog2e;
         wave_lds_sync();
-        stage_rows(lds_q[w], load_bf16x8(q + head_off + trow(qt, lrow) + lcol),
-                   load_bf16x8(q + head_off + trow(qt, lrow + 8) + lcol));
-        stage_rows(lds_do[w], load_bf16x8(dout + head_off + trow(qt, lrow) + lcol),
-                   load_bf16x8(dout + head_off + trow(qt, lrow + 8) + lcol));
+        stage_rows(lds_q[w], load_bf16x8_nt(q + head_off + trow(qt, lrow) + lcol),
+                   load_bf16x8_nt(q + head_off + trow(qt, lrow + 8) + lcol));
+        stage_rows(lds_do[w], load_bf16x8_nt(dout + head_off + trow(qt, lrow) + lcol),
+                   load_bf16x8_nt(dout + head_off + trow(qt, lrow + 8) + lcol));
         wave_lds_sync();
         const bf16x8 qa0 = load_bf16x8(&lds_q[w][c16 * kTS + 8 * g]);
         const bf16x8 qa1 = load_bf16x8(&lds_q[w][c16 * kTS + 32 + 8 * g]);
@@ -1123,8 +1123,8 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
     if (e1 > e0) {
     const __bf16 *krow = k + head_off + trow(f, c16);
     const __bf16 *vrow = v + head_off + trow(f, c16);
-    const bf16x8 kb0 = load_bf16x8(krow + 8 * g), kb1 = load_bf16x8(krow + 32 + 8 * g);
-    const bf16x8 vb0 = load_bf16x8(vrow + 8 * g), vb1 = load_bf16x8(vrow + 32 + 8 * g);
+    const bf16x8 kb0 = load_bf16x8_nt(krow + 8 * g), kb1 = load_bf16x8_nt(krow + 32 + 8 * g);
+    const bf16x8 vb0 = load_bf16x8_nt(vrow + 8 * g), vb1 = load_bf16x8_nt(vrow + 32 + 8 * g);
     const int rofs = (4 * g + (c16 >> 2)) * kTS + 4 * (c16 & 3);
     // Per query block: its Q / dO tiles loaded as whole 128-byte rows per
     // instruction (lane l: rows l / 8 and l / 8 + 8, 16-byte chunk l % 8),
@@ -1292,9 +1292,10 @@ __global__ __launch_bounds__(64, 3) void bwd_dkv_bf16_kernel(
             const f32x4 x = *reinterpret_cast<const f32x4 *>(&lds_out[r * kOutS + oc]) * mul + add;
             const int64_t off = head_off + trow(f, r) + oc;
             if (a.grad_bf16)
-                *reinterpret_cast<u32x2 *>((__bf16 *)dst + off) = __builtin_bit_cast(u32x2, to_bf16x4(x));
+                __builtin_nontemporal_store(__builtin_bit_cast(u32x2, to_bf16x4(x)),
+                                            reinterpret_cast<u32x2 *>((__bf16 *)dst + off));
             else
-                *reinterpret_cast<f32x4 *>((float *)dst + off) = x;
+                __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>((float *)dst + off));
         }
     };
     store_tile(dka, a.scale, ck, dk);
@@ -1437,9 +1438,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_b64_kernel(
             const f32x4 x = *reinterpret_cast<const f32x4 *>(&lds_out[r * kOutS + oc]) * mul + add;
             const int64_t off = head_off + trow(f, r) + oc;
             if (a.grad_bf16)
-                *reinterpret_cast<u32x2 *>((__bf16 *)dst + off) = __builtin_bit_cast(u32x2, to_bf16x4(x));
+                __builtin_nontemporal_store(__builtin_bit_cast(u32x2, to_bf16x4(x)),
+                                            reinterpret_cast<u32x2 *>((__bf16 *)dst + off));
             else
-                *reinterpret_cast<f32x4 *>((float *)dst + off) = x;
+                __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>((float *)dst + off));
         }
     };
     store_tile(dka, a.scale, ck, dk);

@@ -312,8 +312,8 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
     // element offset (within the head) of row r of sequence block b
     auto trow = [&](int b, int r) { return (int64_t)tok_tile_row<ORD>(a.tm, b, r) * kHeadDim; };
     const int lr = lane >> 3, lc = (lane & 7) * 8;
-    const bf16x8 qr0 = load_bf16x8(q + head_off + trow(ib, lr) + lc);
-    const bf16x8 qr1 = load_bf16x8(q + head_off + trow(ib, lr + 8) + lc);
+    const bf16x8 qr0 = load_bf16x8_nt(q + head_off + trow(ib, lr) + lc);
+    const bf16x8 qr1 = load_bf16x8_nt(q + head_off + trow(ib, lr + 8) + lc);
     const int32_t *fine = idx + blk * KT;
     bf16x8 kr[KT][2], vr[KT][2];
 #pragma unroll
@@ -450,8 +450,8 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
         *reinterpret_cast<u32x2 *>(vw + c16 * kVStride + 16 * dt + 4 * g) = __builtin_bit_cast(u32x2, rb);
     }
     wave_lds_sync();
-    store_bf16x8(o + head_off + trow(ib, lr) + lc, load_bf16x8(vw + lr * kVStride + lc));
-    store_bf16x8(o + head_off + trow(ib, lr + 8) + lc, load_bf16x8(vw + (lr + 8) * kVStride + lc));
+    store_bf16x8_nt(o + head_off + trow(ib, lr) + lc, load_bf16x8(vw + lr * kVStride + lc));
+    store_bf16x8_nt(o + head_off + trow(ib, lr + 8) + lc, load_bf16x8(vw + (lr + 8) * kVStride + lc));
     if (g == 0) lse[(int64_t)h * a.N + tok_tile_row<ORD>(a.tm, ib, c16)] = (mx + log2f(lsum)) * kLn2;
 }
 
@@ -492,8 +492,8 @@ __global__ __launch_bounds__(256, NCH == 1 ? 3 : 2) void attn_fwd_chunk_kernel(
         store_bf16x8(dst + lr * kVStride + lc, r0);
         store_bf16x8(dst + (lr + 8) * kVStride + lc, r1);
     };
-    stage_rows(qw, load_bf16x8(q + head_off + trow(ib, lr) + lc),
-               load_bf16x8(q + head_off + trow(ib, lr + 8) + lc));
+    stage_rows(qw, load_bf16x8_nt(q + head_off + trow(ib, lr) + lc),
+               load_bf16x8_nt(q + head_off + trow(ib, lr + 8) + lc));
     const int32_t *fine = idx + blk * a.K1;
     float m = -INFINITY, lsum = 0.f;
     f32x4 oacc[4];
@@ -632,8 +632,8 @@ __global__ __launch_bounds__(256, NCH == 1 ? 3 : 2) void attn_fwd_chunk_kernel(
         *reinterpret_cast<u32x2 *>(vw + c16 * kVStride + 16 * dt + 4 * g) = __builtin_bit_cast(u32x2, to_bf16x4(r));
     }
     wave_lds_sync();
-    store_bf16x8(o + head_off + trow(ib, lr) + lc, load_bf16x8(vw + lr * kVStride + lc));
-    store_bf16x8(o + head_off + trow(ib, lr + 8) + lc, load_bf16x8(vw + (lr + 8) * kVStride + lc));
+    store_bf16x8_nt(o + head_off + trow(ib, lr) + lc, load_bf16x8(vw + lr * kVStride + lc));
+    store_bf16x8_nt(o + head_off + trow(ib, lr + 8) + lc, load_bf16x8(vw + (lr + 8) * kVStride + lc));
     if (g == 0) lse[(int64_t)h * a.N + tok_tile_row<ORD>(a.tm, ib, c16)] = (m + log2f(lsum)) * kLn2;
 }
 
@@ -675,8 +675,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_b64_kernel(
         store_bf16x8(dst + (lr + 8) * kVStride + lc, r1);
     };
     __bf16 *qw = qs_all[w];
-    stage_rows(qw, load_bf16x8(q + head_off + trow(qt, lr) + lc),
-               load_bf16x8(q + head_off + trow(qt, lr + 8) + lc));
+    stage_rows(qw, load_bf16x8_nt(q + head_off + trow(qt, lr) + lc),
+               load_bf16x8_nt(q + head_off + trow(qt, lr + 8) + lc));
     const int32_t *fine = idx + blk * a.K1;
     // wave w's tile of picked block j, as whole rows
     bf16x8 kr[2], vr[2];
@@ -786,8 +786,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_b64_kernel(
         *reinterpret_cast<u32x2 *>(qw + c16 * kVStride + 16 * dt + 4 * g) = __builtin_bit_cast(u32x2, to_bf16x4(r));
     }
     wave_lds_sync();
-    store_bf16x8(o + head_off + trow(qt, lr) + lc, load_bf16x8(qw + lr * kVStride + lc));
-    store_bf16x8(o + head_off + trow(qt, lr + 8) + lc, load_bf16x8(qw + (lr + 8) * kVStride + lc));
+    store_bf16x8_nt(o + head_off + trow(qt, lr) + lc, load_bf16x8(qw + lr * kVStride + lc));
+    store_bf16x8_nt(o + head_off + trow(qt, lr + 8) + lc, load_bf16x8(qw + (lr + 8) * kVStride + lc));
     if (g == 0) lse[(int64_t)h * a.N + tok_tile_row<ORD>(a.tm, qt, c16)] = (m + log2f(lsum)) * kLn2;
 }
 

@@ -66,6 +66,15 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const __bf16 *p) {
 __device__ __forceinline__ void store_bf16x8(__bf16 *p, bf16x8 v) {
     *reinterpret_cast<u32x4 *>(p) = __builtin_bit_cast(u32x4, v);
 }
+// Non-temporal (streaming) forms for rows a kernel reads or writes once: they
+// do not displace the gathered tiles that neighbouring workgroups re-read
+// from L2.
+__device__ __forceinline__ bf16x8 load_bf16x8_nt(const __bf16 *p) {
+    return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)));
+}
+__device__ __forceinline__ void store_bf16x8_nt(__bf16 *p, bf16x8 v) {
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
+}
 
 // Buffer resource over the n_bytes at p (p the same for the whole wave):
 // loads through it take a 32-bit byte offset, which saves the 64-bit address

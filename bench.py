@@ -228,13 +228,13 @@ def transpose_scaling(L, dev, reps):
         L.llsa_attn_fwd(p, q, k, v, B.pyr_k, B.pyr_v, B.idx, B.o, B.lse)
 
         def lists(kind):
+            if kind == "csr":   # every level in one call, as the bench step does
+                L.transpose_levels(B)
+                return
             for l in range(1, B.s.enrich + 2):
                 nl, kl = B.s.level_tokens[l], B.s.level_k[l]
                 pl, cl = B.csr_level(l)
-                if kind == "csr":
-                    L.llsa_index_transpose(heads, nl, kl, nl, B.index_level(l), pl, cl, B.tws, B.tws_bytes)
-                else:
-                    L.llsa_index_transpose_mask(heads, nl, kl, nl, B.index_level(l), pl, cl, mw, mws)
+                L.llsa_index_transpose_mask(heads, nl, kl, nl, B.index_level(l), pl, cl, mw, mws)
 
         def backward(kind):
             lists(kind)

@@ -21,7 +21,9 @@
 //     gradients of every coarse level spread back through the mean (each of
 //     the B^l tokens under a pooled token receives 1/B^l of its gradient).
 // Accumulation order is fixed everywhere (no float atomics), so results are
-// bitwise reproducible.
+// bitwise reproducible.  Rows a pass reads or writes once (its own Q and dO
+// or K and V, and the gradients) use non-temporal loads and stores, leaving
+// the L2 to the gathered tiles.
 #include "common.hpp"
 #include "internal.hpp"
 

@@ -9,12 +9,14 @@
 // transposed, S^T = K Q^T, on v_mfma_f32_16x16x32_bf16 so that lane l owns
 // query l%16 and keys 4(l/16)..+3 of every 16-key tile; that register layout
 // is exactly the B operand of O^T += V^T P^T, so probabilities never leave
-// registers.  K and Q tiles are loaded straight from HBM into MFMA operand
-// registers; a gathered V tile goes through LDS once and is read back with
-// the gfx950 transposing LDS load.  Coarse tokens (float32 pyramid) are
-// converted to bf16 on the fly and carry the logit bias log2(B^l).  Softmax
-// runs in the exp2 domain over chunks of up to 8 tiles with one cross-lane
-// max per chunk.
+// registers.  Q, K and V tiles are loaded as whole 128-byte rows and pass
+// through LDS: the Q and K operand rows are read back as they are, V with the
+// gfx950 transposing LDS load.  The query block's own Q and O rows, which
+// nothing else reads, go through non-temporal loads and stores, so the L2
+// keeps the gathered K / V tiles that neighbouring query blocks share.
+// Coarse tokens (float32 pyramid) are converted to bf16 on the fly and carry
+// the logit bias log2(B^l).  Softmax runs in the exp2 domain over chunks of
+// up to 8 tiles with one cross-lane max per chunk.
 //
 // f32 path: one thread per query, all arithmetic in float32 (used for f32
 // inputs, where the output tolerance is tighter than bf16 products allow).

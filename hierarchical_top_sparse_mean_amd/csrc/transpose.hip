@@ -23,6 +23,9 @@
 // bits, into csr_col; csr_ptr then comes from a binary search of every key in
 // the sorted keys.  Every pick is read once per pass whatever the number of
 // keys, and the histograms stay at 4096 buckets per range.
+// Matrices of at most 131072 picks and 4096 keys take a single kernel
+// instead (tr_one_kernel below), and several such matrices -- the levels of
+// one problem -- share one launch.
 #include <algorithm>
 
 #include "common.hpp"

@@ -307,9 +307,12 @@ __global__ __launch_bounds__(kTrThreads) void tr_bounds_kernel(const int32_t *__
 }
 
 // Matrices of at most kTrOneMaxPicks picks and kTrOneMaxCols keys: the whole
-// transpose in one launch.  Workgroup (part, b) owns keys [256 part, 256 part
-// + 256) of matrix b and reads every pick of the matrix (from L2: each pick
-// is read by cols / 256 workgroups):
+// transpose in one launch.  Workgroup (part, b) owns keys [512 part, 512 part
+// + 512) of matrix b and reads every pick of the matrix (from L2: each pick
+// is read by cols / 512 workgroups).  Every workgroup scans all the picks of
+// its matrix, so fewer, wider parts do less work in total; 512 keys keep the
+// per-wave counters and masks at 96 KB of LDS, one workgroup per CU, and the
+// levels of a 65536-token problem in fewer workgroups than CUs:
 //  - the number of picks with a smaller key gives where its keys' lists start;
 //  - wave w owns elements [w per, (w + 1) per) and counts their picks of its
 //    keys per key, so an exclusive prefix over the waves, plus the scan over
@@ -323,13 +326,15 @@ __global__ __launch_bounds__(kTrThreads) void tr_bounds_kernel(const int32_t *__
 // No workspace, no global atomic, nothing to clear beforehand.
 constexpr int kTrOneThreads = 1024;
 constexpr int kTrOneWaves = kTrOneThreads / kWave;
-constexpr int kTrOneKeys = 256;                                    // keys per workgroup
+constexpr int kTrOneKeys = 512;                                    // keys per workgroup
 constexpr int kTrOneChunks = 32;                                   // 64-pick chunks per round
 constexpr int kTrOneRound = kTrOneChunks * kWave;                  // picks a wave holds at once
 constexpr int kTrOneMaxPicks = 4 * kTrOneWaves * kTrOneRound;      // 131072 per matrix
 constexpr int kTrOneMaxCols = 4096;
 constexpr int kTrOneEBits = 17;                                    // a queued pick: key << 17 | element
 static_assert(kTrOneMaxPicks <= (1 << kTrOneEBits), "element index must fit its field");
+static_assert(((uint64_t)kTrOneKeys << kTrOneEBits) <= (1ull << 32), "key offset and element fit 32 bits");
+static_assert(kTrOneKeys <= kTrOneThreads && kTrOneKeys % kWave == 0, "a thread per key of the part");
 
 static bool tr_one_fits(int rows, int k, int cols) {
     return (int64_t)rows * k <= kTrOneMaxPicks && cols <= kTrOneMaxCols;
@@ -399,7 +404,7 @@ __global__ __launch_bounds__(kTrOneThreads) void tr_one_kernel(TrOneArgs A) {
     for (int d = 1; d < kWave; d <<= 1) below += __shfl_xor(below, d, kWave);
     if (lane == 0) below_w[w] = below;
     __syncthreads();
-    // thread t < 256: key c0 + t -- prefix over the waves, then the scan over keys
+    // thread t < kTrOneKeys: key c0 + t -- prefix over the waves, then the scan over keys
     int tot = 0;
     if (tid < kTrOneKeys) {
 #pragma unroll

@@ -1510,19 +1510,22 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(
     store_grad1(dq, row, acc * a.scale, a.grad_bf16);
 }
 
-// Pooled-token gradients (f32): one wave per (level, pooled token).  The wave
-// walks the CSR of I^(l) and every query block under each row that picked the
-// token, 16 query rows at a time.
-
-__global__ __launch_bounds__(256) void bwd_coarse_f32_kernel(
+// Pooled-token gradients (f32): one workgroup of kCoarseWaves waves per
+// (level, pooled token).  The query blocks under the rows that picked the
+// token (from the CSR of I^(l)) are dealt out to the waves in turn, 16 query
+// rows at a time; each wave keeps its own partial sums, and the partials are
+// added in wave order at the end, so the result does not depend on timing.
+constexpr int kCoarseWaves = 16;
+__global__ __launch_bounds__(kCoarseWaves * kWave) void bwd_coarse_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ pk, const float *__restrict__ pv,
     const int32_t *__restrict__ idx, const float *__restrict__ lse, const float *__restrict__ dout,
     const int32_t *__restrict__ csr_ptr, const int32_t *__restrict__ csr_col, BwdWs ws, BwdArgs a,
     int j) {
-    const int64_t t = (int64_t)blockIdx.x * 4 + wave_id();
+    __shared__ float red[kCoarseWaves][2][kHeadDim];
+    const int64_t t = blockIdx.x;
     const int nl = a.cl_n[j], kl = a.cl_k[j], span = a.cl_span[j];
     if (t >= (int64_t)a.bh * nl) return;
-    const int lane = lane_id();
+    const int lane = lane_id(), w = wave_id();
     const int h = (int)(t / nl);
     const int c = (int)(t % nl);
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
@@ -1533,39 +1536,48 @@ __global__ __launch_bounds__(256) void bwd_coarse_f32_kernel(
     const int32_t *P = csr_ptr + a.cl_ptr_off[j] + (int64_t)h * (nl + 1);
     const int32_t *C = csr_col + a.cl_col_off[j] + (int64_t)h * nl * kl;
     const int e0 = __builtin_amdgcn_readfirstlane(P[c]), e1 = __builtin_amdgcn_readfirstlane(P[c + 1]);
-    for (int e = e0; e < e1; ++e) {
-        const int r = __builtin_amdgcn_readfirstlane(C[e]);
-        for (int ib = r * span; ib < (r + 1) * span; ++ib) {
-            const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
-            if (a.drop && a.K1 >= span) {
-                int cov = 0;
-                for (int ff = 0; ff < a.K1; ++ff) cov += (fine[ff] / span == c) ? 1 : 0;
-                if (cov == span) continue;
+    // query block n of the token's list: picking row e0 + n / span, block n % span under it
+    for (int n = w; n < (e1 - e0) * span; n += kCoarseWaves) {
+        const int r = __builtin_amdgcn_readfirstlane(C[e0 + n / span]);
+        const int ib = r * span + n % span;
+        const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
+        if (a.drop && a.K1 >= span) {
+            int cov = 0;
+            for (int ff = 0; ff < a.K1; ++ff) cov += (fine[ff] / span == c) ? 1 : 0;
+            if (cov == span) continue;
+        }
+        for (int qt = ib * a.sub; qt < (ib + 1) * a.sub; ++qt) {
+            float qx[kBlock], gx[kBlock];
+            int64_t srow[kBlock];
+#pragma unroll
+            for (int tt = 0; tt < kBlock; ++tt) {
+                srow[tt] = tok_row(a.tm, qt * kBlock + tt);
+                qx[tt] = q[head_off + srow[tt] * kHeadDim + lane];
+                gx[tt] = dout[head_off + srow[tt] * kHeadDim + lane];
             }
-            for (int qt = ib * a.sub; qt < (ib + 1) * a.sub; ++qt) {
-                float qx[kBlock], gx[kBlock];
-                int64_t srow[kBlock];
 #pragma unroll
-                for (int tt = 0; tt < kBlock; ++tt) {
-                    srow[tt] = tok_row(a.tm, qt * kBlock + tt);
-                    qx[tt] = q[head_off + srow[tt] * kHeadDim + lane];
-                    gx[tt] = dout[head_off + srow[tt] * kHeadDim + lane];
-                }
-#pragma unroll
-                for (int tt = 0; tt < kBlock; ++tt) {
-                    const int64_t tok = (int64_t)h * a.N + (int64_t)qt * kBlock + tt;
-                    const float s = wave_sum(qx[tt] * kx);
-                    const float dp = wave_sum(gx[tt] * vx);
-                    const float p = exp2f(s * a.sl2 + bias - lse[(int64_t)h * a.N + srow[tt]] * kLog2e);
-                    const float ds = p * (dp - ws.D[tok]);
-                    gk = fmaf(ds, qx[tt], gk);
-                    gv = fmaf(p, gx[tt], gv);
-                }
+            for (int tt = 0; tt < kBlock; ++tt) {
+                const int64_t tok = (int64_t)h * a.N + (int64_t)qt * kBlock + tt;
+                const float s = wave_sum(qx[tt] * kx);
+                const float dp = wave_sum(gx[tt] * vx);
+                const float p = exp2f(s * a.sl2 + bias - lse[(int64_t)h * a.N + srow[tt]] * kLog2e);
+                const float ds = p * (dp - ws.D[tok]);
+                gk = fmaf(ds, qx[tt], gk);
+                gv = fmaf(p, gx[tt], gv);
             }
         }
     }
-    ws.dpk[a.cl_grad_off[j] + ((int64_t)h * nl + c) * kHeadDim + lane] = gk * a.scale;
-    ws.dpv[a.cl_grad_off[j] + ((int64_t)h * nl + c) * kHeadDim + lane] = gv;
+    red[w][0][lane] = gk;
+    red[w][1][lane] = gv;
+    __syncthreads();
+    if (w != 0) return;
+    float sk = 0.f, sv = 0.f;
+    for (int x = 0; x < kCoarseWaves; ++x) {
+        sk += red[x][0][lane];
+        sv += red[x][1][lane];
+    }
+    ws.dpk[a.cl_grad_off[j] + ((int64_t)h * nl + c) * kHeadDim + lane] = sk * a.scale;
+    ws.dpv[a.cl_grad_off[j] + ((int64_t)h * nl + c) * kHeadDim + lane] = sv;
 }
 
 // Pass C (f32): one wave per key token.
@@ -1691,7 +1703,7 @@ hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, cons
                            (const float *)o, lse, (const float *)dout, dq, ws, a);
         for (int j = 0; j < a.ncl; ++j) {
             const int64_t nt = (int64_t)g.bh * a.cl_n[j];
-            hipLaunchKernelGGL(bwd_coarse_f32_kernel, dim3((unsigned)((nt + 3) / 4)), dim3(256), 0,
+            hipLaunchKernelGGL(bwd_coarse_f32_kernel, dim3((unsigned)nt), dim3(kCoarseWaves * kWave), 0,
                                s, (const float *)q, pk, pv, idx, lse, (const float *)dout, csr_ptr,
                                csr_col, ws, a, j);
         }

@@ -130,6 +130,10 @@ int llsa_select(const llsa_problem *p, const float *pyr_q, const float *pyr_k,
  * i.e. logit + ln B^l; see drop_covered).  Logits are scale * q.k.  The
  * kernels read only the index lists, never a dense mask.
  * In : q, k, v (dtype), pyr_k, pyr_v (float32), idx.
+ *      idx must be as llsa_select writes it: every row of level l holds K_l
+ *      distinct values in [0, n_l), ascending.  The values are not checked
+ *      on the host or the device; others make the kernels read out of
+ *      bounds.
  * Out: o [batch, heads, seq_len, head_dim] (dtype), lse [batch*heads*seq_len]
  *      float32 natural-log normaliser of every query row.
  */
@@ -221,7 +225,9 @@ int llsa_index_transpose_mask(int32_t n_batch, int32_t n_rows, int32_t k, int32_
  * then spread back to the B^l tokens under each pooled token (mean adjoint).
  * In : everything llsa_attn_fwd read, its outputs o and lse, dout (dtype),
  *      csr_ptr / csr_col for levels 1..Le+1 at sizes.csr_*_offset[l], each
- *      produced by llsa_index_transpose(batch*heads, n_l, K_l, n_l, ...).
+ *      produced by llsa_index_transpose(batch*heads, n_l, K_l, n_l, ...) (or
+ *      llsa_index_transpose_levels) from that same idx; like idx, the lists
+ *      are not checked.
  * Out: dq, dk, dv [batch, heads, seq_len, head_dim] in grad_dtype.
  * workspace: at least sizes.bwd_workspace_bytes of device memory.
  */

@@ -498,30 +498,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
     __bf16 *const k1s = lds_kv[4 * w + 2], *const v1s = lds_kv[4 * w + 3];
     float *const out_w = reinterpret_cast<float *>(k1s);   // dQ rows, over the second slot pair
 
-    // ---- coarse tile, staged by the whole workgroup: thread (entry e, quarter p)
+    // ---- coarse tile, staged by the whole workgroup: thread (entry e, quarter
+    // p).  Its pyramid rows are requested first and written to LDS once the
+    // wave's first fine loads are out (the memory counter is waited on in
+    // order, so the fine loads do not wait for the LDS writes).
+    const int ce = threadIdx.x >> 4, cpart = threadIdx.x & 15;
+    bool cok = false;
+    int cjs = 0, ccol_v = -1;
+    f32x4 ckk = zero4, cvv = zero4;
     if constexpr (CO) {
-        const int e = threadIdx.x >> 4, part = threadIdx.x & 15;
-        int j = 0, pick = e;
+        int j = 0, pick = ce;
         while (j < a.ncl - 1 && pick >= a.cl_k[j]) {
             pick -= a.cl_k[j];
             ++j;
         }
-        const bool ok = e < a.ncoarse;
-        const int js = ok ? j : 0, ps = ok ? pick : 0;
-        const int anc = ib0 >> (4 * (js + 1));   // ancestor at level js + 2
-        const int c = idx[a.cl_idx_off[js] + ((int64_t)h * a.cl_n[js] + anc) * a.cl_k[js] + ps];
-        const int64_t roff = a.cl_pyr_off[js] + ((int64_t)h * a.cl_n[js] + c) * kHeadDim + 4 * part;
-        f32x4 kk = *reinterpret_cast<const f32x4 *>(pk + roff);
-        f32x4 vv = *reinterpret_cast<const f32x4 *>(pv + roff);
-        if (!ok) kk = vv = zero4;
-        const bf16x4 kb = to_bf16x4(f32x4{kk[0], kk[1], kk[2], kk[3]});
-        const bf16x4 vb = to_bf16x4(f32x4{vv[0], vv[1], vv[2], vv[3]});
-        *reinterpret_cast<u32x2 *>(&ck[e * kTS + 4 * part]) = __builtin_bit_cast(u32x2, kb);
-        *reinterpret_cast<u32x2 *>(&cv[e * kTS + 4 * part]) = __builtin_bit_cast(u32x2, vb);
-        if (part == 0) {
-            cbias[e] = ok ? 4.0f * (float)(js + 2) : -INFINITY;
-            ccol[e] = ok && js == 0 ? c : -1;
-        }
+        cok = ce < a.ncoarse;
+        cjs = cok ? j : 0;
+        const int ps = cok ? pick : 0;
+        const int anc = ib0 >> (4 * (cjs + 1));   // ancestor at level js + 2
+        const int c = idx[a.cl_idx_off[cjs] + ((int64_t)h * a.cl_n[cjs] + anc) * a.cl_k[cjs] + ps];
+        const int64_t roff = a.cl_pyr_off[cjs] + ((int64_t)h * a.cl_n[cjs] + c) * kHeadDim + 4 * cpart;
+        ckk = *reinterpret_cast<const f32x4 *>(pk + roff);
+        cvv = *reinterpret_cast<const f32x4 *>(pv + roff);
+        ccol_v = cok && cjs == 0 ? c : -1;
     }
 
     // ---- this wave's fine picks: pick u (block u / K1T, pick u % K1T) sits in
@@ -575,6 +574,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
     TileRegs R[PD];
 #pragma unroll
     for (int r = 0; r < PD; ++r) load_tile(r, R[r]);
+    if constexpr (CO) {
+        if (!cok) ckk = cvv = zero4;
+        const bf16x4 kb = to_bf16x4(f32x4{ckk[0], ckk[1], ckk[2], ckk[3]});
+        const bf16x4 vb = to_bf16x4(f32x4{cvv[0], cvv[1], cvv[2], cvv[3]});
+        *reinterpret_cast<u32x2 *>(&ck[ce * kTS + 4 * cpart]) = __builtin_bit_cast(u32x2, kb);
+        *reinterpret_cast<u32x2 *>(&cv[ce * kTS + 4 * cpart]) = __builtin_bit_cast(u32x2, vb);
+        if (cpart == 0) {
+            cbias[ce] = cok ? 4.0f * (float)(cjs + 2) : -INFINITY;
+            ccol[ce] = ccol_v;
+        }
+    }
 
     f32x4 dkc[4], dvc[4];
 #pragma unroll

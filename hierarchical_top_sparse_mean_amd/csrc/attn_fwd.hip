@@ -308,46 +308,55 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
     const __bf16 *vh = v + head_off;
     __bf16 *vw = vs_all[w];
 
-    // ---- this wave's loads: Q, then every fine K / V tile, each as whole
-    // 128-byte rows per instruction (lane l: rows l / 8 and l / 8 + 8, 16-byte
-    // chunk l % 8); rows reach the MFMA operand layout through LDS
+    // ---- this wave's loads, in the order they are used (the memory counter
+    // is waited on in order): the coarse tile's pyramid rows, Q, every fine K
+    // tile, then every V tile, each tile as whole 128-byte rows per
+    // instruction (lane l: rows l / 8 and l / 8 + 8, 16-byte chunk l % 8);
+    // rows reach the MFMA operand layout through LDS
     // element offset (within the head) of row r of sequence block b
     auto trow = [&](int b, int r) { return (int64_t)tok_tile_row<ORD>(a.tm, b, r) * kHeadDim; };
     const int lr = lane >> 3, lc = (lane & 7) * 8;
+    // ---- coarse tile, staged by the whole workgroup: thread (entry e, quarter p);
+    // its pyramid rows are requested before the fine tiles, written to LDS after
+    const int ce = threadIdx.x >> 4, cpart = threadIdx.x & 15;   // 16 entries x 16 x 4 columns
+    int cj, cpick;
+    const bool cok = coarse_locate(a, ce, cj, cpick);
+    const int cjs = cok ? cj : 0, cps = cok ? cpick : 0;
+    f32x4 ckk, cvv;
+    {
+        const int anc = ib0 >> (4 * (cjs + 1));                       // ancestor at level js+2
+        const int c = idx[a.cl_idx_off[cjs] + ((int64_t)h * a.cl_n[cjs] + anc) * a.cl_k[cjs] + cps];
+        const int64_t row = a.cl_pyr_off[cjs] + ((int64_t)h * a.cl_n[cjs] + c) * kHeadDim + 4 * cpart;
+        ckk = *reinterpret_cast<const f32x4 *>(pk + row);
+        cvv = *reinterpret_cast<const f32x4 *>(pv + row);
+    }
     const bf16x8 qr0 = load_bf16x8_nt(q + head_off + trow(ib, lr) + lc);
     const bf16x8 qr1 = load_bf16x8_nt(q + head_off + trow(ib, lr + 8) + lc);
     const int32_t *fine = idx + blk * KT;
     bf16x8 kr[KT][2], vr[KT][2];
+    int fp[KT];
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-        const int f = __builtin_amdgcn_readfirstlane(fine[t]);
-        const int64_t o0 = trow(f, lr) + lc, o1 = trow(f, lr + 8) + lc;
-        kr[t][0] = load_bf16x8(kh + o0);
-        kr[t][1] = load_bf16x8(kh + o1);
-        vr[t][0] = load_bf16x8(vh + o0);
-        vr[t][1] = load_bf16x8(vh + o1);
+        fp[t] = __builtin_amdgcn_readfirstlane(fine[t]);
+        kr[t][0] = load_bf16x8(kh + trow(fp[t], lr) + lc);
+        kr[t][1] = load_bf16x8(kh + trow(fp[t], lr + 8) + lc);
+    }
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+        vr[t][0] = load_bf16x8(vh + trow(fp[t], lr) + lc);
+        vr[t][1] = load_bf16x8(vh + trow(fp[t], lr + 8) + lc);
     }
     auto stage_rows = [&](__bf16 *dst, bf16x8 r0, bf16x8 r1) {
         store_bf16x8(dst + (lane >> 3) * kVStride + (lane & 7) * 8, r0);
         store_bf16x8(dst + ((lane >> 3) + 8) * kVStride + (lane & 7) * 8, r1);
     };
-    // ---- coarse tile, staged by the whole workgroup: thread (entry e, quarter p)
     {
-        const int e = threadIdx.x >> 4, part = threadIdx.x & 15;   // 16 entries x 16 x 4 columns
-        int j, pick;
-        const bool ok = coarse_locate(a, e, j, pick);
-        const int js = ok ? j : 0, ps = ok ? pick : 0;
-        const int anc = ib0 >> (4 * (js + 1));                       // ancestor at level js+2
-        const int c = idx[a.cl_idx_off[js] + ((int64_t)h * a.cl_n[js] + anc) * a.cl_k[js] + ps];
-        const int64_t row = a.cl_pyr_off[js] + ((int64_t)h * a.cl_n[js] + c) * kHeadDim + 4 * part;
-        f32x4 kk = *reinterpret_cast<const f32x4 *>(pk + row);
-        f32x4 vv = *reinterpret_cast<const f32x4 *>(pv + row);
-        if (!ok) kk = vv = f32x4{0.f, 0.f, 0.f, 0.f};
-        const bf16x4 kb = to_bf16x4(f32x4{kk[0], kk[1], kk[2], kk[3]});
-        const bf16x4 vb = to_bf16x4(f32x4{vv[0], vv[1], vv[2], vv[3]});
-        *reinterpret_cast<u32x2 *>(&ck[e * kVStride + 4 * part]) = __builtin_bit_cast(u32x2, kb);
-        *reinterpret_cast<u32x2 *>(&cv[e * kVStride + 4 * part]) = __builtin_bit_cast(u32x2, vb);
-        if (part == 0) cbias[e] = ok ? 4.0f * (float)(js + 2) : -INFINITY;
+        if (!cok) ckk = cvv = f32x4{0.f, 0.f, 0.f, 0.f};
+        const bf16x4 kb = to_bf16x4(f32x4{ckk[0], ckk[1], ckk[2], ckk[3]});
+        const bf16x4 vb = to_bf16x4(f32x4{cvv[0], cvv[1], cvv[2], cvv[3]});
+        *reinterpret_cast<u32x2 *>(&ck[ce * kVStride + 4 * cpart]) = __builtin_bit_cast(u32x2, kb);
+        *reinterpret_cast<u32x2 *>(&cv[ce * kVStride + 4 * cpart]) = __builtin_bit_cast(u32x2, vb);
+        if (cpart == 0) cbias[ce] = cok ? 4.0f * (float)(cjs + 2) : -INFINITY;
     }
     // ---- fine scores: K tiles pass through the V staging slots, kHalf at a
     // time (V stays in registers until its half is staged)
@@ -494,9 +503,47 @@ __global__ __launch_bounds__(256, NCH == 1 ? 3 : 2) void attn_fwd_chunk_kernel(
         store_bf16x8(dst + lr * kVStride + lc, r0);
         store_bf16x8(dst + (lr + 8) * kVStride + lc, r1);
     };
-    stage_rows(qw, load_bf16x8_nt(q + head_off + trow(ib, lr) + lc),
-               load_bf16x8_nt(q + head_off + trow(ib, lr + 8) + lc));
+    // Loads go out in the order they are used (the memory counter is waited
+    // on in order): Q, the coarse entry's pick, with a single chunk its K then
+    // V tiles, the coarse pyramid rows.  Several chunks load in turn (their
+    // registers would not also fit across the coarse part).
     const int32_t *fine = idx + blk * a.K1;
+    bf16x8 kr[KT][2], vr[KT][2];
+    auto load_chunk = [&](int c0) {
+        const int nt = min(KT, a.K1 - c0);
+        int fp[KT];
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            fp[t] = __builtin_amdgcn_readfirstlane(fine[c0 + min(t, nt - 1)]);
+            kr[t][0] = load_bf16x8(kh + trow(fp[t], lr) + lc);
+            kr[t][1] = load_bf16x8(kh + trow(fp[t], lr + 8) + lc);
+        }
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            vr[t][0] = load_bf16x8(vh + trow(fp[t], lr) + lc);
+            vr[t][1] = load_bf16x8(vh + trow(fp[t], lr + 8) + lc);
+        }
+    };
+    const bf16x8 qr0 = load_bf16x8_nt(q + head_off + trow(ib, lr) + lc);
+    const bf16x8 qr1 = load_bf16x8_nt(q + head_off + trow(ib, lr + 8) + lc);
+    const int ce = threadIdx.x >> 4, cpart = threadIdx.x & 15;   // coarse entry, quarter
+    int cj = 0, cpick = 0, cc = 0;
+    bool cok = false;
+    if constexpr (CO) {
+        cok = coarse_locate(a, ce, cj, cpick);
+        cj = cok ? cj : 0;
+        cpick = cok ? cpick : 0;
+        const int anc = ib0 >> (4 * (cj + 1));   // ancestor at level cj+2
+        cc = idx[a.cl_idx_off[cj] + ((int64_t)h * a.cl_n[cj] + anc) * a.cl_k[cj] + cpick];
+    }
+    if constexpr (NCH == 1) load_chunk(0);
+    f32x4 ckk = {0.f, 0.f, 0.f, 0.f}, cvv = ckk;
+    if constexpr (CO) {
+        const int64_t row = a.cl_pyr_off[cj] + ((int64_t)h * a.cl_n[cj] + cc) * kHeadDim + 4 * cpart;
+        ckk = *reinterpret_cast<const f32x4 *>(pk + row);
+        cvv = *reinterpret_cast<const f32x4 *>(pv + row);
+    }
+    stage_rows(qw, qr0, qr1);
     float m = -INFINITY, lsum = 0.f;
     f32x4 oacc[4];
 #pragma unroll
@@ -507,19 +554,10 @@ __global__ __launch_bounds__(256, NCH == 1 ? 3 : 2) void attn_fwd_chunk_kernel(
     const bf16x8 qa1 = load_bf16x8(qw + c16 * kVStride + 32 + 8 * g);
     if constexpr (CO) {
         // coarse tile, staged by the whole workgroup: thread (entry e, quarter p)
-        const int e = threadIdx.x >> 4, part = threadIdx.x & 15;
-        int j, pick;
-        const bool ok = coarse_locate(a, e, j, pick);
-        const int js = ok ? j : 0, ps = ok ? pick : 0;
-        const int anc = ib0 >> (4 * (js + 1));   // ancestor at level js+2
-        const int c = idx[a.cl_idx_off[js] + ((int64_t)h * a.cl_n[js] + anc) * a.cl_k[js] + ps];
-        const int64_t row = a.cl_pyr_off[js] + ((int64_t)h * a.cl_n[js] + c) * kHeadDim + 4 * part;
-        f32x4 kk = *reinterpret_cast<const f32x4 *>(pk + row);
-        f32x4 vv = *reinterpret_cast<const f32x4 *>(pv + row);
-        if (!ok) kk = vv = f32x4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<u32x2 *>(&ck[e * kVStride + 4 * part]) = __builtin_bit_cast(u32x2, to_bf16x4(kk));
-        *reinterpret_cast<u32x2 *>(&cv[e * kVStride + 4 * part]) = __builtin_bit_cast(u32x2, to_bf16x4(vv));
-        if (part == 0) cbias[e] = ok ? 4.0f * (float)(js + 2) : -INFINITY;
+        if (!cok) ckk = cvv = f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<u32x2 *>(&ck[ce * kVStride + 4 * cpart]) = __builtin_bit_cast(u32x2, to_bf16x4(ckk));
+        *reinterpret_cast<u32x2 *>(&cv[ce * kVStride + 4 * cpart]) = __builtin_bit_cast(u32x2, to_bf16x4(cvv));
+        if (cpart == 0) cbias[ce] = cok ? 4.0f * (float)(cj + 2) : -INFINITY;
         __syncthreads();
         const __bf16 *ckr = ck + c16 * kVStride;
         f32x4 sc = mfma_bf16_32(load_bf16x8(ckr + 32 + 8 * g), qa1,
@@ -557,16 +595,7 @@ __global__ __launch_bounds__(256, NCH == 1 ? 3 : 2) void attn_fwd_chunk_kernel(
 #pragma unroll 1
     for (int c0 = 0; c0 < NCH * KT; c0 += KT) {
         const int nt = min(KT, a.K1 - c0);   // live tiles of this chunk (>= 1)
-        bf16x8 kr[KT][2], vr[KT][2];
-#pragma unroll
-        for (int t = 0; t < KT; ++t) {
-            const int f = __builtin_amdgcn_readfirstlane(fine[c0 + min(t, nt - 1)]);
-            const int64_t o0 = trow(f, lr) + lc, o1 = trow(f, lr + 8) + lc;
-            kr[t][0] = load_bf16x8(kh + o0);
-            kr[t][1] = load_bf16x8(kh + o1);
-            vr[t][0] = load_bf16x8(vh + o0);
-            vr[t][1] = load_bf16x8(vh + o1);
-        }
+        if (NCH > 1 || c0 > 0) load_chunk(c0);
         f32x4 st[KT];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {

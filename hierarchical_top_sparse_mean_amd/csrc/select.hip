@@ -129,6 +129,13 @@ __global__ __launch_bounds__(COUNT ? 512 : 256) void select_kernel(const float *
     const float *kh = kl + (int64_t)h * n * kHeadDim;
     const int row = gi * kBlock + col;
     const bool row_ok = row < n;
+    const bool dense = parent == nullptr;
+    const int ntiles = dense ? (n + kBlock - 1) / kBlock : kp * sub;
+    const int32_t *prow = dense ? nullptr : parent + ((int64_t)h * (groups_per_head / sub) + gi / sub) * kp;
+    // the parent's picks, one per lane (kp <= 32), requested first: every
+    // candidate address needs them, and waiting for a load waits for every
+    // load issued before it
+    const int ppick = !dense && lane < kp ? prow[lane] : 0;
 
     float qf[16];
     {
@@ -142,10 +149,6 @@ __global__ __launch_bounds__(COUNT ? 512 : 256) void select_kernel(const float *
             qf[4 * j + 3] = t[3];
         }
     }
-
-    const bool dense = parent == nullptr;
-    const int ntiles = dense ? (n + kBlock - 1) / kBlock : kp * sub;
-    const int32_t *prow = dense ? nullptr : parent + ((int64_t)h * (groups_per_head / sub) + gi / sub) * kp;
 
     uint64_t best[KM];
 #pragma unroll
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(COUNT ? 512 : 256) void select_kernel(const float *
             for (int t = 0; t < LB; ++t) {
                 const int tile = min(t0 + hb + t, te - 1);
                 base[t] = dense ? tile * kBlock
-                                : (__builtin_amdgcn_readfirstlane(prow[tile / sub]) * sub + tile % sub) * kBlock;
+                                : (__builtin_amdgcn_readlane(ppick, tile / sub) * sub + tile % sub) * kBlock;
                 const int cand = base[t] + col;
                 const int64_t crow = (unsigned)cand < (unsigned)n ? cand : 0;   // out-of-range parent picks read row 0
                 const f32x4 *src = reinterpret_cast<const f32x4 *>(kh + crow * kHeadDim + 16 * g);

@@ -317,7 +317,8 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
     auto trow = [&](int b, int r) { return (int64_t)tok_tile_row<ORD>(a.tm, b, r) * kHeadDim; };
     const int lr = lane >> 3, lc = (lane & 7) * 8;
     // ---- coarse tile, staged by the whole workgroup: thread (entry e, quarter p);
-    // its pyramid rows are requested before the fine tiles, written to LDS after
+    // its pick and pyramid rows are requested here, written to LDS after the
+    // fine scores
     const int ce = threadIdx.x >> 4, cpart = threadIdx.x & 15;   // 16 entries x 16 x 4 columns
     int cj, cpick;
     const bool cok = coarse_locate(a, ce, cj, cpick);
@@ -350,14 +351,6 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
         store_bf16x8(dst + (lane >> 3) * kVStride + (lane & 7) * 8, r0);
         store_bf16x8(dst + ((lane >> 3) + 8) * kVStride + (lane & 7) * 8, r1);
     };
-    {
-        if (!cok) ckk = cvv = f32x4{0.f, 0.f, 0.f, 0.f};
-        const bf16x4 kb = to_bf16x4(f32x4{ckk[0], ckk[1], ckk[2], ckk[3]});
-        const bf16x4 vb = to_bf16x4(f32x4{cvv[0], cvv[1], cvv[2], cvv[3]});
-        *reinterpret_cast<u32x2 *>(&ck[ce * kVStride + 4 * cpart]) = __builtin_bit_cast(u32x2, kb);
-        *reinterpret_cast<u32x2 *>(&cv[ce * kVStride + 4 * cpart]) = __builtin_bit_cast(u32x2, vb);
-        if (cpart == 0) cbias[ce] = cok ? 4.0f * (float)(cjs + 2) : -INFINITY;
-    }
     // ---- fine scores: K tiles pass through the V staging slots, kHalf at a
     // time (V stays in registers until its half is staged)
     __bf16 *qw = qs_all[w];
@@ -386,6 +379,17 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
     stage_k_half(1);
     wave_lds_sync();
     score_half(1);
+    // the coarse tile goes to LDS only now: its pyramid rows were requested
+    // after the fine K rows (their address waits for the pick), and writing
+    // it earlier would hold the fine scores until every K row had arrived
+    {
+        if (!cok) ckk = cvv = f32x4{0.f, 0.f, 0.f, 0.f};
+        const bf16x4 kb = to_bf16x4(f32x4{ckk[0], ckk[1], ckk[2], ckk[3]});
+        const bf16x4 vb = to_bf16x4(f32x4{cvv[0], cvv[1], cvv[2], cvv[3]});
+        *reinterpret_cast<u32x2 *>(&ck[ce * kVStride + 4 * cpart]) = __builtin_bit_cast(u32x2, kb);
+        *reinterpret_cast<u32x2 *>(&cv[ce * kVStride + 4 * cpart]) = __builtin_bit_cast(u32x2, vb);
+        if (cpart == 0) cbias[ce] = cok ? 4.0f * (float)(cjs + 2) : -INFINITY;
+    }
     __syncthreads();   // coarse tile staged
     const __bf16 *ckr = ck + c16 * kVStride;
     f32x4 sc = mfma_bf16_32(load_bf16x8(ckr + 32 + 8 * g), qa1,

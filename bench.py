@@ -274,7 +274,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--overlap", action="store_true",
-                    help="run the index transposes on a second stream, concurrently with the forward")
+                    help="run the index transposes on a second stream beside the forward attention "
+                         "(measured slower: they wait for the forward's workgroups to drain)")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip the fused count-into-select comparison (for profiled runs)")
     ap.add_argument("--cpu-heads", type=int, default=16)

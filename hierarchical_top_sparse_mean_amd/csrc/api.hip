@@ -12,6 +12,7 @@ using llsa::Geometry;
 namespace {
 
 bool aligned16(const void *p) { return p != nullptr && (((uintptr_t)p) & 15u) == 0; }
+bool aligned4(const void *p);
 
 int64_t ipow(int64_t b, int e) {
     int64_t r = 1;
@@ -35,6 +36,7 @@ int make_geometry(const llsa_problem *p, Geometry *g, llsa_sizes *sz) {
         if (((int64_t)1 << (2 * log2S)) != p->seq_len) return LLSA_ERR_INVALID;
     }
     if (!(p->scale >= 0.0f) || isinf(p->scale)) return LLSA_ERR_INVALID;
+    if (p->index_status != nullptr && !aligned4(p->index_status)) return LLSA_ERR_INVALID;
     if (p->levels > LLSA_MAX_LEVELS) return LLSA_ERR_UNSUPPORTED;
     // divisibility by block^levels (checked in 64 bits before anything else)
     int64_t span = 1;
@@ -121,6 +123,31 @@ int make_geometry(const llsa_problem *p, Geometry *g, llsa_sizes *sz) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? LLSA_OK : LLSA_ERR_HIP; }
 
+bool aligned4(const void *p) { return p != nullptr && (((uintptr_t)p) & 3u) == 0; }
+
+// Debug index check (p->index_status set): waits for the status word on the
+// stream and maps it to a status.
+int debug_status(const llsa_problem *p, hipStream_t s) {
+    int32_t word = 0;
+    if (hipMemcpyAsync(&word, p->index_status, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return LLSA_ERR_HIP;
+    return word == 0 ? LLSA_OK : LLSA_ERR_INDEX;
+}
+
+// Before a call that reads lists: with the debug check on, check idx (and the
+// CSR when given) into the status word and return its verdict; LLSA_OK when
+// the check is off.
+int debug_check_inputs(const llsa_problem *p, const Geometry &g, const int32_t *idx,
+                       const int32_t *csr_ptr, const int32_t *csr_col, hipStream_t s) {
+    if (p->index_status == nullptr) return LLSA_OK;
+    uint32_t *w = (uint32_t *)p->index_status;
+    if (llsa::launch_status_clear(w, s) != hipSuccess ||
+        llsa::launch_check_indices(g, idx, csr_ptr, csr_col, w, s) != hipSuccess)
+        return LLSA_ERR_HIP;
+    return debug_status(p, s);
+}
+
 // Workspace of llsa_select_transpose: the level transposes run one after
 // another and share it; level 1 keeps the selection's counts when fused.
 size_t select_transpose_ws(const Geometry &g) {
@@ -162,7 +189,14 @@ int llsa_select(const llsa_problem *p, const float *pyr_q, const float *pyr_k, i
     const int st = make_geometry(p, &g, nullptr);
     if (st != LLSA_OK) return st;
     if (!aligned16(pyr_q) || !aligned16(pyr_k) || !aligned16(idx)) return LLSA_ERR_INVALID;
-    return status_of(llsa::launch_select(g, pyr_q, pyr_k, idx, nullptr, (hipStream_t)stream));
+    hipStream_t s = (hipStream_t)stream;
+    uint32_t *dbg = (uint32_t *)p->index_status;
+    if (dbg != nullptr && llsa::launch_status_clear(dbg, s) != hipSuccess) return LLSA_ERR_HIP;
+    const int st2 = status_of(llsa::launch_select(g, pyr_q, pyr_k, idx, nullptr, dbg, s));
+    if (st2 != LLSA_OK || dbg == nullptr) return st2;
+    // debug check: the lists just written, on top of any out-of-range parent pick
+    if (llsa::launch_check_indices(g, idx, nullptr, nullptr, dbg, s) != hipSuccess) return LLSA_ERR_HIP;
+    return debug_status(p, s);
 }
 
 size_t llsa_select_transpose_workspace(const llsa_problem *p) {
@@ -184,9 +218,11 @@ int llsa_select_transpose(const llsa_problem *p, const float *pyr_q, const float
     const size_t need = select_transpose_ws(g);
     if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return LLSA_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
+    uint32_t *dbg = (uint32_t *)p->index_status;
+    if (dbg != nullptr && llsa::launch_status_clear(dbg, s) != hipSuccess) return LLSA_ERR_HIP;
     const bool fused = llsa::select_count_fusable(g);
     hipError_t e = llsa::launch_select(g, pyr_q, pyr_k, idx,
-                                       fused ? llsa::transpose_counted_hist(workspace) : nullptr, s);
+                                       fused ? llsa::transpose_counted_hist(workspace) : nullptr, dbg, s);
     for (int l = 1; l <= g.Le + 1 && e == hipSuccess; ++l) {
         const int32_t *il = idx + g.idx_off[l];
         int32_t *pl = csr_ptr + g.ptr_off[l], *cl = csr_col + g.col_off[l];
@@ -194,7 +230,9 @@ int llsa_select_transpose(const llsa_problem *p, const float *pyr_q, const float
                 ? llsa::launch_transpose_counted(g.bh, g.n[1], g.kl[1], g.n[1], il, pl, cl, workspace, s)
                 : llsa::launch_transpose(g.bh, g.n[l], g.kl[l], g.n[l], il, pl, cl, workspace, s);
     }
-    return status_of(e);
+    if (e != hipSuccess || dbg == nullptr) return status_of(e);
+    if (llsa::launch_check_indices(g, idx, csr_ptr, csr_col, dbg, s) != hipSuccess) return LLSA_ERR_HIP;
+    return debug_status(p, s);
 }
 
 size_t llsa_index_transpose_levels_workspace(const llsa_problem *p) {
@@ -219,6 +257,8 @@ int llsa_index_transpose_levels(const llsa_problem *p, const int32_t *idx, int32
     const size_t need = llsa_index_transpose_levels_workspace(p);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
         return LLSA_ERR_WORKSPACE;
+    const int dst = debug_check_inputs(p, g, idx, nullptr, nullptr, (hipStream_t)stream);
+    if (dst != LLSA_OK) return dst;
     int rows[llsa::kMaxLevels + 1], ks[llsa::kMaxLevels + 1];
     const int32_t *il[llsa::kMaxLevels + 1];
     int32_t *pl[llsa::kMaxLevels + 1], *cl[llsa::kMaxLevels + 1];
@@ -244,6 +284,8 @@ int llsa_attn_fwd(const llsa_problem *p, const void *q, const void *k, const voi
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(pyr_k) || !aligned16(pyr_v) ||
         !aligned16(idx) || !aligned16(o) || !aligned16(lse))
         return LLSA_ERR_INVALID;
+    const int dst = debug_check_inputs(p, g, idx, nullptr, nullptr, (hipStream_t)stream);
+    if (dst != LLSA_OK) return dst;
     return status_of(llsa::launch_attn_fwd(g, q, k, v, pyr_k, pyr_v, idx, o, lse, (hipStream_t)stream));
 }
 
@@ -299,6 +341,8 @@ int llsa_attn_bwd(const llsa_problem *p, const void *q, const void *k, const voi
         return LLSA_ERR_INVALID;
     const size_t need = llsa::bwd_workspace_bytes(g);
     if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return LLSA_ERR_WORKSPACE;
+    const int dst = debug_check_inputs(p, g, idx, csr_ptr, csr_col, (hipStream_t)stream);
+    if (dst != LLSA_OK) return dst;
     return status_of(llsa::launch_attn_bwd(g, q, k, v, pyr_k, pyr_v, idx, csr_ptr, csr_col, o, lse,
                                            dout, dq, dk, dv, workspace, (hipStream_t)stream));
 }
@@ -341,6 +385,31 @@ size_t llsa_dense_attn_bwd_workspace(const llsa_problem *p) {
     return sizeof(float) * (size_t)p->batch * p->heads * p->seq_len;
 }
 
+int llsa_check_indices(const llsa_problem *p, const int32_t *idx, const int32_t *csr_ptr,
+                       const int32_t *csr_col, int32_t *status, void *stream) {
+    Geometry g;
+    const int st = make_geometry(p, &g, nullptr);
+    if (st != LLSA_OK) return st;
+    if (!aligned16(idx) || !aligned4(status)) return LLSA_ERR_INVALID;
+    const bool csr = csr_ptr != nullptr && csr_col != nullptr;
+    if (csr && (!aligned16(csr_ptr) || !aligned16(csr_col))) return LLSA_ERR_INVALID;
+    hipStream_t s = (hipStream_t)stream;
+    if (llsa::launch_status_clear((uint32_t *)status, s) != hipSuccess) return LLSA_ERR_HIP;
+    return status_of(llsa::launch_check_indices(g, idx, csr ? csr_ptr : nullptr, csr ? csr_col : nullptr,
+                                                (uint32_t *)status, s));
+}
+
+int llsa_check_indices_host(const llsa_problem *p, const int32_t *idx, const int32_t *csr_ptr,
+                            const int32_t *csr_col, int32_t *flags) {
+    Geometry g;
+    const int st = make_geometry(p, &g, nullptr);
+    if (st != LLSA_OK) return st;
+    if (idx == nullptr || flags == nullptr) return LLSA_ERR_INVALID;
+    const bool csr = csr_ptr != nullptr && csr_col != nullptr;
+    *flags = (int32_t)llsa::check_indices_host(g, idx, csr ? csr_ptr : nullptr, csr ? csr_col : nullptr);
+    return LLSA_OK;
+}
+
 const char *llsa_strerror(int status) {
     switch (status) {
     case LLSA_OK: return "ok";
@@ -348,6 +417,7 @@ const char *llsa_strerror(int status) {
     case LLSA_ERR_UNSUPPORTED: return "unsupported problem";
     case LLSA_ERR_WORKSPACE: return "workspace missing or too small";
     case LLSA_ERR_HIP: return "kernel launch failed";
+    case LLSA_ERR_INDEX: return "invalid index list or CSR (debug index check)";
     default: return "unknown status";
     }
 }

@@ -35,8 +35,10 @@ hipError_t launch_pool(const Geometry &g, const void *q, const void *k, const vo
                        float *pq, float *pk, float *pv, hipStream_t s);
 // count_hist: when not null (and select_count_fusable), level 1 also counts
 // its picks per key into it, one range per 128 rows (the first transpose step).
+// status: when not null (debug index check), a parent pick outside its level
+// sets LLSA_IDX_RANGE in it.
 hipError_t launch_select(const Geometry &g, const float *pq, const float *pk, int32_t *idx,
-                         int32_t *count_hist, hipStream_t s);
+                         int32_t *count_hist, uint32_t *status, hipStream_t s);
 bool select_count_fusable(const Geometry &g);
 constexpr int kSelectRowsPerRange = 128;
 hipError_t launch_attn_fwd(const Geometry &g, const void *q, const void *k, const void *v,
@@ -61,6 +63,13 @@ hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, cons
                            const int32_t *csr_ptr, const int32_t *csr_col, const void *o,
                            const float *lse, const void *dout, void *dq, void *dk, void *dv,
                            void *ws, hipStream_t s);
+// Debug index check: clear the status word; OR the flags of every failing pick
+// row (all levels) and CSR key (levels 1..Le+1, when csr_ptr is not null) into it.
+hipError_t launch_status_clear(uint32_t *status, hipStream_t s);
+hipError_t launch_check_indices(const Geometry &g, const int32_t *idx, const int32_t *csr_ptr,
+                                const int32_t *csr_col, uint32_t *status, hipStream_t s);
+uint32_t check_indices_host(const Geometry &g, const int32_t *idx, const int32_t *csr_ptr,
+                            const int32_t *csr_col);
 hipError_t launch_dense_fwd(int bh, int N, float scale, const void *q, const void *k,
                             const void *v, void *o, float *lse, hipStream_t s);
 hipError_t launch_dense_bwd(int bh, int N, float scale, const void *q, const void *k,

@@ -16,6 +16,7 @@
 // their lists through two butterfly exchanges.
 #include "common.hpp"
 #include "internal.hpp"
+#include "llsa.h"
 
 namespace llsa {
 
@@ -106,7 +107,8 @@ __global__ __launch_bounds__(COUNT ? 512 : 256) void select_kernel(const float *
                                                      int32_t *__restrict__ out, int n, int kout,
                                                      int kp, int groups_per_head,
                                                      int64_t groups_total, int sub,
-                                                     int32_t *__restrict__ hist) {
+                                                     int32_t *__restrict__ hist,
+                                                     uint32_t *__restrict__ status) {
     static_assert(SPLIT == 1 || SPLIT == 4, "a row group takes one wave or the whole workgroup");
     static_assert(!COUNT || SPLIT == 1, "the fused count takes four row groups per workgroup");
     __shared__ uint64_t part_best[SPLIT == 1 ? 1 : SPLIT][kBlock][KM];
@@ -171,7 +173,11 @@ __global__ __launch_bounds__(COUNT ? 512 : 256) void select_kernel(const float *
                 base[t] = dense ? tile * kBlock
                                 : (__builtin_amdgcn_readlane(ppick, tile / sub) * sub + tile % sub) * kBlock;
                 const int cand = base[t] + col;
-                const int64_t crow = (unsigned)cand < (unsigned)n ? cand : 0;   // out-of-range parent picks read row 0
+                // a parent pick outside its level (never one the selection wrote) reads row 0,
+                // and the debug index check reports it
+                const bool in_level = (unsigned)cand < (unsigned)n;
+                const int64_t crow = in_level ? cand : 0;
+                if (!dense && !in_level && status != nullptr) atomicOr(status, (uint32_t)LLSA_IDX_RANGE);
                 const f32x4 *src = reinterpret_cast<const f32x4 *>(kh + crow * kHeadDim + 16 * g);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -256,7 +262,7 @@ __global__ __launch_bounds__(COUNT ? 512 : 256) void select_kernel(const float *
 
 template <int KM>
 static void launch_level(const Geometry &g, int l, const float *pq, const float *pk, int32_t *idx,
-                         int32_t *hist, hipStream_t s) {
+                         int32_t *hist, uint32_t *status, hipStream_t s) {
     const bool dense = (l == g.L);
     const int n = g.n[l];
     const int gph = dense ? (n + kBlock - 1) / kBlock : n / kBlock;
@@ -269,15 +275,15 @@ static void launch_level(const Geometry &g, int l, const float *pq, const float 
     if (hist != nullptr)   // fused count (select_count_fusable holds)
         hipLaunchKernelGGL((select_kernel<KM, 1, true>), dim3((unsigned)(total / 8)), dim3(512), 0,
                            s, pq + g.pyr_off[l], pk + g.pyr_off[l], parent, idx + g.idx_off[l], n,
-                           g.kl[l], kp, gph, total, g.sub, hist);
+                           g.kl[l], kp, gph, total, g.sub, hist, status);
     else if (total < 1024 && ntiles >= 4 * 2)
         hipLaunchKernelGGL((select_kernel<KM, 4, false>), dim3((unsigned)total), dim3(256), 0, s,
                            pq + g.pyr_off[l], pk + g.pyr_off[l], parent, idx + g.idx_off[l], n,
-                           g.kl[l], kp, gph, total, g.sub, nullptr);
+                           g.kl[l], kp, gph, total, g.sub, nullptr, status);
     else
         hipLaunchKernelGGL((select_kernel<KM, 1, false>), dim3((unsigned)((total + 3) / 4)), dim3(256),
                            0, s, pq + g.pyr_off[l], pk + g.pyr_off[l], parent, idx + g.idx_off[l], n,
-                           g.kl[l], kp, gph, total, g.sub, nullptr);
+                           g.kl[l], kp, gph, total, g.sub, nullptr, status);
 }
 
 // The level-1 selection can also count its picks for the transpose when the
@@ -294,15 +300,15 @@ bool select_count_fusable(const Geometry &g) {
 }
 
 hipError_t launch_select(const Geometry &g, const float *pq, const float *pk, int32_t *idx,
-                         int32_t *count_hist, hipStream_t s) {
+                         int32_t *count_hist, uint32_t *status, hipStream_t s) {
     for (int l = g.L; l >= 1; --l) {
         int32_t *hist = l == 1 ? count_hist : nullptr;
         if (g.K <= 8)
-            launch_level<8>(g, l, pq, pk, idx, hist, s);
+            launch_level<8>(g, l, pq, pk, idx, hist, status, s);
         else if (g.K <= 16)
-            launch_level<16>(g, l, pq, pk, idx, hist, s);
+            launch_level<16>(g, l, pq, pk, idx, hist, status, s);
         else
-            launch_level<32>(g, l, pq, pk, idx, hist, s);
+            launch_level<32>(g, l, pq, pk, idx, hist, status, s);
     }
     return hipGetLastError();
 }

@@ -15,7 +15,8 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllsa.so")
 MAX_LEVELS = 6
 
-LLSA_OK, LLSA_ERR_INVALID, LLSA_ERR_UNSUPPORTED, LLSA_ERR_WORKSPACE, LLSA_ERR_HIP = range(5)
+LLSA_OK, LLSA_ERR_INVALID, LLSA_ERR_UNSUPPORTED, LLSA_ERR_WORKSPACE, LLSA_ERR_HIP, LLSA_ERR_INDEX = range(6)
+LLSA_IDX_RANGE, LLSA_IDX_ORDER, LLSA_IDX_PARENT, LLSA_IDX_CSR_PTR, LLSA_IDX_CSR_COL = 1, 2, 4, 8, 16
 LLSA_F32, LLSA_BF16 = 0, 1
 
 _c_i32, _c_i64, _c_sz, _c_f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
@@ -25,7 +26,7 @@ class Problem(ctypes.Structure):
     _fields_ = [("batch", _c_i32), ("heads", _c_i32), ("seq_len", _c_i32), ("head_dim", _c_i32),
                 ("block", _c_i32), ("levels", _c_i32), ("topk", _c_i32), ("enrich", _c_i32),
                 ("dtype", _c_i32), ("grad_dtype", _c_i32), ("scale", _c_f32),
-                ("drop_covered", _c_i32), ("token_order", _c_i32)]
+                ("drop_covered", _c_i32), ("token_order", _c_i32), ("index_status", _vp)]
 
 
 class Sizes(ctypes.Structure):
@@ -74,12 +75,14 @@ def _load():
     L.llsa_dense_attn_bwd_workspace.restype = _c_sz
     L.llsa_dense_attn_bwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz,
                                       _vp]
+    L.llsa_check_indices.argtypes = [P, _vp, _vp, _vp, _vp, _vp]
+    L.llsa_check_indices_host.argtypes = [P, _vp, _vp, _vp, ctypes.POINTER(_c_i32)]
     L.llsa_strerror.argtypes = [ctypes.c_int]
     L.llsa_strerror.restype = ctypes.c_char_p
     for name in ("llsa_sizes_query", "llsa_pool", "llsa_select", "llsa_attn_fwd",
                  "llsa_index_transpose", "llsa_attn_bwd", "llsa_dense_attn_fwd",
                  "llsa_dense_attn_bwd", "llsa_index_transpose_mask", "llsa_select_transpose",
-                 "llsa_index_transpose_levels"):
+                 "llsa_index_transpose_levels", "llsa_check_indices", "llsa_check_indices_host"):
         getattr(L, name).restype = ctypes.c_int
     return L
 
@@ -89,11 +92,13 @@ lib = _load()
 
 def problem(batch, heads, seq_len, head_dim=64, block=16, levels=2, topk=8, enrich=-1,
             dtype=torch.bfloat16, grad_dtype=torch.float32, scale=0.0, drop_covered=True,
-            token_order=0) -> Problem:
+            token_order=0, index_status=None) -> Problem:
+    """index_status: a one-element int32 CUDA tensor (or a device address) to
+    turn the debug index check on; None leaves it off."""
     code = {torch.float32: LLSA_F32, torch.bfloat16: LLSA_BF16}
     return Problem(batch, heads, seq_len, head_dim, block, levels, topk, enrich,
                    code.get(dtype, -1), code.get(grad_dtype, -1), float(scale), int(drop_covered),
-                   int(token_order))
+                   int(token_order), _ptr(index_status))
 
 
 def _ptr(t):
@@ -208,6 +213,27 @@ def llsa_dense_attn_bwd(p, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspa
            lib.llsa_dense_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                    _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                    workspace_bytes, _stream(stream)))
+
+
+def llsa_check_indices(p, idx, csr_ptr, csr_col, status, stream=None):
+    _check("llsa_check_indices",
+           lib.llsa_check_indices(ctypes.byref(p), _ptr(idx), _ptr(csr_ptr), _ptr(csr_col), _ptr(status),
+                                  _stream(stream)))
+
+
+def llsa_check_indices_host(p, idx, csr_ptr=None, csr_col=None) -> int:
+    """The debug index check on host (CPU) int32 tensors laid out as on the
+    device; returns the OR of LLSA_IDX_* flags (0: valid)."""
+    def host(t):
+        if t is None:
+            return None
+        assert t.device.type == "cpu" and t.dtype == torch.int32 and t.is_contiguous()
+        return t.data_ptr()
+    flags = _c_i32(0)
+    _check("llsa_check_indices_host",
+           lib.llsa_check_indices_host(ctypes.byref(p), host(idx), host(csr_ptr), host(csr_col),
+                                       ctypes.byref(flags)))
+    return int(flags.value)
 
 
 # --------------------------------------------------------------- buffers --

@@ -12,7 +12,8 @@
  * ---------------------------------------
  *  - Tensor pointers are DEVICE pointers owned by the caller, contiguous and
  *    row-major, at least 16-byte aligned.  The library never allocates or
- *    frees device memory and never synchronises: each call enqueues its
+ *    frees device memory and, outside the debug index check (see
+ *    llsa_problem.index_status), never synchronises: each call enqueues its
  *    kernels on `stream` (a hipStream_t passed as void*, NULL = default
  *    stream) and returns.  It keeps no global state and is thread-safe.
  *  - Q, K, V, O, dO are [batch, heads, seq_len, head_dim] in `dtype`.
@@ -28,6 +29,12 @@
  *  - All shape, pointer and alignment checks run on the host before any HIP
  *    call; on an error status nothing is launched and no output is touched.
  *    Launch failures are reported as LLSA_ERR_HIP.
+ *  - Index lists and CSR are trusted: outside the debug index check
+ *    (llsa_problem.index_status) their values are not checked, and values
+ *    other than the library's own make the kernels read out of bounds.  With
+ *    the check on, a call that reads lists checks them on the device first and
+ *    returns LLSA_ERR_INDEX, with nothing else launched, when they are
+ *    invalid.
  *  - Supported set: head_dim = 64, block = 16 or 64, 1 <= levels <= 6,
  *    1 <= topk <= 32, seq_len <= 2^25, batch * heads * seq_len < 2^31, dtype
  *    LLSA_F32 or LLSA_BF16, non-causal.  Other values give
@@ -50,7 +57,18 @@ enum llsa_status {
     LLSA_ERR_INVALID = 1,      /* bad shape, null or misaligned pointer, inconsistent sizes */
     LLSA_ERR_UNSUPPORTED = 2,  /* valid but outside the supported set above               */
     LLSA_ERR_WORKSPACE = 3,    /* workspace pointer null or smaller than required          */
-    LLSA_ERR_HIP = 4           /* a kernel launch failed                                   */
+    LLSA_ERR_HIP = 4,          /* a kernel launch failed                                   */
+    LLSA_ERR_INDEX = 5         /* debug index check only: an index list or CSR is invalid   */
+};
+
+/* Flags of the debug index check's status word (OR-ed). */
+enum llsa_index_flag {
+    LLSA_IDX_RANGE = 1,    /* a pick outside [0, n_l)                                      */
+    LLSA_IDX_ORDER = 2,    /* a pick row not strictly ascending                            */
+    LLSA_IDX_PARENT = 4,   /* a pick at level l < L that is no child of its parent's picks */
+    LLSA_IDX_CSR_PTR = 8,  /* ptr[0] != 0, ptr[n_l] != n_l * K_l, or ptr decreasing        */
+    LLSA_IDX_CSR_COL = 16  /* a CSR row outside [0, n_l), not ascending in its key's
+                              segment, or not having picked that key                       */
 };
 
 enum llsa_dtype { LLSA_F32 = 0, LLSA_BF16 = 1 };
@@ -73,6 +91,17 @@ typedef struct llsa_problem {
                              level-l token pools a 4^l x 4^l patch.  Q, K, V, O, dO, dQ,
                              dK, dV and lse stay in raster order; pyramids, index lists
                              and CSR are in patch-sequence order                          */
+    int32_t *index_status; /* debug index check; NULL (the default) turns it off.  Else a
+                             DEVICE pointer to one int32 status word.  llsa_attn_fwd,
+                             llsa_index_transpose_levels and llsa_attn_bwd then check the
+                             lists they read (as llsa_check_indices), wait for the check on
+                             their stream and return LLSA_ERR_INDEX, launching nothing
+                             else, when it fails; llsa_select and llsa_select_transpose
+                             check the lists they wrote (after writing them) and also
+                             report a parent pick outside its level, which the selection
+                             otherwise reads as key 0.  The word is cleared by each such
+                             call and holds the LLSA_IDX_* flags of what failed.  These
+                             calls synchronise their stream, so the check is for debugging */
 } llsa_problem;
 
 typedef struct llsa_sizes {
@@ -131,9 +160,9 @@ int llsa_select(const llsa_problem *p, const float *pyr_q, const float *pyr_k,
  * kernels read only the index lists, never a dense mask.
  * In : q, k, v (dtype), pyr_k, pyr_v (float32), idx.
  *      idx must be as llsa_select writes it: every row of level l holds K_l
- *      distinct values in [0, n_l), ascending.  The values are not checked
- *      on the host or the device; others make the kernels read out of
- *      bounds.
+ *      distinct values in [0, n_l), ascending.  The values are checked only
+ *      in the debug index check (llsa_problem.index_status); otherwise others
+ *      make the kernels read out of bounds.
  * Out: o [batch, heads, seq_len, head_dim] (dtype), lse [batch*heads*seq_len]
  *      float32 natural-log normaliser of every query row.
  */
@@ -205,9 +234,9 @@ int llsa_select_transpose(const llsa_problem *p, const float *pyr_q, const float
 /*
  * Baseline for comparison with llsa_index_transpose: the same output built
  * from a dense bit mask of n_rows x n_cols per matrix (set every pick's bit,
- * then read every key's column), the mask-based route whose cost grows
- * with n_rows * n_cols (explainer "Step 4": mask-based methods bring back
- * quadratic overhead).  Same arguments and output; rows ascend within a key.
+ * then read every key's column): the mask-based route of explainer "Step 4",
+ * whose time and memory grow with n_rows * n_cols, the square of the
+ * sequence length.  Same arguments and output; rows ascend within a key.
  * workspace: at least llsa_index_transpose_mask_workspace(n_batch, n_rows,
  *      n_cols) bytes (the mask and per-key counts).
  */
@@ -227,7 +256,7 @@ int llsa_index_transpose_mask(int32_t n_batch, int32_t n_rows, int32_t k, int32_
  *      csr_ptr / csr_col for levels 1..Le+1 at sizes.csr_*_offset[l], each
  *      produced by llsa_index_transpose(batch*heads, n_l, K_l, n_l, ...) (or
  *      llsa_index_transpose_levels) from that same idx; like idx, the lists
- *      are not checked.
+ *      are checked only in the debug index check.
  * Out: dq, dk, dv [batch, heads, seq_len, head_dim] in grad_dtype.
  * workspace: at least sizes.bwd_workspace_bytes of device memory.
  */
@@ -263,6 +292,30 @@ size_t llsa_dense_attn_bwd_workspace(const llsa_problem *p);
 int llsa_dense_attn_bwd(const llsa_problem *p, const void *q, const void *k, const void *v,
                         const void *o, const float *lse, const void *dout, float *dq, float *dk,
                         float *dv, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The debug index check on its own (the pick lists of every level, and the CSR
+ * of levels 1..Le+1 unless csr_ptr or csr_col is NULL).  Every pick row must
+ * hold K_l distinct values in [0, n_l), ascending, each (below level L) a child
+ * of one of its parent's picks; every CSR level must be exactly the transpose
+ * of its pick list (ptr bounds and monotonicity, each listed row in range,
+ * ascending within the key, and having picked the key).  The sparse lists drive
+ * every gather of the forward and backward passes (abstract: the operator uses
+ * only sparse indices in both passes), so a caller that builds or edits lists
+ * itself can check them before use.
+ * In : idx (sizes.index_elems int32), csr_ptr / csr_col (layout of sizes), all
+ *      DEVICE pointers; reads stay inside these buffers whatever their values.
+ * Out: *status (DEVICE int32): cleared, then the OR of LLSA_IDX_* flags of
+ *      what failed (0: valid).  Asynchronous on `stream`; p->index_status is
+ *      ignored.
+ */
+int llsa_check_indices(const llsa_problem *p, const int32_t *idx, const int32_t *csr_ptr,
+                       const int32_t *csr_col, int32_t *status, void *stream);
+
+/* The same check on HOST copies of the lists (no HIP call): *flags receives
+ * the OR of LLSA_IDX_* flags (0: valid). */
+int llsa_check_indices_host(const llsa_problem *p, const int32_t *idx, const int32_t *csr_ptr,
+                            const int32_t *csr_col, int32_t *flags);
 
 /* Human-readable name of a status code (static string). */
 const char *llsa_strerror(int status);

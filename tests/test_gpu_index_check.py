@@ -58,7 +58,8 @@ def test_device_check_flags_equal_host_flags(what):
 def test_debug_mode_full_path_matches_normal_path(b, h, N, L_, K, Le, block):
     # on valid lists the debug mode returns ok everywhere and writes the same bytes
     _log(f"[index check] debug path {b} {h} {N} L{L_} K{K} Le{Le} B{block}")
-    c = Case(b, h, N, torch.bfloat16, L_, K, Le, backward=True, sinus=True, block=block)
+    c = Case(b, h, N, torch.bfloat16, L_, K, Le, backward=True, sinus=round(N ** 0.5) ** 2 == N,
+             block=block)
     q, k, v, do = c.q.cuda(), c.k.cuda(), c.v.cuda(), c.dout.cuda()
     out = []
     for debug in (False, True):
@@ -78,7 +79,10 @@ def test_debug_mode_full_path_matches_normal_path(b, h, N, L_, K, Le, block):
             L.llsa_select_transpose(p, B.pyr_q, B.pyr_k, B.idx, B.csr_ptr, B.csr_col, B.tws, B.tws_bytes)
             torch.cuda.synchronize()
             assert status.item() == 0
-        out.append([t.clone() for t in (B.idx, B.csr_ptr, B.csr_col, B.o, B.lse, B.dq, B.dk, B.dv)])
+        # the lists level by level (the padding between level segments is never written)
+        lists = [B.index_level(l) for l in range(1, L_ + 1)]
+        lists += [t for l in range(1, Le + 2) for t in B.csr_level(l)]
+        out.append([t.clone() for t in lists + [B.o, B.lse, B.dq, B.dk, B.dv]])
     for a, b_ in zip(*out):
         assert torch.equal(a, b_)
 

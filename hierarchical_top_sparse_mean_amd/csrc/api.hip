@@ -1,13 +1,21 @@
 // C ABI of the LLSA library: host-side validation, derived sizes and kernel
 // launches.  Every check runs before any HIP call; nothing allocates device
-// memory or synchronises.
+// memory or synchronises (outside the debug index check).
 #include <math.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "llsa.h"
 #include "internal.hpp"
 
 using llsa::Geometry;
+
+// Scratch of llsa_attn_bwd_noalloc: the backward workspace for callers that
+// cannot allocate.  Each GPU the library runs on holds its own copy until the
+// process ends; in host code its device address comes from
+// hipGetSymbolAddress (scratch_address below), never from the name.
+static __device__ __align__(256) unsigned char scratch[LLSA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -122,6 +130,28 @@ int make_geometry(const llsa_problem *p, Geometry *g, llsa_sizes *sz) {
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? LLSA_OK : LLSA_ERR_HIP; }
+
+// Device address of the current device's scratch array, looked up once per
+// device (the first llsa_attn_bwd_noalloc call with that device current).
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_ptr[kMaxDevices];
+
+hipError_t scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+        scratch_ptr[dev] = ptr;
+    }
+    *out = scratch_ptr[dev];
+    return hipSuccess;
+}
 
 bool aligned4(const void *p) { return p != nullptr && (((uintptr_t)p) & 3u) == 0; }
 
@@ -324,27 +354,57 @@ int llsa_index_transpose_mask(int32_t n_batch, int32_t n_rows, int32_t k, int32_
                                                  workspace, (hipStream_t)stream));
 }
 
+// Checks of llsa_attn_bwd and llsa_attn_bwd_noalloc that precede the
+// workspace: shapes, the coarse-entry limit and pointer alignment.
+int bwd_args_status(const llsa_problem *p, Geometry *g, const void *q, const void *k, const void *v,
+                    const float *pyr_k, const float *pyr_v, const int32_t *idx,
+                    const int32_t *csr_ptr, const int32_t *csr_col, const void *o, const float *lse,
+                    const void *dout, void *dq, void *dk, void *dv) {
+    const int st = make_geometry(p, g, nullptr);
+    if (st != LLSA_OK) return st;
+    int ncoarse = 0;
+    for (int l = 2; l <= g->Le + 1; ++l) ncoarse += g->kl[l];
+    if (ncoarse > 32) return LLSA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(pyr_k) || !aligned16(pyr_v) ||
+        !aligned16(idx) || !aligned16(csr_ptr) || !aligned16(csr_col) || !aligned16(o) ||
+        !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return LLSA_ERR_INVALID;
+    return LLSA_OK;
+}
+
 int llsa_attn_bwd(const llsa_problem *p, const void *q, const void *k, const void *v,
                   const float *pyr_k, const float *pyr_v, const int32_t *idx,
                   const int32_t *csr_ptr, const int32_t *csr_col, const void *o, const float *lse,
                   const void *dout, void *dq, void *dk, void *dv, void *workspace,
                   size_t workspace_bytes, void *stream) {
     Geometry g;
-    const int st = make_geometry(p, &g, nullptr);
+    const int st = bwd_args_status(p, &g, q, k, v, pyr_k, pyr_v, idx, csr_ptr, csr_col, o, lse, dout,
+                                   dq, dk, dv);
     if (st != LLSA_OK) return st;
-    int ncoarse = 0;
-    for (int l = 2; l <= g.Le + 1; ++l) ncoarse += g.kl[l];
-    if (ncoarse > 32) return LLSA_ERR_UNSUPPORTED;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(pyr_k) || !aligned16(pyr_v) ||
-        !aligned16(idx) || !aligned16(csr_ptr) || !aligned16(csr_col) || !aligned16(o) ||
-        !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
-        return LLSA_ERR_INVALID;
     const size_t need = llsa::bwd_workspace_bytes(g);
     if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return LLSA_ERR_WORKSPACE;
     const int dst = debug_check_inputs(p, g, idx, csr_ptr, csr_col, (hipStream_t)stream);
     if (dst != LLSA_OK) return dst;
     return status_of(llsa::launch_attn_bwd(g, q, k, v, pyr_k, pyr_v, idx, csr_ptr, csr_col, o, lse,
                                            dout, dq, dk, dv, workspace, (hipStream_t)stream));
+}
+
+int llsa_attn_bwd_noalloc(const llsa_problem *p, const void *q, const void *k, const void *v,
+                          const float *pyr_k, const float *pyr_v, const int32_t *idx,
+                          const int32_t *csr_ptr, const int32_t *csr_col, const void *o,
+                          const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                          void *stream) {
+    Geometry g;
+    const int st = bwd_args_status(p, &g, q, k, v, pyr_k, pyr_v, idx, csr_ptr, csr_col, o, lse, dout,
+                                   dq, dk, dv);
+    if (st != LLSA_OK) return st;
+    if (llsa::bwd_workspace_bytes(g) > (size_t)LLSA_NOALLOC_SCRATCH_BYTES) return LLSA_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess) return LLSA_ERR_HIP;
+    const int dst = debug_check_inputs(p, g, idx, csr_ptr, csr_col, (hipStream_t)stream);
+    if (dst != LLSA_OK) return dst;
+    return status_of(llsa::launch_attn_bwd(g, q, k, v, pyr_k, pyr_v, idx, csr_ptr, csr_col, o, lse,
+                                           dout, dq, dk, dv, ws, (hipStream_t)stream));
 }
 
 int llsa_dense_attn_fwd(const llsa_problem *p, const void *q, const void *k, const void *v,
@@ -418,6 +478,7 @@ const char *llsa_strerror(int status) {
     case LLSA_ERR_WORKSPACE: return "workspace missing or too small";
     case LLSA_ERR_HIP: return "kernel launch failed";
     case LLSA_ERR_INDEX: return "invalid index list or CSR (debug index check)";
+    case LLSA_ERR_SCRATCH: return "problem needs more than the allocation-free call's static scratch";
     default: return "unknown status";
     }
 }

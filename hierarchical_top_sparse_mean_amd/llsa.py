@@ -15,7 +15,9 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllsa.so")
 MAX_LEVELS = 6
 
-LLSA_OK, LLSA_ERR_INVALID, LLSA_ERR_UNSUPPORTED, LLSA_ERR_WORKSPACE, LLSA_ERR_HIP, LLSA_ERR_INDEX = range(6)
+(LLSA_OK, LLSA_ERR_INVALID, LLSA_ERR_UNSUPPORTED, LLSA_ERR_WORKSPACE, LLSA_ERR_HIP, LLSA_ERR_INDEX,
+ LLSA_ERR_SCRATCH) = range(7)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 LLSA_IDX_RANGE, LLSA_IDX_ORDER, LLSA_IDX_PARENT, LLSA_IDX_CSR_PTR, LLSA_IDX_CSR_COL = 1, 2, 4, 8, 16
 LLSA_F32, LLSA_BF16 = 0, 1
 
@@ -70,6 +72,8 @@ def _load():
                                             _vp]
     L.llsa_attn_bwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, _c_sz, _vp]
+    L.llsa_attn_bwd_noalloc.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _vp, _vp, _vp, _vp]
     L.llsa_dense_attn_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp]
     L.llsa_dense_attn_bwd_workspace.argtypes = [P]
     L.llsa_dense_attn_bwd_workspace.restype = _c_sz
@@ -82,7 +86,8 @@ def _load():
     for name in ("llsa_sizes_query", "llsa_pool", "llsa_select", "llsa_attn_fwd",
                  "llsa_index_transpose", "llsa_attn_bwd", "llsa_dense_attn_fwd",
                  "llsa_dense_attn_bwd", "llsa_index_transpose_mask", "llsa_select_transpose",
-                 "llsa_index_transpose_levels", "llsa_check_indices", "llsa_check_indices_host"):
+                 "llsa_index_transpose_levels", "llsa_check_indices", "llsa_check_indices_host",
+                 "llsa_attn_bwd_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     return L
 
@@ -196,6 +201,15 @@ def llsa_attn_bwd(p, q, k, v, pyr_k, pyr_v, idx, csr_ptr, csr_col, o, lse, dout,
                              _ptr(idx), _ptr(csr_ptr), _ptr(csr_col), _ptr(o), _ptr(lse),
                              _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                              workspace_bytes, _stream(stream)))
+
+
+def llsa_attn_bwd_noalloc(p, q, k, v, pyr_k, pyr_v, idx, csr_ptr, csr_col, o, lse, dout, dq, dk, dv,
+                          stream=None):
+    _check("llsa_attn_bwd_noalloc",
+           lib.llsa_attn_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(pyr_k),
+                                     _ptr(pyr_v), _ptr(idx), _ptr(csr_ptr), _ptr(csr_col), _ptr(o),
+                                     _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                     _stream(stream)))
 
 
 def llsa_dense_attn_fwd(p, q, k, v, o, lse, stream=None):

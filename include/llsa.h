@@ -15,7 +15,8 @@
  *    frees device memory and, outside the debug index check (see
  *    llsa_problem.index_status), never synchronises: each call enqueues its
  *    kernels on `stream` (a hipStream_t passed as void*, NULL = default
- *    stream) and returns.  It keeps no global state and is thread-safe.
+ *    stream) and returns.  It keeps no global state (except the static scratch
+ *    of llsa_attn_bwd_noalloc) and is thread-safe.
  *  - Q, K, V, O, dO are [batch, heads, seq_len, head_dim] in `dtype`.
  *  - Level l = 1..L has n_l = seq_len / block^l tokens; level 0 is the input.
  *    Pyramids are float32, levels stored in order, each starting on a
@@ -58,7 +59,9 @@ enum llsa_status {
     LLSA_ERR_UNSUPPORTED = 2,  /* valid but outside the supported set above               */
     LLSA_ERR_WORKSPACE = 3,    /* workspace pointer null or smaller than required          */
     LLSA_ERR_HIP = 4,          /* a kernel launch failed                                   */
-    LLSA_ERR_INDEX = 5         /* debug index check only: an index list or CSR is invalid   */
+    LLSA_ERR_INDEX = 5,        /* debug index check only: an index list or CSR is invalid   */
+    LLSA_ERR_SCRATCH = 6       /* llsa_attn_bwd_noalloc: the problem needs more workspace
+                                  than LLSA_NOALLOC_SCRATCH_BYTES                          */
 };
 
 /* Flags of the debug index check's status word (OR-ed). */
@@ -266,6 +269,28 @@ int llsa_attn_bwd(const llsa_problem *p, const void *q, const void *k, const voi
                   const void *o, const float *lse, const void *dout,
                   void *dq, void *dk, void *dv,
                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * llsa_attn_bwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, results and kernels without the workspace.  Its
+ * workspace is a static device array of LLSA_NOALLOC_SCRATCH_BYTES bytes that
+ * every GPU the library runs on holds until the process ends (its address is
+ * looked up on the first call with that device current; the stream must
+ * belong to the current device).  No allocation and no allocating library
+ * routine is called.  Problems whose sizes.bwd_workspace_bytes exceed the
+ * scratch are rejected on the host with LLSA_ERR_SCRATCH (nothing launched);
+ * the 65536-token, 16-head, K = 8 problem needs 22 MiB.  Every call on one
+ * GPU shares that GPU's scratch and leaves its contents behind (each call
+ * writes every byte it reads, so nothing needs clearing): calls that overlap
+ * on one GPU, on different streams or threads, race and must not be issued.
+ */
+#define LLSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int llsa_attn_bwd_noalloc(const llsa_problem *p, const void *q, const void *k, const void *v,
+                          const float *pyr_k, const float *pyr_v, const int32_t *idx,
+                          const int32_t *csr_ptr, const int32_t *csr_col,
+                          const void *o, const float *lse, const void *dout,
+                          void *dq, void *dk, void *dv, void *stream);
 
 /*
  * Dense (full, non-causal) softmax attention in the same kernel style, the

@@ -56,9 +56,34 @@ def algorithmic(w, s):
         tr += bh * n[l] * kl[l] * 4 + bh * (n[l] + 1) * 4 + bh * n[l] * kl[l] * 4
     out["transpose"] = dict(bytes=tr, flops=0)
     g = 4  # float32 gradients
-    out["attn_bwd"] = dict(bytes=4 * tok + 3 * bh * N * d * g + 3 * bh * N * 4 + 2 * coarse_pyr + idx + tr,
+    # the survey's definition: Q, K, V, O, dO read, dQ, dK, dV written, LSE and D
+    # once each.  The kernels never read O (D = sum P dP comes out of the dQ
+    # pass), but read the coarse pyramids, the pick lists and the CSR and read
+    # D back: "bytes_kernel_inputs".
+    out["attn_bwd"] = dict(bytes=5 * tok + 3 * bh * N * d * g + 2 * bh * N * 4,
+                           bytes_kernel_inputs=4 * tok + 3 * bh * N * d * g + 3 * bh * N * 4
+                           + 2 * coarse_pyr + idx + tr,
                            flops=int(2.5 * 4 * bh * N * d * nkv))
     return out, nkv
+
+
+def cpu_model():
+    """The host CPU's model string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def oracle_threads():
+    cores = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    return min(cores, int(omp)) if omp else cores
 
 
 def source_hash(paths):
@@ -75,9 +100,7 @@ def cpu_baseline(w, max_heads):
     import torch
     from hierarchical_top_sparse_mean_amd.inputs import make_inputs
     from oracle import oracle as O
-    cores = len(os.sched_getaffinity(0))
-    omp = os.environ.get("OMP_NUM_THREADS")
-    threads = min(cores, int(omp)) if omp else cores
+    threads = oracle_threads()
     heads = max(1, min(w.heads, max_heads, threads))
     q, k, v, do = make_inputs(1, heads, w.seq_len, w.head_dim, w.dtype, w.sinusoid, True, 0)
     q, k, v, do = (x.double().numpy().reshape(heads, w.seq_len, w.head_dim) for x in (q, k, v, do))
@@ -97,9 +120,65 @@ def cpu_baseline(w, max_heads):
         if dt >= 10.0 or reps >= 20:
             break
     tokens = reps * heads * w.seq_len          # batch 1
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"{reps} passes over {heads} of {w.heads} heads x {w.seq_len} tokens, "
                       f"pool+select+fwd+transpose+bwd in fp64 ({dt:.1f} s)"}
+
+
+def oracle_leg(w, g):
+    """The CPU-baseline leg of a per-workload record: the oracle, untouched,
+    timed over one whole pass of the full workload on the host cores (its own
+    pooling, selection, attention and, with a backward, transposes and
+    gradients); then, untimed, the parity of the GPU results g against it as
+    the parity tests check it: pyramids; picks level by level with the GPU's
+    parent picks as the oracle's (near-ties below 1e-5 relative exempt);
+    O, LSE and gradients from the oracle over the GPU's own pick lists."""
+    import numpy as np
+    import torch
+    from hierarchical_top_sparse_mean_amd.inputs import workload_inputs
+    from oracle import oracle as O
+    q, k, v, do = workload_inputs(w)
+    bh, N, d = w.bh, w.seq_len, w.head_dim
+    f64 = lambda t: t.double().numpy().reshape(bh, N, d)   # noqa: E731
+    q, k, v = f64(q), f64(k), f64(v)
+    do = f64(do) if do is not None else None
+    B, Lv, K, Le = w.block, w.levels, w.topk, w.enrich
+    t0 = time.perf_counter()
+    pq, pk, pv = O.pool(q, B, Lv), O.pool(k, B, Lv), O.pool(v, B, Lv)
+    idx, _ = O.select(pq, pk, B, K)
+    O.attn_fwd(q, k, v, pk, pv, idx, B, K, Le, w.scale)
+    if do is not None:
+        for l in range(1, Le + 2):
+            O.transpose(idx[l - 1], N // B ** l)
+        O.attn_bwd(q, k, v, pk, pv, idx, do, B, K, Le, w.scale)
+    dt = time.perf_counter() - t0
+    cpu = {"value": round(w.batch * N / dt, 1), "unit": "tokens/s", "cores": oracle_threads(),
+           "cpu_model": cpu_model(), "kind": "oracle",
+           "sample": f"one whole pass of the workload in fp64 ({dt:.2f} s)"}
+    par = {"pyramids": max(float(np.abs(a - b).max()) for name in ("pq", "pk", "pv")
+                           for a, b in zip(g[name], {"pq": pq, "pk": pk, "pv": pv}[name]))}
+    agree = exempt = fail = 0
+    for l in range(Lv, 0, -1):
+        oi, gap = O.select_level(pq[l - 1], pk[l - 1], B, K, None if l == Lv else g["idx"][l])
+        same = (oi == g["idx"][l - 1]).all(axis=-1)
+        near = (gap > 0) & (gap < 1e-5)
+        agree += int(same.sum())
+        exempt += int((~same & near).sum())
+        fail += int((~same & ~near).sum())
+    par.update(picks_agree=agree, picks_exempt=exempt, picks_fail=fail,
+               picks_equal_unforced=sum(int((a == b).all(axis=-1).sum()) for a, b in zip(g["idx"], idx)))
+    o, lse = O.attn_fwd(q, k, v, pk, pv, g["idx"], B, K, Le, w.scale)
+    par["o_max_abs"] = float(np.abs(g["o"] - o).max())
+    par["lse_max_abs"] = float(np.abs(g["lse"] - lse).max())
+    if do is not None:
+        dq, dk, dv = O.attn_bwd(q, k, v, pk, pv, g["idx"], do, B, K, Le, w.scale)
+        for name, want in (("dq", dq), ("dk", dk), ("dv", dv)):
+            par[name + "_max_abs"] = float(np.abs(g[name] - want).max())
+    tol = 1e-4 if w.dtype == torch.float32 else 2e-2
+    par["bar"] = tol
+    par["pass"] = bool(fail == 0 and all(v <= tol for key, v in par.items() if key.endswith("_max_abs")))
+    return cpu, par
 
 
 def time_workload(L, w, steps, warmup, dev, grad_bf16=False, token_order=0, overlap=False):
@@ -265,6 +344,111 @@ def transpose_scaling(L, dev, reps):
         torch.cuda.empty_cache()
 
 
+def call_details(alg, per_call):
+    """Per-call ms, algorithmic GB/s and HBM fraction, TFLOP/s and bf16 MFMA
+    fraction (attention) for measured per-call milliseconds."""
+    detail = {}
+    for c, ms in per_call.items():
+        a = alg[c]
+        detail[c] = {"ms": round(ms, 4), "GB/s": round(a["bytes"] / ms / 1e6, 1),
+                     "hbm_frac": round(a["bytes"] / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        if a["flops"]:
+            detail[c]["TFLOP/s"] = round(a["flops"] / ms / 1e9, 2)
+        if c in ("attn_fwd", "attn_bwd"):
+            detail[c]["bf16_mfma_frac"] = round(detail[c]["TFLOP/s"] / BF16_PEAK_TFLOPS, 4)
+            # MFMA fraction this kernel could reach if it ran at the HBM peak
+            detail[c]["bf16_mfma_frac_cap_at_hbm_peak"] = round(
+                a["flops"] / (a["bytes"] / (HBM_PEAK_GBS * 1e9)) / 1e12 / BF16_PEAK_TFLOPS, 4)
+        if "bytes_kernel_inputs" in a:
+            detail[c]["GB/s_kernel_inputs"] = round(a["bytes_kernel_inputs"] / ms / 1e6, 1)
+    return detail
+
+
+def step_calls(L, w, p, B, q, k, v, dout):
+    """The calls of one step, in order, as (name, function)."""
+    calls = [("pool", lambda: L.llsa_pool(p, q, k, v, B.pyr_q, B.pyr_k, B.pyr_v)),
+             ("select", lambda: L.llsa_select(p, B.pyr_q, B.pyr_k, B.idx)),
+             ("attn_fwd", lambda: L.llsa_attn_fwd(p, q, k, v, B.pyr_k, B.pyr_v, B.idx, B.o, B.lse))]
+    if w.backward:
+        calls += [("transpose", lambda: L.transpose_levels(B)),
+                  ("attn_bwd", lambda: L.llsa_attn_bwd(p, q, k, v, B.pyr_k, B.pyr_v, B.idx, B.csr_ptr,
+                                                       B.csr_col, B.o, B.lse, dout, B.dq, B.dk, B.dv,
+                                                       B.ws, B.ws.numel()))]
+    return calls
+
+
+def time_cold(L, w, p, B, q, k, v, dout, reps, dev):
+    """Per-call milliseconds with every call timed on its own right after a
+    512 MiB write, which evicts the 256 MB memory-side cache (MALL): the cold
+    counterpart of the warm, back-to-back step timing."""
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    calls = step_calls(L, w, p, B, q, k, v, dout)
+    tot = {c: 0.0 for c, _ in calls}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for r in range(reps):
+        for c, fn in calls:
+            flush.fill_(r & 255)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            tot[c] += e0.elapsed_time(e1)
+    del flush
+    return {c: v / reps for c, v in tot.items()}
+
+
+def gpu_results(B, w):
+    """Host copies of the GPU results of the last step, for the parity leg."""
+    bh, N, d, Lv = w.bh, w.seq_len, w.head_dim, w.levels
+    host = lambda t: t.detach().double().cpu().numpy()   # noqa: E731
+    g = {name: [host(B.pyramid_level(buf, l)) for l in range(1, Lv + 1)]
+         for name, buf in (("pq", B.pyr_q), ("pk", B.pyr_k), ("pv", B.pyr_v))}
+    g["idx"] = [B.index_level(l).cpu().numpy() for l in range(1, Lv + 1)]
+    g["o"] = host(B.o).reshape(bh, N, d)
+    g["lse"] = host(B.lse).reshape(bh, N)
+    if w.backward:
+        for name in ("dq", "dk", "dv"):
+            g[name] = host(getattr(B, name)).reshape(bh, N, d)
+    return g
+
+
+def config_records(L, dev, steps, warmup, cold_reps):
+    """One JSON line per workload of the table: warm per-call times (and cold,
+    after a 512 MiB flush, for the workloads whose working set fits the
+    256 MB MALL), the dominant call's roofline, parity against the oracle and
+    the oracle's own time on the host cores."""
+    import torch
+    from hierarchical_top_sparse_mean_amd.inputs import WORKLOADS
+    for w in WORKLOADS.values():
+        q, k, v, dout, p, B, s, pc, msps = time_workload(L, w, steps, warmup, dev)
+        alg, nkv = algorithmic(w, s)
+        dom = max(pc, key=lambda c: pc[c])
+        ach = alg[dom]["bytes"] / pc[dom] / 1e6
+        rec = {"config_record": w.name, "describe": w.describe(), "keys_per_query_block": nkv,
+               "ms_per_step": round(msps, 4), "tokens_per_s": round(w.batch * w.seq_len / (msps / 1e3), 1),
+               "timing": "warm: calls back to back, inputs resident",
+               "calls": call_details(alg, pc),
+               "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1),
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                            "traffic": None, "algorithmic_bytes": alg[dom]["bytes"]}}
+        # working set (inputs, pyramids, lists, outputs) within the MALL: time it cold too
+        ws_bytes = sum(t.numel() * t.element_size() for t in (q, k, v, B.o, B.pyr_q, B.pyr_k, B.pyr_v))
+        if w.name in ("n4096_bf16", "n16384_bf16"):
+            rec["working_set_MB"] = round(ws_bytes / 1e6, 1)
+            rec["calls_cold"] = call_details(alg, time_cold(L, w, p, B, q, k, v, dout, cold_reps, dev))
+            rec["timing_cold"] = "each call alone after a 512 MiB write (MALL flushed)"
+        # one more step so that every result comes from the same pass, then the oracle
+        for _, fn in step_calls(L, w, p, B, q, k, v, dout):
+            fn()
+        torch.cuda.synchronize()
+        g = gpu_results(B, w)
+        rec["cpu_baseline"], rec["parity"] = oracle_leg(w, g)
+        print(json.dumps(rec), flush=True)
+        del q, k, v, dout, B, g
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -284,6 +468,11 @@ def main():
     ap.add_argument("--transpose-scaling", action="store_true",
                     help="time the level-1 index transpose against the dense-mask baseline for "
                          "4096 .. 1048576 tokens (one JSON line each)")
+    ap.add_argument("--configs", action="store_true",
+                    help="one record per workload of the table: warm (and, where the working set "
+                         "fits the MALL, cold) per-call times, roofline, parity against the oracle "
+                         "and the oracle's time")
+    ap.add_argument("--cold-reps", type=int, default=10)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -321,6 +510,9 @@ def main():
     if args.transpose_scaling:
         transpose_scaling(L, dev, args.steps)
         return
+    if args.configs:
+        config_records(L, dev, args.steps, args.warmup, args.cold_reps)
+        return
     if args.copy_probe:
         n = args.copy_probe * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -339,20 +531,7 @@ def main():
     value = tokens / (ms_per_step / 1e3)
 
     alg, nkv = algorithmic(w, s)
-    detail = {}
-    for c in calls:
-        ms = per_call[c]
-        a = alg[c]
-        detail[c] = {"ms": round(ms, 4), "GB/s": round(a["bytes"] / ms / 1e6, 1),
-                     "hbm_frac": round(a["bytes"] / ms / 1e6 / HBM_PEAK_GBS, 4)}
-        if a["flops"]:
-            detail[c]["TFLOP/s"] = round(a["flops"] / ms / 1e9, 2)
-    for c in ("attn_fwd", "attn_bwd"):
-        if c in detail:
-            detail[c]["bf16_mfma_frac"] = round(detail[c]["TFLOP/s"] / BF16_PEAK_TFLOPS, 4)
-            # MFMA fraction this kernel could reach if it ran at the HBM peak
-            detail[c]["bf16_mfma_frac_cap_at_hbm_peak"] = round(
-                alg[c]["flops"] / (alg[c]["bytes"] / (HBM_PEAK_GBS * 1e9)) / 1e12 / BF16_PEAK_TFLOPS, 4)
+    detail = call_details(alg, per_call)
 
     # dominant call -> roofline (HBM-bound; algorithmic bytes / measured time)
     dom = max(calls, key=lambda c: per_call[c])
@@ -368,6 +547,11 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes": alg[dom]["bytes"]}
+    if "bytes_kernel_inputs" in alg[dom]:
+        # the same time over the bytes the kernels must touch (no O; pyramids, lists, CSR, D read back)
+        bk = alg[dom]["bytes_kernel_inputs"]
+        roofline["bytes_kernel_inputs"] = bk
+        roofline["frac_kernel_inputs"] = round(bk / per_call[dom] / 1e6 / HBM_PEAK_GBS, 4)
 
     dense = None
     if not args.no_dense and w.dtype == torch.bfloat16:

@@ -119,7 +119,9 @@ def cpu_baseline(w, max_heads):
         dt = time.perf_counter() - t0
         if dt >= 10.0 or reps >= 20:
             break
-    tokens = reps * heads * w.seq_len          # batch 1
+    # tokens as the GPU line counts them (batch x sequence, all heads): the
+    # sample covers heads / w.heads of a pass
+    tokens = reps * w.batch * w.seq_len * heads / w.heads
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": f"{reps} passes over {heads} of {w.heads} heads x {w.seq_len} tokens, "

@@ -86,7 +86,6 @@ __device__ __forceinline__ void sort_asc_u32(uint32_t (&a)[N]) {
             }
 }
 
-constexpr int kSelTilesPerChunk = 8;
 constexpr int kSelCountKeys = 4096;   // keys a fused count can hold
 
 // parent == nullptr: coarsest level, candidates 0..n-1, row groups are
@@ -157,13 +156,17 @@ __global__ __launch_bounds__(COUNT ? 512 : 256) void select_kernel(const float *
     for (int i = 0; i < KM; ++i) best[i] = 0;
 
     const int tb = part * ntiles / SPLIT, te = (part + 1) * ntiles / SPLIT;
-    // candidate tiles are read LB at a time (all of a batch before the first
-    // is used); KM = 32 halves the batch to stay within the register budget
-    constexpr int LB = KM > 16 ? kSelTilesPerChunk / 2 : kSelTilesPerChunk;
-    for (int t0 = tb; t0 < te; t0 += kSelTilesPerChunk) {
-        uint64_t keys[4 * kSelTilesPerChunk];
+    // candidate tiles come CH at a time, CH = 4 tiles (16 keys per lane) for
+    // K <= 16: the kernel then fits 4 waves per SIMD, so that a level-1 grid of
+    // 4 row groups per SIMD runs in one round rather than a full one and a
+    // third.  K = 32 needs 8 tiles per sorted group, read in two batches of 4.
+    // All loads of a batch are in flight before its first tile is used.
+    constexpr int CH = KM > 16 ? 8 : 4;
+    constexpr int LB = 4;
+    for (int t0 = tb; t0 < te; t0 += CH) {
+        uint64_t keys[4 * CH];
 #pragma unroll
-        for (int hb = 0; hb < kSelTilesPerChunk; hb += LB) {
+        for (int hb = 0; hb < CH; hb += LB) {
             // tiles past the end re-read the last tile and are masked out
             float kf[LB][16];
             int base[LB];
@@ -202,12 +205,18 @@ __global__ __launch_bounds__(COUNT ? 512 : 256) void select_kernel(const float *
             }
         }
 #pragma unroll
-        for (int grp = 0; grp < 4 * kSelTilesPerChunk / KM; ++grp) {
+        for (int grp = 0; grp < 4 * CH / KM; ++grp) {
+            if (t0 + grp * KM / 4 >= te) break;   // every tile of the group is past the end
             uint64_t part[KM];
 #pragma unroll
             for (int i = 0; i < KM; ++i) part[i] = keys[grp * KM + i];
             sort_desc<KM>(part);
-            merge_top<KM>(best, part);
+            if (t0 == tb && grp == 0) {   // the first group is the running list
+#pragma unroll
+                for (int i = 0; i < KM; ++i) best[i] = part[i];
+            } else {
+                merge_top<KM>(best, part);
+            }
         }
     }
     // the 4 lanes holding one query merge their lists

@@ -311,18 +311,20 @@ __global__ __launch_bounds__(kTrThreads) void tr_bounds_kernel(const int32_t *__
 // + 512) of matrix b and reads every pick of the matrix (from L2: each pick
 // is read by cols / 512 workgroups).  Every workgroup scans all the picks of
 // its matrix, so fewer, wider parts do less work in total; 512 keys keep the
-// per-wave counters and masks at 96 KB of LDS, one workgroup per CU, and the
-// levels of a 65536-token problem in fewer workgroups than CUs:
-//  - the number of picks with a smaller key gives where its keys' lists start;
-//  - wave w owns elements [w per, (w + 1) per) and counts their picks of its
-//    keys per key, so an exclusive prefix over the waves, plus the scan over
-//    the keys, is the first slot of each (wave, key);
-//  - each wave then reads its elements again in order, keeps the picks of its
-//    keys in an LDS queue (ballot and popcount keep their order), and places
-//    them 64 at a time, ranking the picks of one key inside a chunk by a
-//    popcount of an LDS lane mask as the fill kernel does, with its own masks
-//    and cursors: the 16 waves place their picks independently and every list
-//    keeps its row order.
+// per-slice counters and masks at 96 KB of LDS (128 KB with the part's
+// queue), one workgroup per CU, and the levels of a 65536-token problem in
+// fewer workgroups than CUs:
+//  - wave w holds elements [w per, (w + 1) per); the number of picks with a
+//    smaller key gives where the part's lists start;
+//  - the part's picks form a sequence in element order, cut into 16 slices:
+//    either equal slices of an LDS queue that the waves fill in order, or
+//    each wave's own elements.  Wave s counts the picks of slice s per key,
+//    so an exclusive prefix over the slices, plus the scan over the keys, is
+//    the first slot of each (slice, key);
+//  - each wave places its slice's picks 64 at a time, ranking the picks of
+//    one key inside a chunk by a popcount of an LDS lane mask as the fill
+//    kernel does, with its own masks and cursors: the 16 waves place their
+//    picks independently and every list keeps its row order.
 // No workspace, no global atomic, nothing to clear beforehand.
 constexpr int kTrOneThreads = 1024;
 constexpr int kTrOneWaves = kTrOneThreads / kWave;
@@ -331,10 +333,13 @@ constexpr int kTrOneChunks = 32;                                   // 64-pick ch
 constexpr int kTrOneRound = kTrOneChunks * kWave;                  // picks a wave holds at once
 constexpr int kTrOneMaxPicks = 4 * kTrOneWaves * kTrOneRound;      // 131072 per matrix
 constexpr int kTrOneMaxCols = 4096;
+constexpr int kTrOneQueue = 8192;                                 // picks of a part queued in LDS
+constexpr int kTrOneQueueMinPer = 1024;                           // elements per wave from which the queue pays
 constexpr int kTrOneEBits = 17;                                    // a queued pick: key << 17 | element
 static_assert(kTrOneMaxPicks <= (1 << kTrOneEBits), "element index must fit its field");
 static_assert(((uint64_t)kTrOneKeys << kTrOneEBits) <= (1ull << 32), "key offset and element fit 32 bits");
 static_assert(kTrOneKeys <= kTrOneThreads && kTrOneKeys % kWave == 0, "a thread per key of the part");
+static_assert(kTrOneQueue >= kTrOneWaves * 2 * kWave, "the per-wave queues fit the part queue");
 
 static bool tr_one_fits(int rows, int k, int cols) {
     return (int64_t)rows * k <= kTrOneMaxPicks && cols <= kTrOneMaxCols;
@@ -360,10 +365,11 @@ __global__ __launch_bounds__(kTrOneThreads) void tr_one_kernel(TrOneArgs A) {
     int32_t *__restrict__ ptr = A.m[mi].ptr;
     int32_t *__restrict__ col = A.m[mi].col;
     const int rows = A.m[mi].rows, k = A.m[mi].k, cols = A.m[mi].cols;
-    __shared__ int32_t cur[kTrOneWaves][kTrOneKeys];    // per-wave counts, then cursors
+    __shared__ int32_t cur[kTrOneWaves][kTrOneKeys];    // per-slice counts, then cursors
     __shared__ uint64_t mask[kTrOneWaves][kTrOneKeys];
-    __shared__ uint32_t queue[kTrOneWaves][2 * kWave];
+    __shared__ uint32_t queue[kTrOneQueue];             // the part's picks, in element order
     __shared__ int32_t below_w[kTrOneWaves];
+    __shared__ int32_t inr_w[kTrOneWaves];
     __shared__ int32_t scan_w[kTrOneKeys / kWave];
     const int b = blockIdx.y;
     const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
@@ -388,21 +394,67 @@ __global__ __launch_bounds__(kTrOneThreads) void tr_one_kernel(TrOneArgs A) {
             kv[j] = e < ew1 ? I[e] : -1;
         }
     };
+    auto in_part = [&](int c) { return c >= c0 && c < c0 + nk; };
+    auto pack = [&](int c, int e) { return ((uint32_t)(c - c0) << kTrOneEBits) | (uint32_t)e; };
     load(0);
-    __syncthreads();
-    int below = 0;
+    // picks with a smaller key (where the part's lists start) and picks of the part, per wave
+    int below = 0, inr = 0;
     for (int r = 0; r < rounds; ++r) {
 #pragma unroll
         for (int j = 0; j < kTrOneChunks; ++j) {
-            const int c = kv[j];
-            below += (c >= 0 && c < c0) ? 1 : 0;
-            if (c >= c0 && c < c0 + nk) atomicAdd(&cur[w][c - c0], 1);
+            below += (kv[j] >= 0 && kv[j] < c0) ? 1 : 0;
+            inr += in_part(kv[j]) ? 1 : 0;
         }
         if (r + 1 < rounds) load(r + 1);
     }
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) below += __shfl_xor(below, d, kWave);
-    if (lane == 0) below_w[w] = below;
+    for (int d = 1; d < kWave; d <<= 1) {
+        below += __shfl_xor(below, d, kWave);
+        inr += __shfl_xor(inr, d, kWave);
+    }
+    if (lane == 0) {
+        below_w[w] = below;
+        inr_w[w] = inr;
+    }
+    __syncthreads();
+    int qoff = 0, qtot = 0;
+#pragma unroll
+    for (int x = 0; x < kTrOneWaves; ++x) {
+        const int v = inr_w[x];
+        qoff += x < w ? v : 0;
+        qtot += v;
+    }
+    // Picks are local: the rows of one wave's element range pick mostly the
+    // keys of one part, so that a part's picks sit in a few waves.  When they
+    // fit, and the waves hold enough elements for the balance to pay for the
+    // second pass over them, they are queued in element order (ballot and
+    // popcount keep the order inside a chunk) and every wave counts and places
+    // an equal slice of the queue; otherwise every wave counts and places its
+    // own elements' picks.
+    const bool queued = qtot <= kTrOneQueue && per >= kTrOneQueueMinPer;   // uniform over the workgroup
+    const int s0 = w * qtot / kTrOneWaves, s1 = (w + 1) * qtot / kTrOneWaves;
+    if (queued) {
+        for (int r = 0; r < rounds; ++r) {
+            if (rounds > 1) load(r);
+            const int er = ew0 + r * kTrOneRound;
+#pragma unroll
+            for (int j = 0; j < kTrOneChunks; ++j) {
+                const bool in = in_part(kv[j]);
+                const uint64_t bal = __ballot(in);
+                if (in) queue[qoff + __popcll(bal & lower)] = pack(kv[j], er + j * kWave + lane);
+                qoff += __popcll(bal);
+            }
+        }
+        __syncthreads();
+        for (int e = s0 + lane; e < s1; e += kWave) atomicAdd(&cur[w][queue[e] >> kTrOneEBits], 1);
+    } else {
+        for (int r = 0; r < rounds; ++r) {
+            if (rounds > 1) load(r);
+#pragma unroll
+            for (int j = 0; j < kTrOneChunks; ++j)
+                if (in_part(kv[j])) atomicAdd(&cur[w][kv[j] - c0], 1);
+        }
+    }
     __syncthreads();
     // thread t < kTrOneKeys: key c0 + t -- prefix over the waves, then the scan over keys
     int tot = 0;
@@ -430,10 +482,10 @@ __global__ __launch_bounds__(kTrOneThreads) void tr_one_kernel(TrOneArgs A) {
     }
     __syncthreads();
     int32_t *C = col + (int64_t)b * E;
-    uint32_t *Q = queue[w];
-    int fill = 0;   // queued picks (uniform across the wave, below 64 between chunks)
-    // places the first n (<= 64) queued picks and moves the rest to the front
-    auto place = [&](int n) {
+    // places the queued picks Q[0, n), n <= 64, in order: the picks of one key
+    // are ranked by a popcount of an LDS lane mask, then the highest lane of
+    // each key moves its cursor on
+    auto place = [&](const uint32_t *Q, int n) {
         wave_lds_sync();
         const bool ok = lane < n;
         const uint32_t v = ok ? Q[lane] : 0u;
@@ -447,24 +499,33 @@ __global__ __launch_bounds__(kTrOneThreads) void tr_one_kernel(TrOneArgs A) {
             cur[w][cl] += __popcll(mk);
             mask[w][cl] = 0ull;
         }
-        if (lane < fill - n) Q[lane] = Q[n + lane];   // reads [64, 128), writes [0, 64)
-        fill -= n;
-        wave_lds_sync();
     };
+    if (queued) {
+        for (int h = s0; h < s1; h += kWave) place(queue + h, min(kWave, s1 - h));
+        return;
+    }
+    // the wave's own elements, scanned again; their picks of the part go
+    // through a queue of 128 of its own (below 64 between chunks)
+    uint32_t *Q = queue + w * 2 * kWave;
+    int fill = 0;
     for (int r = 0; r < rounds; ++r) {
         if (rounds > 1) load(r);
         const int er = ew0 + r * kTrOneRound;
 #pragma unroll
         for (int j = 0; j < kTrOneChunks; ++j) {
-            const int c = kv[j];
-            const bool in = c >= c0 && c < c0 + nk;
+            const bool in = in_part(kv[j]);
             const uint64_t bal = __ballot(in);
-            if (in) Q[fill + __popcll(bal & lower)] = ((uint32_t)(c - c0) << kTrOneEBits) | (uint32_t)(er + j * kWave + lane);
+            if (in) Q[fill + __popcll(bal & lower)] = pack(kv[j], er + j * kWave + lane);
             fill += __popcll(bal);
-            if (fill >= kWave) place(kWave);
+            if (fill >= kWave) {
+                place(Q, kWave);
+                if (lane < fill - kWave) Q[lane] = Q[kWave + lane];   // reads [64, 128), writes [0, 64)
+                fill -= kWave;
+                wave_lds_sync();
+            }
         }
     }
-    if (fill > 0) place(fill);
+    if (fill > 0) place(Q, fill);
 }
 
 static void launch_tr_one(const TrOneMat *mats, int n, int nb, hipStream_t s) {

@@ -547,13 +547,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
     };
     // element offset (within the head) of row r of sequence block b
     auto trow = [&](int b, int r) { return (int64_t)tok_tile_row<ORD>(a.tm, b, r) * kHeadDim; };
+    // K / V rows through buffer loads with 32-bit byte offsets within the head
+    const uint32_t head_bytes = (uint32_t)a.N * kHeadDim * 2;
+    const Rsrc rk = make_rsrc(k + head_off, head_bytes), rv = make_rsrc(v + head_off, head_bytes);
     auto load_tile = [&](int u, TileRegs &R) {
         const int f = pick(u);
-        const int64_t o0 = head_off + trow(f, lrow) + lcol, o1 = head_off + trow(f, lrow + 8) + lcol;
-        R.ka0 = load_bf16x8(k + o0);
-        R.ka1 = load_bf16x8(k + o1);
-        R.va0 = load_bf16x8(v + o0);
-        R.va1 = load_bf16x8(v + o1);
+        const uint32_t o0 = ((uint32_t)tok_tile_row<ORD>(a.tm, f, lrow) * kHeadDim + lcol) * 2u;
+        const uint32_t o1 = ((uint32_t)tok_tile_row<ORD>(a.tm, f, lrow + 8) * kHeadDim + lcol) * 2u;
+        R.ka0 = buf_load_bf16x8(rk, o0);
+        R.ka1 = buf_load_bf16x8(rk, o1);
+        R.va0 = buf_load_bf16x8(rv, o0);
+        R.va1 = buf_load_bf16x8(rv, o1);
     };
     struct QRegs {
         bf16x8 qa0, qa1, da0, da1;

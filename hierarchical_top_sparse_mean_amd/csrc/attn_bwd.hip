@@ -1465,185 +1465,297 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_b64_kernel(
 }
 
 // ================================================================ f32 path
-// Float32 inputs (the small exact-parity configurations): one wave per token,
-// lane = dimension; every dot product is a butterfly sum across the wave, and
-// keys are visited in a fixed order, so the results are reproducible.
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m, kWave);
-    return x;
-}
+// Float32 inputs run on the float32 matrix cores (16 x 16 x 4).  Keys and
+// queries are visited in a fixed order throughout and every sum is taken in a
+// fixed order, so the results are reproducible.
 
-// Pass A (f32): one wave per query token.
-__global__ __launch_bounds__(256) void bwd_dq_f32_kernel(
+// Pass A (f32): one workgroup per group of 16 consecutive query tiles (all
+// under one level-2 node, so they share their coarse entries), one wave per 4
+// tiles, on the float32 matrix cores and laid out as the float32 forward
+// (scores transposed, lane (g, c): query c against keys 4g .. 4g + 3; row
+// layout for Q, dO, K and V in the score products, column layout for K in
+// dQ^T += K^T dS^T).  D = rowsum(dO * O) comes from O first, so dS = P (dP -
+// D) is formed tile by tile.  The pooled-token gradients of each coarse tile
+// are then summed over the group: the coarse scores are recomputed query-major
+// (lane (g, c): entry c against queries 4g .. 4g + 3), so P and dS feed
+// dK_c^T += Q^T dS and dV_c^T += dO^T P with Q and dO in the column layout;
+// the 4 waves' sums meet in LDS, in wave order, and are written as the group's
+// partial rows, which the coarse reduction adds per pooled token.
+__global__ __launch_bounds__(256, 2) void bwd_dq_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ pk, const float *__restrict__ pv, const int32_t *__restrict__ idx,
     const float *__restrict__ o, const float *__restrict__ lse, const float *__restrict__ dout,
     void *__restrict__ dq, BwdWs ws, BwdArgs a) {
-    const int64_t tq = (int64_t)blockIdx.x * 4 + wave_id();
-    if (tq >= (int64_t)a.bh * a.N) return;
+    __shared__ __attribute__((aligned(16))) float red[4][2][kBlock * kHeadDim];   // waves' coarse sums
+    const int w = wave_id();
     const int lane = lane_id();
-    const int h = (int)(tq / a.N);
-    const int tok = (int)(tq % a.N);
-    const int ib = tok / (kBlock * a.sub);   // query block
+    const int g = lane >> 4, c16 = lane & 15;
+    const int gph = (a.nt1 + kBlock - 1) / kBlock;   // groups per head
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    if (bid >= a.bh * gph) return;   // the whole workgroup
+    const int h = bid / gph;
+    const int G = bid % gph;
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
-    const int64_t srow = tok_row(a.tm, tok);
-    const int64_t row = head_off + srow * kHeadDim + lane;
-    const float qx = q[row], gx = dout[row];
-    const float D = wave_sum(gx * o[row]);
-    if (lane == 0) ws.D[tq] = D;   // by sequence position
-    const float lse2 = lse[(int64_t)h * a.N + srow] * kLog2e;
-    float acc = 0.f;
-    auto visit = [&](float kx, float vx, float bias) {
-        const float s = wave_sum(qx * kx);
-        const float dp = wave_sum(gx * vx);
-        const float p = exp2f(s * a.sl2 + bias - lse2);
-        acc = fmaf(p * (dp - D), kx, acc);
+    auto trow = [&](int b, int r) { return (int64_t)tok_row(a.tm, b * kBlock + r) * kHeadDim; };
+    const int nft = a.K1 * a.sub;
+    const int nct = (a.ncoarse + kBlock - 1) / kBlock;
+    struct KVT {
+        float kr[16], vr[16];   // K and V row c (row layout)
+        f32x4 kc[4];            // K rows 4g + i, dims 4c .. 4c + 3 (column layout)
     };
-    const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
-    for (int jt = 0; jt < a.K1 * a.sub; ++jt) {   // key tiles: sub-tile jt % sub of pick jt / sub
-        const int u0 = (__builtin_amdgcn_readfirstlane(fine[jt / a.sub]) * a.sub + jt % a.sub) * kBlock;
-        float kx[kBlock], vx[kBlock];
+    // pooled row of coarse entry e (-1: no such entry) and its log2 weight for
+    // query block ib (-inf where the entry is dropped for the block)
+    auto coarse_row = [&](int ib, const int32_t *fine, int e, float &bias) -> int64_t {
+        int jl = 0, c = -1;
+        float b = 0.f;
+        const bool ok = bwd_coarse_entry(a, idx, fine, h, ib, e, jl, c, b);
+        bias = ok ? b : -INFINITY;
+        return c >= 0 ? a.cl_pyr_off[jl] + ((int64_t)h * a.cl_n[jl] + c) * kHeadDim : -1;
+    };
+    float Dv[4], L2v[4];   // D and lse * log2(e) of query c16 of the wave's tiles
+    // ---- dQ of the wave's 4 tiles
+    for (int jt = 0; jt < 4; ++jt) {
+        const int qt = G * kBlock + 4 * w + jt;
+        Dv[jt] = L2v[jt] = 0.f;
+        if (qt >= a.nt1) break;   // ragged last group (single level only)
+        const int ib = qt / a.sub;
+        const int64_t qoff = head_off + trow(qt, c16) + 16 * g;
+        float qf[16], gf[16];
+        load_row16(q + qoff, qf);
+        load_row16(dout + qoff, gf);
+        float D;
+        {
+            float of[16];
+            load_row16(o + qoff, of);
+            float part = 0.f;
 #pragma unroll
-        for (int t = 0; t < kBlock; ++t) {
-            const int64_t kr = head_off + (int64_t)tok_row(a.tm, u0 + t) * kHeadDim + lane;
-            kx[t] = k[kr];
-            vx[t] = v[kr];
+            for (int d = 0; d < 16; ++d) part = fmaf(gf[d], of[d], part);
+            D = sum4_groups(part);
         }
-#pragma unroll
-        for (int t = 0; t < kBlock; ++t) visit(kx[t], vx[t], 0.f);
-    }
-    for (int e = 0; e < a.ncoarse; ++e) {
-        int jl, c;
-        float b;
-        if (bwd_coarse_entry(a, idx, fine, h, ib, e, jl, c, b)) {
-            const int64_t roff = a.cl_pyr_off[jl] + ((int64_t)h * a.cl_n[jl] + c) * kHeadDim + lane;
-            visit(pk[roff], pv[roff], b);
-        }
-    }
-    store_grad1(dq, row, acc * a.scale, a.grad_bf16);
-}
-
-// Pooled-token gradients (f32): one workgroup of kCoarseWaves waves per
-// (level, pooled token).  The query blocks under the rows that picked the
-// token (from the CSR of I^(l)) are dealt out to the waves in turn, 16 query
-// rows at a time; each wave keeps its own partial sums, and the partials are
-// added in wave order at the end, so the result does not depend on timing.
-constexpr int kCoarseWaves = 16;
-__global__ __launch_bounds__(kCoarseWaves * kWave) void bwd_coarse_f32_kernel(
-    const float *__restrict__ q, const float *__restrict__ pk, const float *__restrict__ pv,
-    const int32_t *__restrict__ idx, const float *__restrict__ lse, const float *__restrict__ dout,
-    const int32_t *__restrict__ csr_ptr, const int32_t *__restrict__ csr_col, BwdWs ws, BwdArgs a,
-    int j) {
-    __shared__ float red[kCoarseWaves][2][kHeadDim];
-    const int64_t t = blockIdx.x;
-    const int nl = a.cl_n[j], kl = a.cl_k[j], span = a.cl_span[j];
-    if (t >= (int64_t)a.bh * nl) return;
-    const int lane = lane_id(), w = wave_id();
-    const int h = (int)(t / nl);
-    const int c = (int)(t % nl);
-    const int64_t head_off = (int64_t)h * a.N * kHeadDim;
-    const int64_t roff = a.cl_pyr_off[j] + ((int64_t)h * nl + c) * kHeadDim;
-    const float kx = pk[roff + lane], vx = pv[roff + lane];
-    const float bias = a.lgB * (float)(j + 2);
-    float gk = 0.f, gv = 0.f;
-    const int32_t *P = csr_ptr + a.cl_ptr_off[j] + (int64_t)h * (nl + 1);
-    const int32_t *C = csr_col + a.cl_col_off[j] + (int64_t)h * nl * kl;
-    const int e0 = __builtin_amdgcn_readfirstlane(P[c]), e1 = __builtin_amdgcn_readfirstlane(P[c + 1]);
-    // query block n of the token's list: picking row e0 + n / span, block n % span under it
-    for (int n = w; n < (e1 - e0) * span; n += kCoarseWaves) {
-        const int r = __builtin_amdgcn_readfirstlane(C[e0 + n / span]);
-        const int ib = r * span + n % span;
+        if (g == 0) ws.D[(int64_t)h * a.N + (int64_t)qt * kBlock + c16] = D;   // by sequence position
+        const float lse2 = lse[(int64_t)h * a.N + tok_row(a.tm, qt * kBlock + c16)] * kLog2e;
+        Dv[jt] = D;
+        L2v[jt] = lse2;
         const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
-        if (a.drop && a.K1 >= span) {
-            int cov = 0;
-            for (int ff = 0; ff < a.K1; ++ff) cov += (fine[ff] / span == c) ? 1 : 0;
-            if (cov == span) continue;
-        }
-        for (int qt = ib * a.sub; qt < (ib + 1) * a.sub; ++qt) {
-            float qx[kBlock], gx[kBlock];
-            int64_t srow[kBlock];
+        f32x4 acc[4];
 #pragma unroll
-            for (int tt = 0; tt < kBlock; ++tt) {
-                srow[tt] = tok_row(a.tm, qt * kBlock + tt);
-                qx[tt] = q[head_off + srow[tt] * kHeadDim + lane];
-                gx[tt] = dout[head_off + srow[tt] * kHeadDim + lane];
+        for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto load_fine = [&](int tt, KVT &T) {
+            const int f = __builtin_amdgcn_readfirstlane(fine[tt / a.sub]) * a.sub + tt % a.sub;
+            const int64_t rc = head_off + trow(f, c16) + 16 * g;
+            load_row16(k + rc, T.kr);
+            load_row16(v + rc, T.vr);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) T.kc[i] = *reinterpret_cast<const f32x4 *>(k + head_off + trow(f, 4 * g + i) + 4 * c16);
+        };
+        auto visit = [&](const KVT &T, const float (&bias)[4]) {
+            f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = s;
+#pragma unroll
+            for (int d = 0; d < 16; ++d) {
+                s = mfma_f32_4(T.kr[d], qf[d], s);
+                dp = mfma_f32_4(T.vr[d], gf[d], dp);
             }
 #pragma unroll
-            for (int tt = 0; tt < kBlock; ++tt) {
-                const int64_t tok = (int64_t)h * a.N + (int64_t)qt * kBlock + tt;
-                const float s = wave_sum(qx[tt] * kx);
-                const float dp = wave_sum(gx[tt] * vx);
-                const float p = exp2f(s * a.sl2 + bias - lse[(int64_t)h * a.N + srow[tt]] * kLog2e);
-                const float ds = p * (dp - ws.D[tok]);
-                gk = fmaf(ds, qx[tt], gk);
-                gv = fmaf(p, gx[tt], gv);
+            for (int i = 0; i < 4; ++i) {
+                const float p = fast_exp2(s[i] * a.sl2 + bias[i] - lse2);
+                const float ds = p * (dp[i] - D);
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma_f32_4(T.kc[i][dt], ds, acc[dt]);
+            }
+        };
+        const float nobias[4] = {0.f, 0.f, 0.f, 0.f};
+        KVT T0, T1;
+        if (nft > 0) load_fine(0, T0);
+        for (int tt = 0; tt < nft; tt += 2) {
+            if (tt + 1 < nft) load_fine(tt + 1, T1);
+            visit(T0, nobias);
+            if (tt + 2 < nft) load_fine(tt + 2, T0);
+            if (tt + 1 < nft) visit(T1, nobias);
+        }
+        // coarse entries, 16 a tile; absent or dropped ones read row 0 and are masked
+        for (int ct = 0; ct < nct; ++ct) {
+            KVT T;
+            float bias[4], bk;
+            const int64_t rk = coarse_row(ib, fine, ct * kBlock + c16, bk);
+            const int64_t rks = rk < 0 ? 0 : rk;
+            load_row16(pk + rks + 16 * g, T.kr);
+            load_row16(pv + rks + 16 * g, T.vr);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t ri = coarse_row(ib, fine, ct * kBlock + 4 * g + i, bias[i]);
+                T.kc[i] = *reinterpret_cast<const f32x4 *>(pk + (ri < 0 ? 0 : ri) + 4 * c16);
+            }
+            visit(T, bias);
+        }
+        // lane (g, c) holds dims 16g + 4j + dt of query c
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            store_grad4(dq, qoff + 4 * j, f32x4{acc[0][j], acc[1][j], acc[2][j], acc[3][j]} * a.scale, a.grad_bf16);
+    }
+    // ---- pooled-token gradients of the group, one coarse tile at a time
+    for (int ct = 0; ct < nct; ++ct) {
+        f32x4 gk[4], gv[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) gk[dt] = gv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float er[16], ev[16];   // entry c16's pooled K and V rows (the same for the whole group)
+        bool loaded = false;
+        for (int jt = 0; jt < 4; ++jt) {
+            const int qt = G * kBlock + 4 * w + jt;
+            if (qt >= a.nt1) break;
+            const int ib = qt / a.sub;
+            const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
+            float bias;
+            const int64_t rk = coarse_row(ib, fine, ct * kBlock + c16, bias);
+            if (!loaded) {
+                const int64_t rks = rk < 0 ? 0 : rk;
+                load_row16(pk + rks + 16 * g, er);
+                load_row16(pv + rks + 16 * g, ev);
+                loaded = true;
+            }
+            const int64_t qoff = head_off + trow(qt, c16) + 16 * g;
+            float qf[16], gf[16];
+            load_row16(q + qoff, qf);
+            load_row16(dout + qoff, gf);
+            f32x4 qc[4], dc[4];
+            float l2[4], Dq[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t r = head_off + trow(qt, 4 * g + i) + 4 * c16;
+                qc[i] = *reinterpret_cast<const f32x4 *>(q + r);
+                dc[i] = *reinterpret_cast<const f32x4 *>(dout + r);
+                l2[i] = __shfl(L2v[jt], 4 * g + i, kWave);   // lane 4g + i holds query 4g + i
+                Dq[i] = __shfl(Dv[jt], 4 * g + i, kWave);
+            }
+            f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = s;
+#pragma unroll
+            for (int d = 0; d < 16; ++d) {
+                s = mfma_f32_4(qf[d], er[d], s);
+                dp = mfma_f32_4(gf[d], ev[d], dp);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = fast_exp2(s[i] * a.sl2 + bias - l2[i]);
+                const float ds = p * (dp[i] - Dq[i]);
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    gk[dt] = mfma_f32_4(qc[i][dt], ds, gk[dt]);
+                    gv[dt] = mfma_f32_4(dc[i][dt], p, gv[dt]);
+                }
             }
         }
+        // lane (g, c): dims 16g + 4j + dt of entry c
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            *reinterpret_cast<f32x4 *>(&red[w][0][c16 * kHeadDim + 16 * g + 4 * j]) =
+                f32x4{gk[0][j], gk[1][j], gk[2][j], gk[3][j]} * a.scale;
+            *reinterpret_cast<f32x4 *>(&red[w][1][c16 * kHeadDim + 16 * g + 4 * j]) =
+                f32x4{gv[0][j], gv[1][j], gv[2][j], gv[3][j]};
+        }
+        __syncthreads();
+        const int ne = min(kBlock, a.ncoarse - ct * kBlock);
+        float *part = ws.partial + (((int64_t)h * a.npg + G) * a.ncoarse + ct * kBlock) * 2 * kHeadDim;
+        for (int x = threadIdx.x; x < ne * 2 * kHeadDim; x += 256) {
+            const int e = x / (2 * kHeadDim), kv = (x / kHeadDim) & 1, dim = x % kHeadDim;
+            const int oo = e * kHeadDim + dim;
+            part[x] = red[0][kv][oo] + red[1][kv][oo] + red[2][kv][oo] + red[3][kv][oo];
+        }
+        __syncthreads();
     }
-    red[w][0][lane] = gk;
-    red[w][1][lane] = gv;
-    __syncthreads();
-    if (w != 0) return;
-    float sk = 0.f, sv = 0.f;
-    for (int x = 0; x < kCoarseWaves; ++x) {
-        sk += red[x][0][lane];
-        sv += red[x][1][lane];
-    }
-    ws.dpk[a.cl_grad_off[j] + ((int64_t)h * nl + c) * kHeadDim + lane] = sk * a.scale;
-    ws.dpv[a.cl_grad_off[j] + ((int64_t)h * nl + c) * kHeadDim + lane] = sv;
 }
 
-// Pass C (f32): one wave per key token.
+// Pass C (f32): one wave per 16-key tile on the matrix cores, walking the
+// query tiles of its key block's CSR segment.  Scores are computed query-major
+// here, S = Q K^T: lane (g, c) holds key c against queries 4g .. 4g + 3 of a
+// query tile, so P and dS feed dV^T += dO^T P and dK^T += Q^T dS straight from
+// the score registers, with dO and Q in the column layout; lane (g, c) ends
+// with dims 16g .. 16g + 15 of key c.
 __global__ __launch_bounds__(256) void bwd_dkv_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ lse, const float *__restrict__ dout, const int32_t *__restrict__ csr_ptr,
     const int32_t *__restrict__ csr_col, void *__restrict__ dk, void *__restrict__ dv, BwdWs ws,
     BwdArgs a) {
-    const int64_t tu = (int64_t)blockIdx.x * 4 + wave_id();
-    if (tu >= (int64_t)a.bh * a.N) return;
+    const int w = wave_id();
     const int lane = lane_id();
-    const int h = (int)(tu / a.N);
-    const int u = (int)(tu % a.N);
-    const int f = u / (kBlock * a.sub);   // key block
+    const int g = lane >> 4, c16 = lane & 15;
+    const int64_t kb = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + w;   // key tile
+    if (kb >= (int64_t)a.bh * a.nt1) return;
+    const int h = (int)(kb / a.nt1);
+    const int f = (int)(kb % a.nt1);
+    const int fb = f / a.sub;   // its key block
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
-    const int64_t row = head_off + (int64_t)tok_row(a.tm, u) * kHeadDim + lane;
-    const float kx = k[row], vx = v[row];
-    float gk = 0.f, gv = 0.f;
+    auto trow = [&](int b, int r) { return (int64_t)tok_row(a.tm, b * kBlock + r) * kHeadDim; };
+    const int64_t koff = head_off + trow(f, c16) + 16 * g;
+    float kf[16], vf[16];
+    load_row16(k + koff, kf);
+    load_row16(v + koff, vf);
     const int32_t *P = csr_ptr + (int64_t)h * (a.n1 + 1);
     const int32_t *C = csr_col + (int64_t)h * a.n1 * a.K1;
-    const int e0 = __builtin_amdgcn_readfirstlane(P[f]), e1 = __builtin_amdgcn_readfirstlane(P[f + 1]);
-    for (int et = e0 * a.sub; et < e1 * a.sub; ++et) {   // query tiles of the segment's blocks
+    const int e0 = __builtin_amdgcn_readfirstlane(P[fb]), e1 = __builtin_amdgcn_readfirstlane(P[fb + 1]);
+    f32x4 gk[4], gv[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) gk[dt] = gv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    struct QT {
+        float qr[16], dr[16];   // Q and dO row c (row layout)
+        f32x4 qc[4], dc[4];     // Q and dO rows 4g + i, dims 4c .. 4c + 3 (column layout)
+        float l2[4], Dv[4];     // lse * log2(e) and D of queries 4g + i
+    };
+    auto load_q = [&](int et, QT &X) {
         const int qt = __builtin_amdgcn_readfirstlane(C[et / a.sub]) * a.sub + et % a.sub;
-        float qx[kBlock], gx[kBlock];
-        int64_t srow[kBlock];
+        const int64_t rc = head_off + trow(qt, c16) + 16 * g;
+        load_row16(q + rc, X.qr);
+        load_row16(dout + rc, X.dr);
 #pragma unroll
-        for (int tt = 0; tt < kBlock; ++tt) {
-            srow[tt] = tok_row(a.tm, qt * kBlock + tt);
-            qx[tt] = q[head_off + srow[tt] * kHeadDim + lane];
-            gx[tt] = dout[head_off + srow[tt] * kHeadDim + lane];
+        for (int i = 0; i < 4; ++i) {
+            const int pos = qt * kBlock + 4 * g + i;
+            const int64_t srow = tok_row(a.tm, pos);
+            X.qc[i] = *reinterpret_cast<const f32x4 *>(q + head_off + srow * kHeadDim + 4 * c16);
+            X.dc[i] = *reinterpret_cast<const f32x4 *>(dout + head_off + srow * kHeadDim + 4 * c16);
+            X.l2[i] = lse[(int64_t)h * a.N + srow] * kLog2e;
+            X.Dv[i] = ws.D[(int64_t)h * a.N + pos];
+        }
+    };
+    auto visit = [&](const QT &X) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = s;
+#pragma unroll
+        for (int d = 0; d < 16; ++d) {
+            s = mfma_f32_4(X.qr[d], kf[d], s);
+            dp = mfma_f32_4(X.dr[d], vf[d], dp);
         }
 #pragma unroll
-        for (int tt = 0; tt < kBlock; ++tt) {
-            const int64_t tok = (int64_t)h * a.N + (int64_t)qt * kBlock + tt;
-            const float s = wave_sum(qx[tt] * kx);
-            const float dp = wave_sum(gx[tt] * vx);
-            const float p = exp2f(s * a.sl2 - lse[(int64_t)h * a.N + srow[tt]] * kLog2e);
-            gk = fmaf(p * (dp - ws.D[tok]), qx[tt], gk);
-            gv = fmaf(p, gx[tt], gv);
+        for (int i = 0; i < 4; ++i) {
+            const float p = fast_exp2(s[i] * a.sl2 - X.l2[i]);
+            const float ds = p * (dp[i] - X.Dv[i]);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                gv[dt] = mfma_f32_4(X.dc[i][dt], p, gv[dt]);
+                gk[dt] = mfma_f32_4(X.qc[i][dt], ds, gk[dt]);
+            }
         }
+    };
+    QT X;
+    for (int et = e0 * a.sub; et < e1 * a.sub; ++et) {   // query tiles of the segment's blocks
+        load_q(et, X);
+        visit(X);
     }
-    gk *= a.scale;
+    // pooled-level gradients, spread back with weight 1/B^l (dims 16g + 4j .. + 3)
+    f32x4 ck[4], cv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ck[j] = cv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     float inv = 1.f;
-    for (int j = 0; j < a.ncl; ++j) {
+    for (int jl = 0; jl < a.ncl; ++jl) {
         inv *= a.invB;
-        const int c = f / a.cl_span[j];
-        const int64_t off = a.cl_grad_off[j] + ((int64_t)h * a.cl_n[j] + c) * kHeadDim + lane;
-        gk += ws.dpk[off] * (inv * a.invB);
-        gv += ws.dpv[off] * (inv * a.invB);
+        const int64_t off = a.cl_grad_off[jl] + ((int64_t)h * a.cl_n[jl] + fb / a.cl_span[jl]) * kHeadDim + 16 * g;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            ck[j] += *reinterpret_cast<const f32x4 *>(ws.dpk + off + 4 * j) * (inv * a.invB);
+            cv[j] += *reinterpret_cast<const f32x4 *>(ws.dpv + off + 4 * j) * (inv * a.invB);
+        }
     }
-    store_grad1(dk, row, gk, a.grad_bf16);
-    store_grad1(dv, row, gv, a.grad_bf16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        store_grad4(dk, koff + 4 * j, f32x4{gk[0][j], gk[1][j], gk[2][j], gk[3][j]} * a.scale + ck[j], a.grad_bf16);
+        store_grad4(dv, koff + 4 * j, f32x4{gv[0][j], gv[1][j], gv[2][j], gv[3][j]} + cv[j], a.grad_bf16);
+    }
 }
 
 hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, const void *v,
@@ -1711,17 +1823,17 @@ hipError_t launch_attn_bwd(const Geometry &g, const void *q, const void *k, cons
                                csr_ptr + g.ptr_off[1], csr_col + g.col_off[1], dk, dv, ws, a);
         }
     } else {
-        const int64_t total = (int64_t)g.bh * g.N;
-        hipLaunchKernelGGL(bwd_dq_f32_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s,
+        const int64_t tiles = (int64_t)g.bh * a.nt1;   // query tiles = key tiles
+        const int64_t groups = (int64_t)g.bh * ((a.nt1 + kBlock - 1) / kBlock);
+        hipLaunchKernelGGL(bwd_dq_f32_kernel, dim3((unsigned)groups), dim3(256), 0, s,
                            (const float *)q, (const float *)k, (const float *)v, pk, pv, idx,
                            (const float *)o, lse, (const float *)dout, dq, ws, a);
         for (int j = 0; j < a.ncl; ++j) {
-            const int64_t nt = (int64_t)g.bh * a.cl_n[j];
-            hipLaunchKernelGGL(bwd_coarse_f32_kernel, dim3((unsigned)nt), dim3(kCoarseWaves * kWave), 0,
-                               s, (const float *)q, pk, pv, idx, lse, (const float *)dout, csr_ptr,
-                               csr_col, ws, a, j);
+            const int64_t toks = (int64_t)g.bh * a.cl_n[j];
+            hipLaunchKernelGGL(bwd_coarse_reduce_kernel, dim3((unsigned)((toks + 3) / 4)),
+                               dim3(256), 0, s, idx, csr_ptr, csr_col, ws, a, j);
         }
-        hipLaunchKernelGGL(bwd_dkv_f32_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0,
+        hipLaunchKernelGGL(bwd_dkv_f32_kernel, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0,
                            s, (const float *)q, (const float *)k, (const float *)v, lse,
                            (const float *)dout, csr_ptr + g.ptr_off[1], csr_col + g.col_off[1], dk,
                            dv, ws, a);

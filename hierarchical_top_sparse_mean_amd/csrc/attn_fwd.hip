@@ -827,55 +827,119 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_b64_kernel(
 }
 
 // ---------------------------------------------------------------- f32 path
+// Float32 inputs on the matrix cores (v_mfma_f32_16x16x4_f32): one wave per
+// 16-query tile, any block size, fine-tile count and number of coarse tiles,
+// and no LDS.  Scores are computed transposed, S^T = K Q^T, so lane (g, c)
+// holds query c against keys 4g .. 4g + 3 of a key tile; Q and K come in the
+// row layout (load_row16).  O^T += V^T P^T takes P straight from the score
+// registers: step i of a key tile pairs key 4g + i of lane group g with the
+// V rows in the column layout (lane (g, c): dims 4c .. 4c + 3 of row 4g + i,
+// four whole rows per load instruction), and output row r of dim chunk dt
+// stands for dim 4r + dt, so that lane (g, c) ends with dims 16g .. 16g + 15
+// of query c.  The softmax runs online, key tile by key tile.
 __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ pk, const float *__restrict__ pv, const int32_t *__restrict__ idx,
     float *__restrict__ o, float *__restrict__ lse, FwdArgs a) {
-    const int64_t tq = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (tq >= (int64_t)a.bh * a.N) return;
-    const int h = (int)(tq / a.N);
-    const int tok = (int)(tq % a.N);
-    const int bsz = a.sub * kBlock;   // B
-    const int ib = tok / bsz;
+    const int w = wave_id();
+    const int lane = lane_id();
+    const int g = lane >> 4, c16 = lane & 15;
+    const int64_t blk = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + w;   // query tile
+    if (blk >= (int64_t)a.bh * a.nt1) return;
+    const int h = (int)(blk / a.nt1);
+    const int qt = (int)(blk % a.nt1);
+    const int ib = qt / a.sub;   // its query block
     const int64_t head_off = (int64_t)h * a.N * kHeadDim;
-    float qv[kHeadDim], acc[kHeadDim];
-#pragma unroll
-    for (int e = 0; e < kHeadDim; ++e) {
-        qv[e] = q[head_off + (int64_t)tok_row(a.tm, tok) * kHeadDim + e];
-        acc[e] = 0.f;
-    }
-    float m = -INFINITY, l = 0.f;
-    auto attend = [&](const float *kr, const float *vr, float bias) {
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < kHeadDim; ++e) s = fmaf(qv[e], kr[e], s);
-        const float z = s * a.sl2 + bias;
-        const float mn = fmaxf(m, z);
-        const float alpha = exp2f(m - mn);
-        const float p = exp2f(z - mn);
-        l = l * alpha + p;
-#pragma unroll
-        for (int e = 0; e < kHeadDim; ++e) acc[e] = acc[e] * alpha + p * vr[e];
-        m = mn;
-    };
+    const float *kh = k + head_off;
+    const float *vh = v + head_off;
+    // element offset (within the head) of row r of 16-token tile b
+    auto trow = [&](int b, int r) { return (int64_t)tok_row(a.tm, b * kBlock + r) * kHeadDim; };
+    float qf[16];
+    load_row16(q + head_off + trow(qt, c16) + 16 * g, qf);
     const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;
-    for (int j = 0; j < a.K1; ++j) {
-        const int f = fine[j];
-        for (int t = 0; t < bsz; ++t) {
-            const int64_t u = tok_row(a.tm, f * bsz + t);
-            attend(k + head_off + u * kHeadDim, v + head_off + u * kHeadDim, 0.f);
-        }
-    }
-    for (int e = 0; e < a.ncoarse; ++e) {
-        int64_t roff;
-        float b;
-        if (coarse_entry(a, idx, fine, h, ib, e, roff, b)) attend(pk + roff, pv + roff, b);
-    }
-    const float inv = 1.0f / l;
-    const int64_t orow = (int64_t)tok_row(a.tm, tok);
+    const int nft = a.K1 * a.sub;   // fine key tiles: sub-tile t % sub of pick t / sub
+    const int nct = (a.ncoarse + kBlock - 1) / kBlock;
+
+    float m = -INFINITY, lsum = 0.f;
+    f32x4 oacc[4];
 #pragma unroll
-    for (int e = 0; e < kHeadDim; ++e) o[head_off + orow * kHeadDim + e] = acc[e] * inv;
-    lse[(int64_t)h * a.N + orow] = (m + log2f(l)) * kLn2;
+    for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    struct KV {
+        float kr[16];   // K row c (row layout)
+        f32x4 vc[4];    // V rows 4g + i, dims 4c .. 4c + 3 (column layout)
+    };
+    auto load_fine = [&](int tt, KV &T) {
+        const int f = __builtin_amdgcn_readfirstlane(fine[tt / a.sub]) * a.sub + tt % a.sub;
+        load_row16(kh + trow(f, c16) + 16 * g, T.kr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) T.vc[i] = *reinterpret_cast<const f32x4 *>(vh + trow(f, 4 * g + i) + 4 * c16);
+    };
+    // one key tile; bias: log2 weight of keys 4g + i (-inf masks a key)
+    auto attend = [&](const KV &T, const float (&bias)[4]) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int d = 0; d < 16; ++d) s = mfma_f32_4(T.kr[d], qf[d], s);
+        float z[4], mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            z[i] = s[i] * a.sl2 + bias[i];
+            mx = fmaxf(mx, z[i]);
+        }
+        mx = max4_groups(mx);
+        const float mnew = fmaxf(m, mx);
+        const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
+        const float alpha = fast_exp2(m - msafe);
+        m = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p = fast_exp2(z[i] - msafe);
+            lsum += p;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) oacc[dt] = mfma_f32_4(T.vc[i][dt], p, oacc[dt]);
+        }
+    };
+    // ---- fine key tiles, weight 1: two register sets, the next tile's loads
+    // in flight while a tile is computed
+    const float nobias[4] = {0.f, 0.f, 0.f, 0.f};
+    KV T0, T1;
+    if (nft > 0) load_fine(0, T0);
+    for (int tt = 0; tt < nft; tt += 2) {
+        if (tt + 1 < nft) load_fine(tt + 1, T1);
+        attend(T0, nobias);
+        if (tt + 2 < nft) load_fine(tt + 2, T0);
+        if (tt + 1 < nft) attend(T1, nobias);
+    }
+    // ---- coarse tokens of levels 2..ncl+1, weight B^l, 16 entries a tile;
+    // absent or dropped entries read row 0 of the pyramid and are masked
+    for (int ct = 0; ct < nct; ++ct) {
+        KV T;
+        float bias[4];
+        int64_t roff = 0;
+        float bb;
+        const bool okk = coarse_entry(a, idx, fine, h, ib, ct * kBlock + c16, roff, bb);
+        load_row16(pk + (okk ? roff : 0) + 16 * g, T.kr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int64_t ri = 0;
+            float bi = 0.f;
+            const bool ok = coarse_entry(a, idx, fine, h, ib, ct * kBlock + 4 * g + i, ri, bi);
+            T.vc[i] = *reinterpret_cast<const f32x4 *>(pv + (ok ? ri : 0) + 4 * c16);
+            if (!ok) T.vc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            bias[i] = ok ? bi : -INFINITY;
+        }
+        attend(T, bias);
+    }
+    // ---- normalise and store: lane (g, c) writes dims 16g .. 16g + 15 of query c
+    lsum = sum4_groups(lsum);
+    const float inv = 1.0f / lsum;
+    float *orow = o + head_off + trow(qt, c16) + 16 * g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4 *>(orow + 4 * j) = f32x4{oacc[0][j], oacc[1][j], oacc[2][j], oacc[3][j]} * inv;
+    if (g == 0) lse[(int64_t)h * a.N + tok_row(a.tm, qt * kBlock + c16)] = (m + log2f(lsum)) * kLn2;
 }
 
 hipError_t launch_attn_fwd(const Geometry &g, const void *q, const void *k, const void *v,
@@ -921,8 +985,8 @@ hipError_t launch_attn_fwd(const Geometry &g, const void *q, const void *k, cons
                                s, (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, pk, pv, idx,
                                (__bf16 *)o, lse, a);
     } else {
-        const int64_t total = (int64_t)g.bh * g.N;
-        hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+        const int64_t tiles = (int64_t)g.bh * a.nt1;
+        hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0,
                            s, (const float *)q, (const float *)k, (const float *)v, pk, pv, idx,
                            (float *)o, lse, a);
     }

@@ -38,6 +38,20 @@ __device__ __forceinline__ f32x4 mfma_bf16_16(bf16x4 a, bf16x4 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma_f32_4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+// Float32 operands of the 16 x 16 x 4 product straight from memory.  Row
+// layout: lane (g = l / 16, c = l % 16) takes dims 16g .. 16g + 15 of its own
+// row (64 contiguous bytes), so step d of a 16-step product over the head
+// dimension covers dims d, 16 + d, 32 + d and 48 + d in the four lane groups.
+// (The column layout, lane (g, c) holding dims 4c .. 4c + 3 of rows 4g + i,
+// is one 16-byte load per row and needs no helper.)
+__device__ __forceinline__ void load_row16(const float *p, float (&x)[16]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const f32x4 t = reinterpret_cast<const f32x4 *>(p)[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * j + e] = t[e];
+    }
+}
 
 // Transposing LDS read of 4 bf16: within each 16-lane group, lane i receives
 // element i%4 of the 8-byte chunks addressed by lanes i/4, i/4+4, i/4+8, i/4+12.

@@ -75,6 +75,9 @@ EDGE = [
     (1, 2, 16384, torch.bfloat16, 2, 32, 1, True, {}),     # 32 coarse entries: 2 coarse tiles
     (1, 2, 8192, torch.bfloat16, 3, 16, 2, True, {}),      # 16 + 2 coarse entries: 2 coarse tiles
     (1, 1, 2048, torch.float32, 2, 24, 1, True, {}),
+    (1, 4, 16384, torch.float32, 2, 8, 1, True, {}),        # float32 matrix-core path at size
+    (1, 2, 16384, torch.float32, 2, 32, 1, True, {}),       # float32, 32 coarse entries: 2 tiles
+    (1, 2, 2048, torch.float32, 2, 4, 1, True, {"grad_dtype": torch.bfloat16}),
     (1, 2, 4096, torch.bfloat16, 2, 3, 1, True, {"drop_covered": False}),
     (2, 2, 2048, torch.bfloat16, 2, 4, 1, True, {"grad_dtype": torch.bfloat16}),
     (1, 2, 4096, torch.bfloat16, 2, 8, 1, True, {"token_order": 1}),   # 2D patch order

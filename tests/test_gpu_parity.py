@@ -154,10 +154,11 @@ def test_constant_values_give_that_value():
     assert np.abs(g["o"] - vals.double().numpy()).max() <= 2e-2
 
 
-def test_deterministic_bitwise():
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_deterministic_bitwise(dtype):
     # two runs of the whole path give identical bytes (no float atomics)
-    _log("[parity] determinism")
-    c = Case(1, 4, 4096, torch.bfloat16, 2, 8, 1, backward=True, sinus=True)
+    _log(f"[parity] determinism {dtype}")
+    c = Case(1, 4, 4096, dtype, 2, 8, 1, backward=True, sinus=True)
     a = run_gpu(c)
     b = run_gpu(c)
     for key in ("o", "lse", "dq", "dk", "dv"):

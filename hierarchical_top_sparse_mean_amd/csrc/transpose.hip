@@ -308,8 +308,9 @@ __global__ __launch_bounds__(kTrThreads) void tr_bounds_kernel(const int32_t *__
 
 // Matrices of at most kTrOneMaxPicks picks and kTrOneMaxCols keys: the whole
 // transpose in one launch.  Workgroup (part, b) owns keys [512 part, 512 part
-// + 512) of matrix b and reads every pick of the matrix (from L2: each pick
-// is read by cols / 512 workgroups).  Every workgroup scans all the picks of
+// + 512) of matrix b and reads every pick of the matrix; the parts of one
+// matrix run side by side on one XCD, so that all but the first read of a
+// pick come from that XCD's L2.  Every workgroup scans all the picks of
 // its matrix, so fewer, wider parts do less work in total; 512 keys keep the
 // per-slice counters and masks at 96 KB of LDS (128 KB with the part's
 // queue), one workgroup per CU, and the levels of a 65536-token problem in
@@ -359,7 +360,10 @@ struct TrOneArgs {
 };
 
 __global__ __launch_bounds__(kTrOneThreads) void tr_one_kernel(TrOneArgs A) {
-    int mi = 0, part = blockIdx.x;
+    // the parts of one matrix side by side on one XCD (workgroup L runs on XCD L % 8)
+    const int lin = xcd_remap((int)(blockIdx.x + gridDim.x * blockIdx.y), (int)(gridDim.x * gridDim.y));
+    const int b = lin / (int)gridDim.x;
+    int mi = 0, part = lin % (int)gridDim.x;
     while (mi + 1 < A.nmat && part >= A.m[mi].parts) part -= A.m[mi++].parts;
     const int32_t *__restrict__ idx = A.m[mi].idx;
     int32_t *__restrict__ ptr = A.m[mi].ptr;
@@ -371,7 +375,6 @@ __global__ __launch_bounds__(kTrOneThreads) void tr_one_kernel(TrOneArgs A) {
     __shared__ int32_t below_w[kTrOneWaves];
     __shared__ int32_t inr_w[kTrOneWaves];
     __shared__ int32_t scan_w[kTrOneKeys / kWave];
-    const int b = blockIdx.y;
     const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
     const uint64_t lower = (1ull << lane) - 1ull;
     const int c0 = part * kTrOneKeys, nk = min(kTrOneKeys, cols - c0);

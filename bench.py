@@ -56,8 +56,8 @@ def algorithmic(w, s):
         tr += bh * n[l] * kl[l] * 4 + bh * (n[l] + 1) * 4 + bh * n[l] * kl[l] * 4
     out["transpose"] = dict(bytes=tr, flops=0)
     g = 4  # float32 gradients
-    # the survey's definition: Q, K, V, O, dO read, dQ, dK, dV written, LSE and D
-    # once each.  The kernels never read O (D = sum P dP comes out of the dQ
+    # the compulsory bytes of the backward: Q, K, V, O, dO read, dQ, dK, dV
+    # written, LSE and D once each.  The kernels never read O (D = sum P dP comes out of the dQ
     # pass), but read the coarse pyramids, the pick lists and the CSR and read
     # D back: "bytes_kernel_inputs".
     out["attn_bwd"] = dict(bytes=5 * tok + 3 * bh * N * d * g + 2 * bh * N * 4,

@@ -473,8 +473,10 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast_kernel(
 // ---------------------------------------------------------- chunked path
 // The fast path's loads and layout for other shapes (B = 16): any K_1 (fine
 // tiles in chunks of 8, the last chunk masked), with a shared coarse tile of at
-// most 16 entries (CO) or none (no enrichment).  The coarse tile goes first,
-// then every chunk updates the running max and rescales (online softmax).
+// most 16 entries (CO) or none (no enrichment).  Every chunk updates the
+// running max and rescales (online softmax); the coarse tile comes last.  The
+// next chunk's K rows go out half by half as the chunk's V halves are staged,
+// and its V rows once the chunk's P V is done, so the loads overlap the work.
 // Several chunks need the registers of two waves per SIMD.
 template <int NCH, bool CO, int ORD>
 __global__ __launch_bounds__(256, NCH == 1 ? 3 : 2) void attn_fwd_chunk_kernel(
@@ -508,24 +510,27 @@ __global__ __launch_bounds__(256, NCH == 1 ? 3 : 2) void attn_fwd_chunk_kernel(
         store_bf16x8(dst + (lr + 8) * kVStride + lc, r1);
     };
     // Loads go out in the order they are used (the memory counter is waited
-    // on in order): Q, the coarse entry's pick, with a single chunk its K then
-    // V tiles, the coarse pyramid rows.  Several chunks load in turn (their
-    // registers would not also fit across the coarse part).
+    // on in order): Q, the coarse entry's pick, the first chunk's K then V
+    // tiles, the coarse pyramid rows.
     const int32_t *fine = idx + blk * a.K1;
     bf16x8 kr[KT][2], vr[KT][2];
-    auto load_chunk = [&](int c0) {
-        const int nt = min(KT, a.K1 - c0);
-        int fp[KT];
+    auto chunk_tile = [&](int c0, int t) {   // tiles past the chunk's end re-read its last tile
+        return __builtin_amdgcn_readfirstlane(fine[c0 + min(t, min(KT, a.K1 - c0) - 1)]);
+    };
+    auto load_k = [&](int c0, int t0, int t1) {   // tiles t0 .. t1 - 1
 #pragma unroll
-        for (int t = 0; t < KT; ++t) {
-            fp[t] = __builtin_amdgcn_readfirstlane(fine[c0 + min(t, nt - 1)]);
-            kr[t][0] = load_bf16x8(kh + trow(fp[t], lr) + lc);
-            kr[t][1] = load_bf16x8(kh + trow(fp[t], lr + 8) + lc);
+        for (int t = t0; t < t1; ++t) {
+            const int f = chunk_tile(c0, t);
+            kr[t][0] = load_bf16x8(kh + trow(f, lr) + lc);
+            kr[t][1] = load_bf16x8(kh + trow(f, lr + 8) + lc);
         }
+    };
+    auto load_v = [&](int c0) {
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
-            vr[t][0] = load_bf16x8(vh + trow(fp[t], lr) + lc);
-            vr[t][1] = load_bf16x8(vh + trow(fp[t], lr + 8) + lc);
+            const int f = chunk_tile(c0, t);
+            vr[t][0] = load_bf16x8(vh + trow(f, lr) + lc);
+            vr[t][1] = load_bf16x8(vh + trow(f, lr + 8) + lc);
         }
     };
     const bf16x8 qr0 = load_bf16x8_nt(q + head_off + trow(ib, lr) + lc);
@@ -540,7 +545,8 @@ __global__ __launch_bounds__(256, NCH == 1 ? 3 : 2) void attn_fwd_chunk_kernel(
         const int anc = ib0 >> (4 * (cj + 1));   // ancestor at level cj+2
         cc = idx[a.cl_idx_off[cj] + ((int64_t)h * a.cl_n[cj] + anc) * a.cl_k[cj] + cpick];
     }
-    if constexpr (NCH == 1) load_chunk(0);
+    load_k(0, 0, KT);
+    load_v(0);
     f32x4 ckk = {0.f, 0.f, 0.f, 0.f}, cvv = ckk;
     if constexpr (CO) {
         const int64_t row = a.cl_pyr_off[cj] + ((int64_t)h * a.cl_n[cj] + cc) * kHeadDim + 4 * cpart;
@@ -556,50 +562,10 @@ __global__ __launch_bounds__(256, NCH == 1 ? 3 : 2) void attn_fwd_chunk_kernel(
     wave_lds_sync();
     const bf16x8 qa0 = load_bf16x8(qw + c16 * kVStride + 8 * g);
     const bf16x8 qa1 = load_bf16x8(qw + c16 * kVStride + 32 + 8 * g);
-    if constexpr (CO) {
-        // coarse tile, staged by the whole workgroup: thread (entry e, quarter p)
-        if (!cok) ckk = cvv = f32x4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<u32x2 *>(&ck[ce * kVStride + 4 * cpart]) = __builtin_bit_cast(u32x2, to_bf16x4(ckk));
-        *reinterpret_cast<u32x2 *>(&cv[ce * kVStride + 4 * cpart]) = __builtin_bit_cast(u32x2, to_bf16x4(cvv));
-        if (cpart == 0) cbias[ce] = cok ? 4.0f * (float)(cj + 2) : -INFINITY;
-        __syncthreads();
-        const __bf16 *ckr = ck + c16 * kVStride;
-        f32x4 sc = mfma_bf16_32(load_bf16x8(ckr + 32 + 8 * g), qa1,
-                                mfma_bf16_32(load_bf16x8(ckr + 8 * g), qa0, f32x4{0.f, 0.f, 0.f, 0.f})) * a.sl2;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sc[i] += cbias[4 * g + i];
-            if (drop_possible(a)) {
-                // a level-2 pick whose 16 children are all fine picks of this
-                // block is dropped for it (only level 2 can be covered: K_1 <= 32)
-                int j2, p2;
-                if (coarse_locate(a, 4 * g + i, j2, p2) && j2 == 0) {
-                    const int c = idx[a.cl_idx_off[0] + ((int64_t)h * a.cl_n[0] + (ib >> 4)) * a.cl_k[0] + p2];
-                    int cov = 0;
-                    for (int f = 0; f < a.K1; ++f) cov += (fine[f] >> 4) == c ? 1 : 0;
-                    if (cov == kBlock) sc[i] = -INFINITY;
-                }
-            }
-            mx = fmaxf(mx, sc[i]);
-        }
-        m = max4_groups(mx);
-        const float ms = m == -INFINITY ? 0.f : m;   // every entry absent or dropped
-        float pc[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pc[i] = fast_exp2(sc[i] - ms);
-            lsum += pc[i];
-        }
-        const bf16x4 pcb = to_bf16x4(f32x4{pc[0], pc[1], pc[2], pc[3]});
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-            oacc[dt] = mfma_bf16_16(lds_read_tr4(cv + rofs + 16 * dt), pcb, oacc[dt]);
-    }
 #pragma unroll 1
     for (int c0 = 0; c0 < NCH * KT; c0 += KT) {
         const int nt = min(KT, a.K1 - c0);   // live tiles of this chunk (>= 1)
-        if (NCH > 1 || c0 > 0) load_chunk(c0);
+        const bool more = c0 + KT < a.K1;    // another chunk follows
         f32x4 st[KT];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -635,6 +601,8 @@ __global__ __launch_bounds__(256, NCH == 1 ? 3 : 2) void attn_fwd_chunk_kernel(
 #pragma unroll
             for (int t = 0; t < kHalf; ++t)
                 stage_rows(vw + t * kTileElems, vr[half * kHalf + t][0], vr[half * kHalf + t][1]);
+            // this half of the V rows is staged: the next chunk's K rows of the same half go out
+            if (more) load_k(c0 + KT, half * kHalf, (half + 1) * kHalf);
             wave_lds_sync();
 #pragma unroll
             for (int tp = 0; tp < kHalf / 2; ++tp) {
@@ -656,6 +624,51 @@ __global__ __launch_bounds__(256, NCH == 1 ? 3 : 2) void attn_fwd_chunk_kernel(
                 }
             }
         }
+        if (more) load_v(c0 + KT);
+    }
+    if constexpr (CO) {
+        // coarse tile, staged by the whole workgroup: thread (entry e, quarter p)
+        if (!cok) ckk = cvv = f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<u32x2 *>(&ck[ce * kVStride + 4 * cpart]) = __builtin_bit_cast(u32x2, to_bf16x4(ckk));
+        *reinterpret_cast<u32x2 *>(&cv[ce * kVStride + 4 * cpart]) = __builtin_bit_cast(u32x2, to_bf16x4(cvv));
+        if (cpart == 0) cbias[ce] = cok ? 4.0f * (float)(cj + 2) : -INFINITY;
+        __syncthreads();
+        const __bf16 *ckr = ck + c16 * kVStride;
+        f32x4 sc = mfma_bf16_32(load_bf16x8(ckr + 32 + 8 * g), qa1,
+                                mfma_bf16_32(load_bf16x8(ckr + 8 * g), qa0, f32x4{0.f, 0.f, 0.f, 0.f})) * a.sl2;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sc[i] += cbias[4 * g + i];
+            if (drop_possible(a)) {
+                // a level-2 pick whose 16 children are all fine picks of this
+                // block is dropped for it (only level 2 can be covered: K_1 <= 32)
+                int j2, p2;
+                if (coarse_locate(a, 4 * g + i, j2, p2) && j2 == 0) {
+                    const int c = idx[a.cl_idx_off[0] + ((int64_t)h * a.cl_n[0] + (ib >> 4)) * a.cl_k[0] + p2];
+                    int cov = 0;
+                    for (int f = 0; f < a.K1; ++f) cov += (fine[f] >> 4) == c ? 1 : 0;
+                    if (cov == kBlock) sc[i] = -INFINITY;
+                }
+            }
+            mx = fmaxf(mx, sc[i]);
+        }
+        const float mnew = fmaxf(m, max4_groups(mx));   // finite: the fine tiles came first
+        const float alpha = fast_exp2(m - mnew);
+        m = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
+        float pc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pc[i] = fast_exp2(sc[i] - m);
+            lsum += pc[i];
+        }
+        const bf16x4 pcb = to_bf16x4(f32x4{pc[0], pc[1], pc[2], pc[3]});
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            oacc[dt] = mfma_bf16_16(lds_read_tr4(cv + rofs + 16 * dt), pcb, oacc[dt]);
     }
     // ---- normalise and store (whole rows through the free V slot)
     lsum = sum4_groups(lsum);

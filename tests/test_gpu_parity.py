@@ -89,6 +89,7 @@ EDGE = [
     # blocks of 64 tokens (4 MFMA tiles per block)
     (1, 2, 8192, torch.bfloat16, 1, 8, 0, True, {"block": 64}),     # single level, 128 blocks
     (1, 2, 64 * 37, torch.bfloat16, 1, 5, 0, True, {"block": 64}),  # 37 blocks: ragged tile groups
+    (1, 2, 64 * 37, torch.float32, 1, 5, 0, True, {"block": 64}),   # float32, ragged last tile group
     (1, 2, 16384, torch.bfloat16, 2, 8, 1, True, {"block": 64}),    # 16384 -> 256 -> 4
     (1, 2, 8192, torch.float32, 2, 2, 1, True, {"block": 64}),
     (1, 1, 2048, torch.bfloat16, 1, 32, 0, True, {"block": 64}),    # K = all 32 blocks

@@ -23,8 +23,8 @@ def _log(msg):
     sys.stdout.flush()
 
 
-def _both(b, h, N, L_, K, Le, grad_dtype=torch.float32):
-    c = Case(b, h, N, torch.bfloat16, L_, K, Le, backward=True, sinus=round(N ** 0.5) ** 2 == N,
+def _both(b, h, N, L_, K, Le, grad_dtype=torch.float32, dtype=torch.bfloat16):
+    c = Case(b, h, N, dtype, L_, K, Le, backward=True, sinus=round(N ** 0.5) ** 2 == N,
              grad_dtype=grad_dtype)
     q, k, v, do = c.q.cuda(), c.k.cuda(), c.v.cuda(), c.dout.cuda()
     B = L.Buffers(c.p, backward=True)
@@ -54,6 +54,8 @@ def test_noalloc_backward_matches_workspace_backward_twice():
     _both(2, 4, 16384, 2, 8, 1, torch.bfloat16)
     _log("[no-alloc] 1x2x8192 three levels")
     _both(1, 2, 8192, 3, 4, 2)
+    _log("[no-alloc] 1x4x16384 float32 inputs")
+    _both(1, 4, 16384, 2, 8, 1, dtype=torch.float32)
 
 
 def test_noalloc_rejects_problems_beyond_the_scratch():

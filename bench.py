@@ -12,6 +12,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import statistics
 import math
 import os
 import sys
@@ -186,7 +187,7 @@ def oracle_leg(w, g):
 def time_workload(L, w, steps, warmup, dev, grad_bf16=False, token_order=0, overlap=False):
     """Runs `warmup` untimed and `steps` timed steps of the whole path on
     workload `w` (inputs resident on the GPU); returns the inputs, problem,
-    buffers, sizes, the mean per-call milliseconds (HIP events on the stream
+    buffers, sizes, the median per-call milliseconds (HIP events on the stream
     each call runs on) and the wall-clock milliseconds per step.  overlap: the
     index transposes, which only the backward reads, run on a second stream
     (default priority) concurrently with the forward attention."""
@@ -250,7 +251,8 @@ def time_workload(L, w, steps, warmup, dev, grad_bf16=False, token_order=0, over
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / steps
-    per_call = {c: sum(events[i][c][0].elapsed_time(events[i][c][1]) for i in range(steps)) / steps
+    # the median over the timed steps of each call's HIP-event time
+    per_call = {c: statistics.median(events[i][c][0].elapsed_time(events[i][c][1]) for i in range(steps))
                 for c in calls}
     return q, k, v, dout, p, B, s, per_call, ms_per_step
 

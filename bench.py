@@ -297,8 +297,8 @@ def sweep_workloads():
     """The workload table plus the variations the scaling study asks for, all
     at the 65536-token shape unless named otherwise: more pooling steps,
     no enrichment, wider selection, single-level selection (quadratic in the
-    number of blocks), blocks of 64 tokens, bfloat16 gradients and the 2D
-    patch order."""
+    number of blocks), blocks of 64 tokens, bfloat16 gradients, and the 2D
+    patch order at every image size."""
     from dataclasses import replace
     from hierarchical_top_sparse_mean_amd.inputs import WORKLOADS
     base = WORKLOADS["n65536_bf16"]
@@ -314,7 +314,11 @@ def sweep_workloads():
         (replace(base, name="n65536_B64_L1_K8", block=64, levels=1, enrich=0), ""),
         (replace(base, name="n65536_B64_L2_K8", block=64, levels=2, enrich=1), ""),
         (base, "grad_bf16"),
-        (base, "patch_order"),   # the image tokens read as nested 2D patches
+        # the image tokens read as nested 2D patches, at every image size of the table
+        (WORKLOADS["n4096_bf16"], "patch_order"),
+        (WORKLOADS["n16384_bf16"], "patch_order"),
+        (base, "patch_order"),
+        (WORKLOADS["n262144_bf16"], "patch_order"),
     ]
     return out
 

@@ -59,7 +59,7 @@ int make_geometry(const llsa_problem *p, Geometry *g, llsa_sizes *sz) {
     if (p->head_dim != 64 || (p->block != 16 && p->block != 64)) return LLSA_ERR_UNSUPPORTED;
     if (p->topk > 32) return LLSA_ERR_UNSUPPORTED;
     // kernels address one head's rows with 32-bit byte offsets (seq_len * 128 B < 4 GiB)
-    if (p->seq_len > (1 << 25)) return LLSA_ERR_UNSUPPORTED;
+    if (p->seq_len >= (1 << 25)) return LLSA_ERR_UNSUPPORTED;
     const int64_t bh = (int64_t)p->batch * p->heads;
     if (bh * p->seq_len * p->head_dim >= ((int64_t)1 << 40) || bh * p->seq_len >= ((int64_t)1 << 31) ||
         bh > (1 << 30))

@@ -37,7 +37,7 @@
  *    returns LLSA_ERR_INDEX, with nothing else launched, when they are
  *    invalid.
  *  - Supported set: head_dim = 64, block = 16 or 64, 1 <= levels <= 6,
- *    1 <= topk <= 32, seq_len <= 2^25, batch * heads * seq_len < 2^31, dtype
+ *    1 <= topk <= 32, seq_len < 2^25, batch * heads * seq_len < 2^31, dtype
  *    LLSA_F32 or LLSA_BF16, non-causal.  Other values give
  *    LLSA_ERR_UNSUPPORTED.
  */

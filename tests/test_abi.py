@@ -87,6 +87,7 @@ def test_picks_clamped_to_candidates():
     (dict(token_order=1, seq_len=2048), L.LLSA_ERR_INVALID),    # not a square image
     (dict(levels=7, seq_len=16 ** 5), L.LLSA_ERR_UNSUPPORTED),
     (dict(heads=1, seq_len=1 << 26), L.LLSA_ERR_UNSUPPORTED),    # one head beyond 2^25 tokens
+    (dict(heads=1, seq_len=1 << 25), L.LLSA_ERR_UNSUPPORTED),    # 2^25 tokens: 4 GiB per head
 ])
 def test_sizes_query_rejects(kw, status):
     args = dict(batch=1, heads=2, seq_len=4096, levels=2, topk=8)

@@ -2,11 +2,12 @@
 // ("Trainable Log-linear Sparse Attention for Efficient Diffusion
 // Transformers", explainer "Step 1: Hierarchical Compression").
 //
-// A streaming, HBM-bound pass.  One 256-thread workgroup pools 4*BPW
-// consecutive level-1 blocks (16 tokens each) of one tensor; lane (b, c) of a
-// wave reads the 16 rows of block b at 16-byte column chunk c, so every load
-// instruction of a wave reads whole 128-byte row segments and the block sum
-// needs no cross-lane reduction.  Level 2 is formed from the level-1 means in
+// A streaming, HBM-bound pass.  One 256-thread workgroup pools 16 consecutive
+// level-1 blocks (16 tokens each) of one tensor, 4 per wave; lane (b, hh, c)
+// of a wave reads rows of block b at 16-byte column chunk c, bf16 rows 8 hh ..
+// 8 hh + 7 (two lanes per chunk, added with one exchange) and float32 rows all
+// 16, so every load instruction reads whole row segments.  Small waves keep
+// the last round of the grid nearly full.  Level 2 is formed from the level-1 means in
 // LDS; deeper levels (rare, small) are pooled from the level below by a
 // second kernel.  Blocks of 64 tokens take a kernel of their own (one wave per
 // block) and every level above 1 comes from the level below.
@@ -43,7 +44,9 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ q, cons
                                                    TokMap tm) {
     constexpr int EPC = ElemTraits<T>::kPerChunk;  // elements per 16-byte chunk
     constexpr int CPR = kHeadDim / EPC;            // chunks per row
-    constexpr int BPW = kWave / CPR;               // level-1 blocks per wave
+    constexpr int BPW = 4;                         // level-1 blocks per wave
+    constexpr int RS = kWave / (BPW * CPR);        // lanes that share a block's chunk, a row range each
+    constexpr int RPL = kBlock / RS;               // rows per lane
     constexpr int BPG = 4 * BPW;                   // level-1 blocks per workgroup
     __shared__ float lvl1[BPG][kHeadDim];
 
@@ -53,7 +56,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ q, cons
     float *out = tensor == 0 ? pq : (tensor == 1 ? pk : pv);
 
     const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int b = lane / CPR, c = lane % CPR;
+    const int c = lane % CPR, hh = (lane / CPR) % RS, b = lane / (CPR * RS);
     const int64_t blk0 = (int64_t)wg * BPG;
     const int64_t blk = blk0 + w * BPW + b;
 
@@ -65,22 +68,28 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ q, cons
         const int64_t h = blk / n1;
         const int lb = (int)(blk % n1);
         const T *src = x + h * (int64_t)n1 * kBlock * kHeadDim + c * EPC;
-        u32x4 r[kBlock];
+        u32x4 r[RPL];
 #pragma unroll
-        for (int t = 0; t < kBlock; ++t)
+        for (int t = 0; t < RPL; ++t)
             r[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                src + (int64_t)tok_tile_row<ORD>(tm, lb, t) * kHeadDim));
+                src + (int64_t)tok_tile_row<ORD>(tm, lb, hh * RPL + t) * kHeadDim));
 #pragma unroll
-        for (int t = 0; t < kBlock; ++t) {
+        for (int t = 0; t < RPL; ++t) {
             float f[EPC];
             chunk_to_f32(r[t], f, (T *)nullptr);
 #pragma unroll
             for (int j = 0; j < EPC; ++j) acc[j] += f[j];
         }
+        if constexpr (RS == 2) {   // the two row halves of the block's chunk (lanes CPR apart)
+#pragma unroll
+            for (int j = 0; j < EPC; ++j) acc[j] += shfl_xor_f(acc[j], CPR);
+        }
+        static_assert(RS == 1 || RS == 2, "one or two lanes per chunk");
 #pragma unroll
         for (int j = 0; j < EPC; ++j) acc[j] *= (1.0f / kBlock);
         float *dst = out + blk * kHeadDim + c * EPC;
-        if constexpr (EPC == 8) {
+        if (hh != 0) {
+        } else if constexpr (EPC == 8) {
             *reinterpret_cast<f32x4 *>(dst) = f32x4{acc[0], acc[1], acc[2], acc[3]};
             *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
         } else {
@@ -190,7 +199,7 @@ static void launch_pool_t(const Geometry &g, const T *q, const T *k, const T *v,
                                pq, pk, pv, total_blocks, wg_per_tensor, g.n[1], tm);
         return;
     }
-    constexpr int BPG = 4 * (kWave / (kHeadDim / ElemTraits<T>::kPerChunk));
+    constexpr int BPG = 16;   // 4 waves x 4 level-1 blocks
     const int64_t total_blocks = (int64_t)g.bh * g.n[1];
     const int wg_per_tensor = (int)((total_blocks + BPG - 1) / BPG);
     const int do2 = g.L >= 2 ? 1 : 0;

@@ -23,10 +23,12 @@ def _log(msg):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("b,h,N,L_,K,Le", [(1, 4, 16384, 2, 8, 1), (1, 2, 8192, 3, 4, 2)])
-def test_graph_replays_equal_eager(b, h, N, L_, K, Le):
-    _log(f"[graph] {b} {h} {N} L{L_} K{K} Le{Le}")
-    c = Case(b, h, N, torch.bfloat16, L_, K, Le, backward=True, sinus=round(N ** 0.5) ** 2 == N)
+@pytest.mark.parametrize("b,h,N,L_,K,Le,dtype", [(1, 4, 16384, 2, 8, 1, torch.bfloat16),
+                                                  (1, 2, 8192, 3, 4, 2, torch.bfloat16),
+                                                  (1, 2, 8192, 2, 8, 1, torch.float32)])
+def test_graph_replays_equal_eager(b, h, N, L_, K, Le, dtype):
+    _log(f"[graph] {b} {h} {N} L{L_} K{K} Le{Le} {dtype}")
+    c = Case(b, h, N, dtype, L_, K, Le, backward=True, sinus=round(N ** 0.5) ** 2 == N)
     q, k, v, do = c.q.cuda(), c.k.cuda(), c.v.cuda(), c.dout.cuda()
     B = L.Buffers(c.p, backward=True)
 

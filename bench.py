@@ -542,7 +542,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the operator shards by (batch, head) with no "
-              "communication, and this build runs on a single MI355X; use --gpus 1.",
+              "communication, so a step on N GPUs is N independent one-GPU steps; use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -72,6 +72,8 @@ EDGE = [
     (1, 2, 4096, torch.bfloat16, 1, 20, 0, True, {}),      # single level, K = 20
     (1, 2, 4096, torch.bfloat16, 1, 32, 0, True, {}),      # single level, K = 32 (largest)
     (1, 16, 16384, torch.bfloat16, 1, 8, 0, True, {}),     # single level, 1024 row groups: one wave each
+    (1, 16, 16384, torch.bfloat16, 1, 20, 0, True, {}),    # the same with K = 20 (32-key sorted groups)
+    (1, 2, 4096, torch.bfloat16, 2, 20, 1, True, {}),      # K = 20 and one coarse tile: 3 forward chunks
     (1, 2, 4096, torch.bfloat16, 2, 32, 1, True, {}),      # K = 32 with enrichment (16 coarse: 1 tile)
     (1, 2, 16384, torch.bfloat16, 2, 32, 1, True, {}),     # 32 coarse entries: 2 coarse tiles
     (1, 2, 8192, torch.bfloat16, 3, 16, 2, True, {}),      # 16 + 2 coarse entries: 2 coarse tiles

@@ -449,7 +449,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
 // Pass A for B = 16 with K_1 = K1T (even) fine picks per query block and one
 // coarse tile of at most 16 entries (CO) or none.  The 16 query blocks under
 // a level-2 node share their coarse picks, so the workgroup stages that tile
-// once in LDS as bf16 together with its log2 weights.  Every wave streams the
+// once in LDS as bf16 together with its log2 weights.  Wave w takes blocks
+// w, w + 4, w + 8, w + 12 of the node, so the four waves work on neighbouring
+// blocks at any time (neighbours pick many of the same key blocks, which the
+// L1 then serves once).  Every wave streams the
 // 4 K1T fine tiles of its 4 query blocks through two register sets without a
 // break at block boundaries (the next block's first tiles and its Q / dO are
 // in flight while a block's coarse part is computed); the wave's fine picks
@@ -525,9 +528,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
 
     // ---- this wave's fine picks: pick u (block u / K1T, pick u % K1T) sits in
     // lane u of fidx0 (u < 64) or lane u - 64 of fidx1
-    const int32_t *wpicks = idx + ((int64_t)h * a.n1 + ib0 + w * 4) * K1T;
-    const int fidx0 = lane < NT ? wpicks[lane] : 0;
-    const int fidx1 = NT > kWave && lane < NT - kWave ? wpicks[kWave + lane] : 0;
+    // block jb of this wave is ib0 + 4 jb + w: the four waves work on four
+    // neighbouring blocks at a time, whose picks overlap in the L1
+    const int32_t *hpicks = idx + ((int64_t)h * a.n1 + ib0) * K1T;
+    auto wpick = [&](int u) { return hpicks[((u / K1T) * 4 + w) * K1T + u % K1T]; };
+    const int fidx0 = lane < NT ? wpick(lane) : 0;
+    const int fidx1 = NT > kWave && lane < NT - kWave ? wpick(kWave + lane) : 0;
     auto pick = [&](int u) {
         if constexpr (NT <= kWave)
             return __builtin_amdgcn_readlane(fidx0, u);
@@ -564,7 +570,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
         float lse2;
     };
     auto load_q = [&](int jb, QRegs &X) {
-        const int b = ib0 + w * 4 + jb;
+        const int b = ib0 + jb * 4 + w;
         const int64_t o0 = head_off + trow(b, lrow) + lcol, o1 = head_off + trow(b, lrow + 8) + lcol;
         X.qa0 = load_bf16x8_nt(q + o0);
         X.qa1 = load_bf16x8_nt(q + o1);
@@ -600,7 +606,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
     __syncthreads();   // coarse tile staged
 
     for (int jb = 0; jb < 4; ++jb) {
-        const int64_t row = (int64_t)(ib0 + w * 4 + jb) * kBlock + c16;
+        const int64_t row = (int64_t)(ib0 + jb * 4 + w) * kBlock + c16;
         const float lse2 = X.lse2;
         wave_lds_sync();
         stage_rows(lds_q[w], X.qa0, X.qa1);
@@ -686,7 +692,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
                 const int r = g + 4 * it;
-                store_grad4(dq, head_off + trow(ib0 + w * 4 + jb, r) + 4 * c16,
+                store_grad4(dq, head_off + trow(ib0 + jb * 4 + w, r) + 4 * c16,
                             *reinterpret_cast<const f32x4 *>(&out_w[r * kOutS + 4 * c16]), a.grad_bf16);
             }
             continue;
@@ -765,7 +771,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fast_kernel(
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int r = g + 4 * it;
-            store_grad4(dq, head_off + trow(ib0 + w * 4 + jb, r) + 4 * c16,
+            store_grad4(dq, head_off + trow(ib0 + jb * 4 + w, r) + 4 * c16,
                         *reinterpret_cast<const f32x4 *>(&out_w[r * kOutS + 4 * c16]), a.grad_bf16);
         }
         }

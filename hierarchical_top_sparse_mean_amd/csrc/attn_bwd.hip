@@ -240,7 +240,8 @@ __device__ __forceinline__ void load_coarse_tile(const BwdArgs &a, const float *
 }
 
 // One workgroup (4 waves) per 16 consecutive query tiles (a level-2 node for
-// B = 16), every wave 4 of them in turn; the fine key tiles of a query tile
+// B = 16), wave w taking tiles w, w + 4, w + 8, w + 12 in turn, so that the
+// four waves work on neighbouring tiles at any time; the fine key tiles of a query tile
 // stream through two register sets (the next tile's K / V are in flight while
 // the current one is computed).
 template <int NCT>
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
         bf16x8 ka0, ka1, va0, va1;
     };
     for (int jb = 0; jb < 4; ++jb) {
-        const int qt = G * kBlock + w * 4 + jb;   // query tile
+        const int qt = G * kBlock + jb * 4 + w;   // query tile: the waves take neighbours at a time
         if (qt >= a.nt1) break;
         const int ib = qt / a.sub;                // its query block
         const int64_t row = (int64_t)qt * kBlock + c16;          // sequence position

@@ -1477,8 +1477,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_b64_kernel(
 // fixed order, so the results are reproducible.
 
 // Pass A (f32): one workgroup per group of 16 consecutive query tiles (all
-// under one level-2 node, so they share their coarse entries), one wave per 4
-// tiles, on the float32 matrix cores and laid out as the float32 forward
+// under one level-2 node, so they share their coarse entries), wave w taking
+// tiles w, w + 4, w + 8, w + 12 (neighbours at a time, which share key tiles
+// in the L1), on the float32 matrix cores and laid out as the float32 forward
 // (scores transposed, lane (g, c): query c against keys 4g .. 4g + 3; row
 // layout for Q, dO, K and V in the score products, column layout for K in
 // dQ^T += K^T dS^T).  D = rowsum(dO * O) comes from O first, so dS = P (dP -
@@ -1522,7 +1523,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_f32_kernel(
     float Dv[4], L2v[4];   // D and lse * log2(e) of query c16 of the wave's tiles
     // ---- dQ of the wave's 4 tiles
     for (int jt = 0; jt < 4; ++jt) {
-        const int qt = G * kBlock + 4 * w + jt;
+        const int qt = G * kBlock + 4 * jt + w;
         Dv[jt] = L2v[jt] = 0.f;
         if (qt >= a.nt1) break;   // ragged last group (single level only)
         const int ib = qt / a.sub;
@@ -1607,7 +1608,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_f32_kernel(
         float er[16], ev[16];   // entry c16's pooled K and V rows (the same for the whole group)
         bool loaded = false;
         for (int jt = 0; jt < 4; ++jt) {
-            const int qt = G * kBlock + 4 * w + jt;
+            const int qt = G * kBlock + 4 * jt + w;
             if (qt >= a.nt1) break;
             const int ib = qt / a.sub;
             const int32_t *fine = idx + ((int64_t)h * a.n1 + ib) * a.K1;

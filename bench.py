@@ -490,6 +490,7 @@ def config_records(L, dev, steps, warmup, cold_reps):
         rec = {"config_record": w.name, "describe": w.describe(), "keys_per_query_block": nkv,
                "ms_per_step": round(msps, 4), "tokens_per_s": round(w.batch * w.seq_len / (msps / 1e3), 1),
                "timing": "warm: calls back to back, inputs resident",
+               "steps": steps, "warmup": warmup, "per_call": "median over the timed steps",
                "calls": call_details(alg, pc),
                "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1),
                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
@@ -499,7 +500,7 @@ def config_records(L, dev, steps, warmup, cold_reps):
         if w.name in ("n4096_bf16", "n16384_bf16"):
             rec["working_set_MB"] = round(ws_bytes / 1e6, 1)
             rec["calls_cold"] = call_details(alg, time_cold(L, w, p, B, q, k, v, dout, cold_reps, dev))
-            rec["timing_cold"] = "each call alone after a 512 MiB write (MALL flushed)"
+            rec["timing_cold"] = f"each call alone after a 512 MiB write (MALL flushed), mean of {cold_reps}"
         # one more step so that every result comes from the same pass, then the oracle
         for _, fn in step_calls(L, w, p, B, q, k, v, dout):
             fn()

@@ -27,9 +27,10 @@ FP32_PEAK_TFLOPS = 157.3
 METRIC = "LLSA fwd+bwd tokens/sec at N=65536, K=8; % bf16 MFMA peak; sel GB/s"
 
 
-def algorithmic(w, s):
+def algorithmic(w, s, grad_bytes=4):
     """Compulsory HBM bytes and useful FLOPs per call (see the derivation in the
-    design notes): every tensor the call must read or write, once."""
+    design notes): every tensor the call must read or write, once.  grad_bytes:
+    4 for float32 dQ, dK, dV, 2 for bfloat16."""
     bh, N, d = w.bh, w.seq_len, w.head_dim
     e = 2 if str(w.dtype) == "torch.bfloat16" else 4
     L = w.levels
@@ -56,7 +57,7 @@ def algorithmic(w, s):
     for l in range(1, Le + 2):
         tr += bh * n[l] * kl[l] * 4 + bh * (n[l] + 1) * 4 + bh * n[l] * kl[l] * 4
     out["transpose"] = dict(bytes=tr, flops=0)
-    g = 4  # float32 gradients
+    g = grad_bytes
     # the compulsory bytes of the backward: Q, K, V, O, dO read, dQ, dK, dV
     # written, LSE and D once each.  The kernels never read O (D = sum P dP comes out of the dQ
     # pass), but read the coarse pyramids, the pick lists and the CSR and read
@@ -558,7 +559,7 @@ def main():
         for sw, var in sweep_workloads():
             _, _, _, _, _, _, ss, pc, msps = time_workload(L, sw, args.steps, args.warmup, dev,
                                                           var == "grad_bf16", int(var == "patch_order"))
-            alg, nkv = algorithmic(sw, ss)
+            alg, nkv = algorithmic(sw, ss, 2 if var == "grad_bf16" else 4)
             tok = sw.batch * sw.seq_len
             rec = {"sweep": sw.name + ("_" + var if var else ""), "describe": sw.describe(),
                    "keys_per_query_block": nkv, "ms_per_step": round(msps, 4),

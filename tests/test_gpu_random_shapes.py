@@ -5,7 +5,8 @@ built for; this module draws a fixed list of further shapes from one seed
 (block size, pooling steps, top-K, enrichment levels, dtypes, token order,
 the drop rule, batch and heads), so that a path the edge list misses still
 meets the oracle.  Each shape is small enough for the oracle to finish in a
-second or two.  The list is the same on every run.
+second or two.  A second list draws shapes in the 2D patch order (N a power
+of 4).  The lists are the same on every run.
 """
 import sys
 
@@ -50,7 +51,33 @@ def _draw_cases():
     return cases
 
 
-CASES = _draw_cases()
+def _draw_patch_cases(n_cases=8):
+    """Shapes in 2D patch order: N = 4^m pixels of a square image."""
+    rng = np.random.default_rng(4096)
+    cases = []
+    while len(cases) < n_cases:
+        B = 64 if rng.random() < 0.25 else 16
+        N = int(4 ** rng.integers(4, 9))            # 256 .. 65536 pixels
+        Lmax = 1
+        while Lmax < 3 and N % (B ** (Lmax + 1)) == 0 and N // (B ** (Lmax + 1)) >= 1:
+            Lmax += 1
+        if N % B != 0:
+            continue
+        Lv = int(rng.integers(1, Lmax + 1))
+        K = int(rng.integers(1, 33))
+        Le = int(rng.integers(0, Lv)) if Lv > 1 else 0
+        if K * B * N > MAX_PAIRS:
+            continue
+        dtype = torch.float32 if rng.random() < 0.25 else torch.bfloat16
+        grad = torch.bfloat16 if rng.random() < 0.2 else torch.float32
+        drop = bool(rng.random() < 0.85)
+        batch = int(rng.integers(1, 3))
+        heads = int(rng.integers(1, 4))
+        cases.append((batch, heads, N, dtype, Lv, K, Le, B, 1, grad, drop))
+    return cases
+
+
+CASES = _draw_cases() + _draw_patch_cases()
 IDS = [f"b{c[0]}h{c[1]}N{c[2]}{str(c[3])[6:]}L{c[4]}K{c[5]}Le{c[6]}B{c[7]}o{c[8]}g{str(c[9])[6:]}d{int(c[10])}"
        for c in CASES]
 
